@@ -1,0 +1,292 @@
+"""Plain fp64 CPU oracle for the sparse top-k MoE layer forward.
+
+TEST INFRASTRUCTURE ONLY. Nothing on the product path imports this module:
+only the tests, the smoke check and the benchmark's CPU-baseline leg may call
+it. It shares no code with the HIP path (no kernels, tables, helpers or pre-
+and post-processing); both sides only share the seeded input generator.
+
+Everything is float64 NumPy, written as the plain definition of each step so a
+reader can check it against the pages by eye. Library primitives (matmul, a
+stable argsort, bincount, exp) serve as single steps; there is no blocking,
+fusion or reordering beyond what the definitions state.
+
+Pages cited (by title, then section):
+  [Deep Dive]  "MoE (Mixture of Experts) Deep Dive: Principles, Formulas, and
+               Implementation" (kongchang.com)
+  [Arch]       "MoE Architecture" (infra.bea.ai guide)
+  [Notes]      "Mixture of Experts" (avinashkadimisetty.com ML-algorithm notes)
+  [Handbook]   "Mixture of experts (MoE)" (ai-infra-handbooks)
+  [Concept]    "One Deep Concept #04 -- Mixture of Experts" (Miniblog)
+
+Readings taken where the pages are silent or disagree (each also listed in the
+design notes): router weight stored [E, d] (a linear layer's weight); top-k on
+the logits plus the selection bias, equal keys broken toward the lower expert
+index, slots in descending key order; the selection bias never reaches the
+gates or p_i; gates always renormalised over the kept k; capacity
+ceil(cf * T*k / E) in IEEE double; overflow dropped first-come in ascending
+flat assignment order a = t*k + j with no gate renormalisation afterwards;
+f_i counted before dropping over T*k assignments; alpha inside L_balance.
+
+Pin status: every function below is pinned by a `-m "not gpu"` test against
+values the pages print, closed forms, library special cases or brute force,
+except the readings themselves (drop order, the Zipf offset, what the
+selection bias is added to), which no page fixes beyond plausibility.
+"""
+from __future__ import annotations
+
+import math
+from typing import Callable, Optional, Sequence, Tuple
+
+import numpy as np
+
+__all__ = [
+    "router_logits", "softmax", "selection_keys", "select_topk", "renormalised_gates",
+    "route", "capacity", "align", "silu", "swiglu_expert", "moe_forward",
+    "moe_forward_naive", "token_output", "balance", "expert_table",
+]
+
+ExpertFn = Callable[[int], Tuple[np.ndarray, np.ndarray, np.ndarray]]
+
+
+# ----------------------------------------------------------------------------- router
+def router_logits(x: np.ndarray, w_gate: np.ndarray,
+                  logit_bias: Optional[np.ndarray] = None) -> np.ndarray:
+    """Router scores, one per (token, expert).
+
+    [Arch] §2 "Gating Function" writes the scores as x times W_gate with
+    W_gate of shape d x E; [Notes] "Routing math" writes W_g x with W_g of
+    shape N x d. Here w_gate is stored [E, d] (the second form), so the
+    scores are x @ w_gate.T -- the same numbers as x @ W_gate with
+    W_gate = w_gate.T. An optional per-expert offset is part of the logits
+    (it enters the softmax, the selection and p_i)."""
+    x = np.asarray(x, dtype=np.float64)
+    w_gate = np.asarray(w_gate, dtype=np.float64)
+    logits = x @ w_gate.T
+    if logit_bias is not None:
+        logits = logits + np.asarray(logit_bias, dtype=np.float64)[None, :]
+    return logits
+
+
+def softmax(logits: np.ndarray) -> np.ndarray:
+    """Softmax over the experts of each token ([Deep Dive] "Router Network
+    Computation"; [Arch] §2; [Concept] §4), shifted by the row maximum so no
+    exponential overflows (the shift cancels in the ratio)."""
+    m = logits.max(axis=1, keepdims=True)
+    e = np.exp(logits - m)
+    return e / e.sum(axis=1, keepdims=True)
+
+
+def selection_keys(logits: np.ndarray, sel_bias: Optional[np.ndarray] = None) -> np.ndarray:
+    """The values top-k selects on: the logits, plus the per-expert balancing
+    bias if one is given. [Handbook] "Load balancing" and [Arch] §2 describe
+    that bias as used only to choose the experts, never in the weights;
+    [Notes] adds it to the router logits."""
+    if sel_bias is None:
+        return logits
+    return logits + np.asarray(sel_bias, dtype=np.float64)[None, :]
+
+
+def select_topk(keys: np.ndarray, k: int) -> np.ndarray:
+    """Each token's k experts with the largest keys, largest first
+    ([Arch] §2 route(); [Handbook] "Structure" step 2). Equal keys go to the
+    lower expert index (a stable sort of the negated keys keeps index order
+    among equals). Selecting on logits rather than probabilities selects the
+    same set, since softmax is increasing."""
+    order = np.argsort(-keys, axis=1, kind="stable")
+    return order[:, :k].astype(np.int64)
+
+
+def renormalised_gates(probs: np.ndarray, ids: np.ndarray) -> np.ndarray:
+    """The kept probabilities divided by their sum, so each token's k gates
+    add to 1 ([Deep Dive] "Weighted Sum Output": 0.55 and 0.3 are divided by
+    0.85; [Handbook] "Structure"). This equals [Arch]'s softmax over the k
+    selected scores."""
+    sel = np.take_along_axis(probs, ids, axis=1)
+    return sel / sel.sum(axis=1, keepdims=True)
+
+
+def route(x, w_gate, k: int, logit_bias=None, sel_bias=None):
+    """Router forward: returns (ids [T,k], gates [T,k], probs [T,E], keys [T,E])."""
+    logits = router_logits(x, w_gate, logit_bias)
+    probs = softmax(logits)
+    keys = selection_keys(logits, sel_bias)
+    ids = select_topk(keys, k)
+    gates = renormalised_gates(probs, ids)
+    return ids, gates, probs, keys
+
+
+# ----------------------------------------------------------------------------- grouping
+def capacity(capacity_factor: float, T: int, k: int, E: int) -> Optional[int]:
+    """Per-expert limit on kept assignments, or None for no limit.
+
+    [Notes] "How it works" sizes each expert's buffer as the capacity factor
+    times the average load per expert; [Arch] §2 calls it 1.0-1.5x of the
+    average. With top-k routing the average is T*k/E assignments, so the limit
+    is ceil(cf * (T*k) / E), evaluated in IEEE double in that order."""
+    if capacity_factor is None or capacity_factor <= 0:
+        return None
+    return int(math.ceil(float(capacity_factor) * float(T * k) / float(E)))
+
+
+def align(ids: np.ndarray, E: int, cap: Optional[int] = None) -> dict:
+    """Group the T*k assignments by expert ([Handbook] "Implementation: token
+    by token vs. grouped by expert": flatten, stable sort by expert, count,
+    segment starts by prefix sum).
+
+    Assignment a = t*k + j goes to expert ids[t, j]. Within an expert the
+    assignments keep ascending a. With a capacity limit, assignment a is kept
+    iff fewer than `cap` earlier assignments went to its expert; a dropped
+    assignment contributes nothing ([Arch] §2 "Expert capacity and token
+    dropping"; [Handbook] "Load balancing").
+
+    Returns int64 arrays: counts_pre [E] (before dropping), counts [E] (kept),
+    offsets [E+1], sorted_assign [offsets[E]] (flat a, expert-major), and
+    assign_pos [T*k] (row of a in sorted order, or -1 if dropped)."""
+    ids = np.asarray(ids, dtype=np.int64)
+    T, k = ids.shape
+    flat = ids.reshape(-1)
+    n = flat.size
+    counts_pre = np.bincount(flat, minlength=E).astype(np.int64)
+    order = np.argsort(flat, kind="stable")          # expert-major, ascending a inside
+    starts = np.concatenate([[0], np.cumsum(counts_pre)[:-1]])
+    rank = np.empty(n, dtype=np.int64)
+    rank[order] = np.arange(n, dtype=np.int64) - starts[flat[order]]
+    kept = np.ones(n, dtype=bool) if cap is None else rank < cap
+    counts = counts_pre.copy() if cap is None else np.minimum(counts_pre, cap)
+    offsets = np.concatenate([[0], np.cumsum(counts)]).astype(np.int64)
+    assign_pos = np.where(kept, offsets[flat] + rank, -1).astype(np.int64)
+    sorted_assign = np.empty(int(offsets[-1]), dtype=np.int64)
+    sorted_assign[assign_pos[kept]] = np.nonzero(kept)[0]
+    return dict(counts_pre=counts_pre, counts=counts, offsets=offsets,
+                sorted_assign=sorted_assign, assign_pos=assign_pos)
+
+
+# ----------------------------------------------------------------------------- experts
+def silu(z: np.ndarray) -> np.ndarray:
+    """SiLU(z) = z * sigmoid(z), evaluated without overflow: for z < 0 the
+    sigmoid is written exp(z) / (1 + exp(z))."""
+    z = np.asarray(z, dtype=np.float64)
+    out = np.empty_like(z)
+    pos = z >= 0
+    out[pos] = z[pos] / (1.0 + np.exp(-z[pos]))
+    ez = np.exp(z[~pos])
+    out[~pos] = z[~pos] * ez / (1.0 + ez)
+    return out
+
+
+def swiglu_expert(rows: np.ndarray, w1: np.ndarray, w3: np.ndarray, w2: np.ndarray) -> np.ndarray:
+    """One SwiGLU expert on a batch of rows: W2 (SiLU(W1 x) * (W3 x)).
+
+    [Arch] §3 "Standard MoE" makes each expert a SwiGLU FFN with 3*d*d_ff
+    parameters; [Handbook]'s expert has a gate projection (through SiLU), an
+    up projection and a down projection. w1 = gate [d_ff, d], w3 = up
+    [d_ff, d], w2 = down [d, d_ff], all "out x in"."""
+    rows = np.asarray(rows, dtype=np.float64)
+    u = rows @ np.asarray(w1, dtype=np.float64).T
+    v = rows @ np.asarray(w3, dtype=np.float64).T
+    h = silu(u) * v
+    return h @ np.asarray(w2, dtype=np.float64).T
+
+
+def expert_table(w1, w3, w2) -> ExpertFn:
+    """Wrap stacked [E, ...] arrays as an expert lookup e -> (w1_e, w3_e, w2_e) in fp64."""
+    def get(e: int):
+        return (np.asarray(w1[e], dtype=np.float64), np.asarray(w3[e], dtype=np.float64),
+                np.asarray(w2[e], dtype=np.float64))
+    return get
+
+
+def _shared_sum(x: np.ndarray, shared: Sequence[Tuple[np.ndarray, np.ndarray, np.ndarray]]) -> np.ndarray:
+    """Always-on shared experts, ungated and added to the routed sum
+    ([Deep Dive] "Shared Experts"; [Arch] §3 "Shared Experts (DeepSeek)")."""
+    out = np.zeros((x.shape[0], x.shape[1]), dtype=np.float64)
+    for (s1, s3, s2) in shared:
+        out += swiglu_expert(x, s1, s3, s2)
+    return out
+
+
+# ----------------------------------------------------------------------------- forward
+def moe_forward(x, w_gate, experts: ExpertFn, E: int, k: int, logit_bias=None, sel_bias=None,
+                shared: Sequence = (), capacity_factor: float = 0.0, ids=None):
+    """Grouped forward ([Handbook] "Implementation": group by expert, one
+    batched expert call per non-empty segment, weighted scatter back).
+
+    y[t] = sum over kept slots j of g[t,j] * Expert_{ids[t,j]}(x[t]) + shared(x[t])
+    ([Arch] §1; [Notes] "Routing math"). If `ids` is given, routing uses those
+    ids and the oracle's own probabilities (gates renormalised over them).
+    Returns (y [T,d], info dict with ids, gates, probs, keys and the align
+    outputs)."""
+    x = np.asarray(x, dtype=np.float64)
+    T, d = x.shape
+    r_ids, gates, probs, keys = route(x, w_gate, k, logit_bias, sel_bias)
+    if ids is not None:
+        r_ids = np.asarray(ids, dtype=np.int64)
+        gates = renormalised_gates(probs, r_ids)
+    cap = capacity(capacity_factor, T, k, E)
+    al = align(r_ids, E, cap)
+    flat_gates = gates.reshape(-1)
+    y = np.zeros((T, d), dtype=np.float64)
+    for e in range(E):
+        seg = al["sorted_assign"][al["offsets"][e]:al["offsets"][e + 1]]
+        if seg.size == 0:                         # an empty group does nothing
+            continue
+        tok = seg // k
+        out = swiglu_expert(x[tok], *experts(e))
+        np.add.at(y, tok, flat_gates[seg][:, None] * out)
+    y += _shared_sum(x, shared)
+    info = dict(ids=r_ids, gates=gates, probs=probs, keys=keys, cap=cap, **al)
+    return y, info
+
+
+def token_output(x_t: np.ndarray, ids_t, gates_t, kept_t, experts: ExpertFn,
+                 shared: Sequence = ()) -> np.ndarray:
+    """One token's output, slot by slot ([Deep Dive] "Code Implementation
+    Essentials" item 3: for each token, for each chosen expert, add the
+    gate-weighted expert output), plus the shared experts."""
+    x_t = np.asarray(x_t, dtype=np.float64).reshape(1, -1)
+    y = np.zeros(x_t.shape[1], dtype=np.float64)
+    for j in range(len(ids_t)):
+        if kept_t[j]:
+            y += float(gates_t[j]) * swiglu_expert(x_t, *experts(int(ids_t[j])))[0]
+    y += _shared_sum(x_t, shared)[0]
+    return y
+
+
+def moe_forward_naive(x, w_gate, experts: ExpertFn, E: int, k: int, logit_bias=None,
+                      sel_bias=None, shared: Sequence = (), capacity_factor: float = 0.0):
+    """Token-by-token forward ([Handbook] forward_naive's method). The
+    capacity rule is applied with a running per-expert counter in ascending
+    (t, j) order, a formulation independent of align()'s stable sort."""
+    x = np.asarray(x, dtype=np.float64)
+    T, d = x.shape
+    ids, gates, _, _ = route(x, w_gate, k, logit_bias, sel_bias)
+    cap = capacity(capacity_factor, T, k, E)
+    used = np.zeros(E, dtype=np.int64)
+    y = np.zeros((T, d), dtype=np.float64)
+    for t in range(T):
+        kept = []
+        for j in range(k):
+            e = int(ids[t, j])
+            ok = cap is None or used[e] < cap
+            used[e] += 1
+            kept.append(ok)
+        y[t] = token_output(x[t], ids[t], gates[t], kept, experts, shared)
+    return y
+
+
+# ----------------------------------------------------------------------------- statistics
+def balance(counts_pre: np.ndarray, probs: np.ndarray, T: int, k: int, alpha: float = 0.01):
+    """Load statistics and the auxiliary balance loss.
+
+    f_i: share of the T*k routed assignments that chose expert i (counted
+    before capacity dropping; [Handbook] "Load balancing" divides the top-k id
+    histogram by the number of ids). P_i: mean router probability of expert i
+    over the tokens. L = alpha * E * sum_i f_i * P_i ([Arch] §2 "Load
+    Balancing"; [Notes] gives alpha ~ 0.01; [Deep Dive] "Load Balancing Loss
+    Derivation" has the same N * sum F_i P_i form). Returns (f, P, L)."""
+    counts_pre = np.asarray(counts_pre, dtype=np.float64)
+    E = counts_pre.size
+    f = counts_pre / float(T * k)
+    P = np.asarray(probs, dtype=np.float64).mean(axis=0)
+    L = float(alpha) * E * float(np.sum(f * P))
+    return f, P, L

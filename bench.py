@@ -1,0 +1,271 @@
+#!/usr/bin/env python3
+"""Benchmark of the sparse top-k MoE layer forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload mixtral_prefill]
+
+A step is one moe_forward call (router -> align -> grouped gate-up GEMM with
+SwiGLU -> grouped down GEMM -> combine) over one batch of synthetic input
+already resident in HBM. W untimed warm-up steps, then exactly K steps
+between two device synchronisations. Prints ONE JSON line on stdout:
+tokens/s of the whole job, the roofline of the dominant kernel (its average
+duration measured live with HIP events recorded on the launch stream between
+the stages of every timed step), and the fp64 CPU oracle timed on a bounded
+sample of the same workload (1 core).
+
+The default workload is the Mixtral-shaped prefill layer (T=4096, d=4096,
+E=8, k=2, d_ff=14336, bf16). The other presets can be timed with --workload.
+Only one GPU: --gpus N > 1 exits with a message.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "MoE-layer tokens/sec at 1 GPU (prefill, decode); % MFMA bf16 / HBM roofline"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3        # MI355X fp32 vector
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)   # flop per byte
+KERNEL_SOURCES = {"gate_up": "gemm.hip", "down": "gemm.hip", "route": "route.hip",
+                  "align": "align.hip", "schedule": "align.hip", "combine": "combine.hip"}
+KERNEL_NAMES = {"gate_up": "gemm_bf16_kernel<true>", "down": "gemm_bf16_kernel<false>",
+                "route": "route_kernel", "align": "align_*_kernel", "schedule": "schedule_kernel",
+                "combine": "combine_kernel"}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ----------------------------------------------------------------------------- accounting
+def expert_params(d: int, d_ff: int) -> int:
+    """Parameters of one SwiGLU expert: gate, up and down projections."""
+    return 3 * d * d_ff
+
+
+def algorithmic_work(w, counts, T=None):
+    """Layer flops and bytes from the actual routing (kept rows per expert).
+
+    flops: router 2*T*d*E + 6*d*d_ff per kept routed row + 6*d*d_ff_s per token for
+    a shared expert. bytes: x + W_gate + the full weights of every expert with at
+    least one kept row + the shared expert's weights + fp32 y. Padding rows, the
+    intermediate h, per-row expert outputs and routing metadata are implementation
+    traffic and are not counted."""
+    T = w.T if T is None else T
+    esz = 2 if w.dtype == "bf16" else 4
+    kept = int(sum(counts))
+    touched = int(sum(1 for c in counts if c > 0))
+    flops = 2 * T * w.d * w.E + 6 * w.d * w.d_ff * kept + 6 * w.d * w.d_ff_shared * T * w.n_shared
+    byts = (T * w.d * esz + w.E * w.d * esz + touched * expert_params(w.d, w.d_ff) * esz
+            + w.n_shared * expert_params(w.d, w.d_ff_shared) * esz + T * w.d * 4)
+    return dict(flops=flops, bytes=byts, kept=kept, touched=touched)
+
+
+def kernel_work(w, counts, stage, T=None):
+    """Algorithmic flops and bytes of one launch of a GEMM stage.
+
+    gate-up: 4*d*d_ff flops per row (routed kept rows + shared rows); bytes = x
+    (read once) + W1 and W3 of every touched expert (+ shared) + h written (bf16,
+    one row per kept row). down: 2*d*d_ff flops per row; bytes = h read + W2 of
+    every touched expert (+ shared) + fp32 output rows written."""
+    T = w.T if T is None else T
+    esz = 2 if w.dtype == "bf16" else 4
+    hsz = 2 if w.dtype == "bf16" else 4
+    kept = int(sum(counts))
+    touched = int(sum(1 for c in counts if c > 0))
+    rows = kept + T * w.n_shared
+    wmat = w.d * w.d_ff * esz
+    groups = touched + w.n_shared
+    if stage == "gate_up":
+        return dict(flops=4 * w.d * w.d_ff * rows,
+                    bytes=T * w.d * esz + 2 * wmat * groups + rows * w.d_ff * hsz)
+    if stage == "down":
+        return dict(flops=2 * w.d * w.d_ff * rows,
+                    bytes=rows * w.d_ff * hsz + wmat * groups + rows * w.d * 4)
+    raise ValueError(stage)
+
+
+def source_sha(stage: str) -> str:
+    path = os.path.join(ROOT, "mixture_experts_layer_44_amd", "csrc", KERNEL_SOURCES[stage])
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def traffic_from_profile(stage: str, workload: str):
+    """HBM bytes per launch from the committed counter summary, or None if there is
+    none or the kernel source has changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{stage}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_sha") != source_sha(stage):
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+# ----------------------------------------------------------------------------- CPU baseline
+def cpu_baseline(w, inp, sample_tokens: int):
+    """The fp64 oracle, as it stands, on the first `sample_tokens` tokens of the
+    workload (all of its experts' weights), on one host core."""
+    import numpy as np
+    import torch
+    from threadpoolctl import threadpool_limits
+    import oracle as O
+
+    S = min(sample_tokens, w.T)
+    cpu = {k: (None if v is None else v[:S].cpu() if k == "x" else v.cpu()) for k, v in inp.items()}
+
+    def f64(t):
+        return None if t is None else t.to(torch.float64).numpy()
+
+    def experts(e):
+        return f64(cpu["w1"][e]), f64(cpu["w3"][e]), f64(cpu["w2"][e])
+
+    shared = [(f64(cpu["ws1"][0]), f64(cpu["ws3"][0]), f64(cpu["ws2"][0]))] if w.n_shared else []
+    torch_threads = torch.get_num_threads()
+    torch.set_num_threads(1)
+    try:
+        with threadpool_limits(limits=1):
+            t0 = time.perf_counter()
+            y, info = O.moe_forward(f64(cpu["x"]), f64(cpu["w_gate"]), experts, w.E, w.k,
+                                    logit_bias=f64(cpu["logit_bias"]), sel_bias=f64(cpu["sel_bias"]),
+                                    shared=shared, capacity_factor=w.capacity_factor)
+            O.balance(info["counts_pre"], info["probs"], S, w.k)
+            dt = time.perf_counter() - t0
+    finally:
+        torch.set_num_threads(torch_threads)
+    assert np.isfinite(y).all()
+    return {"value": S / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "sample": f"first {S} of {w.T} tokens of {w.name}, every expert's full weights "
+                      f"(fp64 up-cast included), route+align+experts+combine+balance; {dt:.1f} s",
+            "seconds": dt}
+
+
+# ----------------------------------------------------------------------------- main
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixtral_prefill")
+    ap.add_argument("--cpu-sample", type=int, default=64,
+                    help="tokens of the workload the CPU oracle baseline runs on")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
+              "(the layer is built and measured on a single MI355X).", file=sys.stderr)
+        return 2
+
+    import torch
+    import workloads
+    import mixture_experts_layer_44_amd as moe
+
+    w = workloads.get(args.workload)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"[bench] workload {w}")
+    t0 = time.time()
+    inp = workloads.generate(w, device=dev)
+    torch.cuda.synchronize()
+    log(f"[bench] inputs generated in {time.time() - t0:.1f} s")
+    p = moe.problem_for(w)
+    ws = torch.empty(moe.workspace_bytes(p), dtype=torch.uint8, device=dev)
+    y = torch.empty((w.T, w.d), dtype=torch.float32, device=dev)
+    g = inp
+    kw = dict(logit_bias=g["logit_bias"], sel_bias=g["sel_bias"], ws1=g["ws1"], ws3=g["ws3"],
+              ws2=g["ws2"], ws=ws)
+
+    # routing of this batch (for the algorithmic work); identical in every step
+    _, r = moe.forward(p, g["x"], g["w_gate"], g["w1"], g["w3"], g["w2"], return_routing=True, y=y,
+                       **kw)
+    counts = r["counts"].cpu().tolist()
+    del r
+
+    n_ev = 7
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
+    stream = torch.cuda.current_stream(dev)
+    for evs in events:                       # materialise the HIP event handles
+        for e in evs:
+            e.record(stream)
+    torch.cuda.synchronize()
+    handles = [[e.cuda_event for e in evs] for evs in events]
+
+    for _ in range(args.warmup):
+        moe.forward_staged(p, g["x"], g["w_gate"], g["w1"], g["w3"], g["w2"], handles[0], y=y, **kw)
+    torch.cuda.synchronize()
+    log(f"[bench] warm-up done ({args.warmup} steps)")
+
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        moe.forward_staged(p, g["x"], g["w_gate"], g["w1"], g["w3"], g["w2"], handles[s], y=y, **kw)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    tokens_per_s = w.T * args.steps / elapsed
+    assert torch.isfinite(y).all().item()
+
+    stage_ms = {}
+    for i, name in enumerate(moe.STAGES):
+        vals = [events[s][i].elapsed_time(events[s][i + 1]) for s in range(args.steps)]
+        stage_ms[name] = sum(vals) / len(vals)
+    log("[bench] stage ms: " + ", ".join(f"{k}={v:.4f}" for k, v in stage_ms.items()))
+    log(f"[bench] {ms_per_step:.4f} ms/step, {tokens_per_s:,.0f} tokens/s")
+
+    # dominant kernel roofline
+    dom = max(("gate_up", "down"), key=lambda s: stage_ms[s])
+    kwk = kernel_work(w, counts, dom)
+    t_dom = stage_ms[dom] * 1e-3
+    ai = kwk["flops"] / kwk["bytes"]
+    bf16 = w.dtype == "bf16"
+    if ai >= RIDGE and bf16:
+        roof = {"bound": "mfma", "achieved": kwk["flops"] / t_dom / 1e12, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s"}
+    elif not bf16:
+        roof = {"bound": "alu", "achieved": kwk["flops"] / t_dom / 1e12, "peak": PEAK_F32_TFLOPS,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": kwk["bytes"] / t_dom / 1e9, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = traffic_from_profile(dom, w.name)
+    roof["kernel"] = KERNEL_NAMES[dom]
+    roof["avg_launch_ms"] = stage_ms[dom]
+    roof["algorithmic_per_launch"] = {"flops": kwk["flops"], "bytes": kwk["bytes"]}
+
+    lw = algorithmic_work(w, counts)
+    t_layer = ms_per_step * 1e-3
+    layer = {"flops": lw["flops"], "bytes": lw["bytes"], "kept_rows": lw["kept"],
+             "touched_experts": lw["touched"],
+             "mfma_frac": lw["flops"] / t_layer / (PEAK_BF16_TFLOPS * 1e12),
+             "hbm_frac": lw["bytes"] / t_layer / (PEAK_HBM_GBS * 1e9),
+             "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()}}
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"[bench] CPU oracle baseline on {args.cpu_sample} tokens ...")
+        cpu = cpu_baseline(w, inp, args.cpu_sample)
+        log(f"[bench] CPU oracle: {cpu['value']:.2f} tokens/s ({cpu['seconds']:.1f} s)")
+        cpu.pop("seconds")
+
+    cfg = {"workload": w.name, "T": w.T, "d": w.d, "E": w.E, "k": w.k, "d_ff": w.d_ff,
+           "n_shared": w.n_shared, "capacity_factor": w.capacity_factor, "seed": w.seed}
+    line = {"metric": METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "bf16" if bf16 else "f32", "data": "synthetic", "config": cfg,
+            "roofline": roof, "cpu_baseline": cpu, "layer": layer}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

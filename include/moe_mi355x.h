@@ -1,0 +1,186 @@
+/*
+ * moe_mi355x.h -- C ABI of the sparse top-k MoE layer forward on one MI355X (gfx950).
+ *
+ * The layer (pages cited by title and section):
+ *   router scores x . W_gate, softmax, top-k with renormalised gates and an
+ *   optional selection-only per-expert bias ("MoE Architecture" §2 "The
+ *   Router"; "Mixture of experts (MoE)" handbook, "Structure" and "Load
+ *   balancing"); grouping of the T*k assignments by expert with an optional
+ *   capacity limit that drops overflow (handbook, "Implementation: token by
+ *   token vs. grouped by expert"; "MoE Architecture" §2 "Expert capacity and
+ *   token dropping"); one SwiGLU FFN per expert over its contiguous segment
+ *   ("MoE Architecture" §3 "Standard MoE"); the gate-weighted combine back to
+ *   token order plus an always-on shared expert ("MoE Architecture" §1 and §3
+ *   "Shared Experts (DeepSeek)").
+ *
+ * Conventions for every call below:
+ *   - Every array argument is a DEVICE pointer owned by the caller; the
+ *     library never allocates or frees device memory and keeps no pointer
+ *     after returning. Row-major, densely packed.
+ *   - Weights use the "out x in" layout of a linear layer: w_gate [E,d],
+ *     w1 (gate proj, through SiLU) and w3 (up proj) [E,d_ff,d], w2 (down
+ *     proj) [E,d,d_ff]; the shared expert's ws1/ws3 [d_ff_shared,d] and ws2
+ *     [d,d_ff_shared].
+ *   - x and all weights are stored in problem->dtype (bf16 or fp32);
+ *     accumulation is fp32; gates, probabilities, expert output rows and y
+ *     are fp32; ids, counts and positions are int32.
+ *   - Flat assignment index a = t*k + j (token t, slot j).
+ *   - All work is enqueued on `stream` in order; nothing synchronises the host.
+ *   - Argument errors return before anything is enqueued. MOE_EHIP means a
+ *     launch failed. Faults inside kernels surface at the caller's next
+ *     synchronisation. The library is stateless: calls on different streams
+ *     with different workspaces may run concurrently.
+ *   - `ws` is caller-provided device scratch of at least
+ *     moe_workspace_bytes() bytes (any 256-byte-aligned buffer); its contents
+ *     on entry are ignored.
+ *   - Limits (else MOE_EUNSUPPORTED): 1 <= k <= E <= 256, k <= 32; T >= 0 and
+ *     T*k < 2^31; n_shared in {0,1} with d_ff_shared == d_ff when 1; bf16:
+ *     d and d_ff multiples of 128; fp32: d a multiple of 4.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_EINVAL = 1,        /* null pointer where one is required, negative size, bad enum */
+  MOE_EUNSUPPORTED = 2,  /* a shape outside the limits above */
+  MOE_EWORKSPACE = 3,    /* ws_bytes smaller than moe_workspace_bytes() */
+  MOE_EHIP = 4           /* a HIP launch or runtime call failed */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1 } moe_dtype;
+
+typedef struct {
+  int32_t T;               /* tokens */
+  int32_t d;               /* hidden size */
+  int32_t E;               /* routed experts */
+  int32_t k;               /* experts per token */
+  int32_t d_ff;            /* routed-expert intermediate size */
+  int32_t n_shared;        /* always-on shared experts: 0 or 1 */
+  int32_t d_ff_shared;     /* shared-expert intermediate size (== d_ff when n_shared = 1) */
+  int32_t dtype;           /* moe_dtype: storage of x and every weight */
+  double capacity_factor;  /* <= 0: no limit; else cap = ceil(capacity_factor * (T*k) / E),
+                              evaluated in IEEE double in that order */
+} moe_problem;
+
+/* Host-only helpers (no HIP call, no GPU needed). */
+const char* moe_status_str(int status);
+/* Checks every field against the limits above. */
+moe_status moe_validate(const moe_problem* p);
+/* Capacity limit in assignments per expert, or -1 for no limit
+   ("Mixture of Experts" notes, "How it works": capacity factor times the
+   average load per expert; the average with top-k routing is T*k/E). */
+moe_status moe_capacity(const moe_problem* p, int32_t* cap_out);
+/* Scratch bytes any entry point below may need for problem p (the maximum
+   over all of them, moe_forward included). */
+moe_status moe_workspace_bytes(const moe_problem* p, size_t* bytes_out);
+
+/* Router: logits l = x . w_gate^T (+ logit_bias), p = softmax(l) over the E
+   experts, keys = l (+ sel_bias), the k largest keys per token in descending
+   order (equal keys: lower expert index first), gates = p at those experts
+   divided by their sum ("MoE (Mixture of Experts) Deep Dive", "Router Network
+   Computation" and "Weighted Sum Output"; "MoE Architecture" §2 "Gating
+   Function"). sel_bias only chooses experts, never enters gates or p
+   (handbook "Load balancing": the DeepSeek-V3 bias).
+     x [T,d] dtype; w_gate [E,d] dtype; logit_bias [E] fp32 or NULL;
+     sel_bias [E] fp32 or NULL;
+     topk_ids [T,k] int32 out; topk_w [T,k] fp32 out;
+     prob_sum [E] fp32 out or NULL: sum over tokens of p[t,e]. */
+moe_status moe_route(const moe_problem* p, const void* x, const void* w_gate,
+                     const float* logit_bias, const float* sel_bias,
+                     int32_t* topk_ids, float* topk_w, float* prob_sum,
+                     void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Grouping by expert (handbook "Implementation: token by token vs. grouped
+   by expert": per-expert count is a histogram, segment starts a prefix sum,
+   assignments sorted stably by expert). Assignment a is kept iff fewer than
+   cap earlier assignments (smaller a) chose its expert; dropped assignments
+   contribute nothing ("MoE Architecture" §2 "Expert capacity and token
+   dropping"). Bit-exact and deterministic.
+     topk_ids [T,k] int32 in, each in [0,E) (an id outside that range is
+       treated as dropped and counted nowhere);
+     counts_pre [E] out: assignments per expert before dropping;
+     counts [E] out: kept per expert; offsets [E+1] out: exclusive prefix of counts;
+     sorted_assign [T*k] out: flat a of kept assignments, expert-major,
+       ascending a inside an expert; the first offsets[E] entries are valid;
+     assign_pos [T*k] out: row of a in sorted order, -1 if dropped. */
+moe_status moe_align(const moe_problem* p, const int32_t* topk_ids,
+                     int32_t* counts_pre, int32_t* counts, int32_t* offsets,
+                     int32_t* sorted_assign, int32_t* assign_pos,
+                     void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Expert FFNs: for each kept assignment row r of expert e (token t =
+   sorted_assign[r] / k), out_rows[r] = w2_e (SiLU(w1_e x_t) * (w3_e x_t))
+   ("MoE Architecture" §3 "Standard MoE": SwiGLU experts; handbook Expert:
+   gate, up and down projections). With a shared expert, shared_out[t] is the
+   same FFN with ws1/ws3/ws2 on every token ("MoE Architecture" §3 "Shared
+   Experts (DeepSeek)").
+     x [T,d]; w1,w3 [E,d_ff,d]; w2 [E,d,d_ff]; ws1,ws3,ws2 or NULL (n_shared=0);
+     sorted_assign, offsets as produced by moe_align;
+     out_rows [T*k,d] fp32 out (rows >= offsets[E] untouched);
+     shared_out [T,d] fp32 out, or NULL when n_shared = 0. */
+moe_status moe_expert_ffn(const moe_problem* p, const void* x,
+                          const void* w1, const void* w3, const void* w2,
+                          const void* ws1, const void* ws3, const void* ws2,
+                          const int32_t* sorted_assign, const int32_t* offsets,
+                          float* out_rows, float* shared_out,
+                          void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Combine: y[t] = sum over slots j with assign_pos[t*k+j] >= 0 of
+   topk_w[t*k+j] * out_rows[assign_pos[t*k+j]], plus shared_out[t] if given
+   ("MoE Architecture" §1: y is the gate-weighted sum of the chosen experts;
+   dropped slots add nothing and the remaining gates are not renormalised).
+     y [T,d] fp32 out. */
+moe_status moe_combine(const moe_problem* p, const float* out_rows, const int32_t* assign_pos,
+                       const float* topk_w, const float* shared_out, float* y,
+                       hipStream_t stream);
+
+/* Balance statistics: f[e] = counts_pre[e] / (T*k), P[e] = prob_sum[e] / T,
+   L = alpha * E * sum_e f[e] * P[e] ("MoE Architecture" §2 "Load Balancing";
+   the Deep Dive's "Load Balancing Loss Derivation" has the same form).
+     f [E], P [E], L [1] fp32 out. */
+moe_status moe_balance(const moe_problem* p, const int32_t* counts_pre, const float* prob_sum,
+                       float alpha, float* f, float* P, float* L, hipStream_t stream);
+
+/* The whole layer in one call: route -> align -> expert FFNs -> combine.
+   y [T,d] fp32 out (required). Every routing output pointer may be NULL, in
+   which case it lives in ws; when given, it receives the same values the
+   separate calls above would produce. */
+moe_status moe_forward(const moe_problem* p, const void* x, const void* w_gate,
+                       const float* logit_bias, const float* sel_bias,
+                       const void* w1, const void* w3, const void* w2,
+                       const void* ws1, const void* ws3, const void* ws2,
+                       float* y,
+                       int32_t* topk_ids, float* topk_w, float* prob_sum,
+                       int32_t* counts_pre, int32_t* counts, int32_t* offsets,
+                       int32_t* sorted_assign, int32_t* assign_pos,
+                       void* ws, size_t ws_bytes, hipStream_t stream);
+
+/* Per-stage timing of moe_forward, for measurement tools. Same computation and
+   kernels as moe_forward (routing outputs stay in ws), and additionally records
+   caller-created HIP events on `stream`: stage_events[0] before the router,
+   then one after each stage -- [1] route, [2] align, [3] GEMM schedule,
+   [4] gate-up GEMM (+SwiGLU), [5] down GEMM, [6] combine. The caller owns
+   the events (hipEventCreate) and reads them with hipEventElapsedTime after
+   synchronising. Returns MOE_EINVAL if stage_events or any of its
+   MOE_STAGE_EVENTS entries is NULL. */
+#define MOE_STAGE_EVENTS 7
+moe_status moe_forward_staged(const moe_problem* p, const void* x, const void* w_gate,
+                              const float* logit_bias, const float* sel_bias,
+                              const void* w1, const void* w3, const void* w2,
+                              const void* ws1, const void* ws3, const void* ws2, float* y,
+                              void* ws, size_t ws_bytes, hipStream_t stream,
+                              hipEvent_t* stage_events);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

@@ -1,0 +1,285 @@
+// C ABI of libmoe_mi355x: argument validation, workspace layout and the stream-ordered
+// launch sequence route -> align -> schedule -> gate-up GEMM -> down GEMM -> combine.
+// Validation never touches the GPU, so invalid calls return before anything is enqueued.
+#include <climits>
+#include <cmath>
+
+#include "moe_internal.h"
+
+#define MOE_API extern "C" __attribute__((visibility("default")))
+
+namespace moe {
+namespace {
+
+struct Layout {
+  size_t psum_part, blk_counts, blk_base, grp_rows, grp_off, mt_start, mt_group, h;
+  size_t ids, gates, prob_sum, counts_pre, counts, offsets, sorted_assign, assign_pos;
+  size_t out_rows, shared_out;
+  size_t total;
+  int max_mt, BM;
+};
+
+Layout layout(const moe_problem& p) {
+  Layout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align_up(off + (bytes ? bytes : 1), 256);
+    return o;
+  };
+  const size_t n = (size_t)p.T * p.k;
+  const int G = p.E + p.n_shared;
+  const int nblk_route = ceil_div(p.T, kRouteTok);
+  const int nblk_align = ceil_div((int)n, kAlignChunk);
+  L.BM = p.dtype == MOE_BF16 ? kGemmBM : kGemmBM32;
+  L.max_mt = max_mtiles(p.T, p.k, p.E, p.n_shared, L.BM);
+  const size_t esz = p.dtype == MOE_BF16 ? 2 : 4;
+  L.psum_part = take((size_t)nblk_route * p.E * 4);
+  L.blk_counts = take((size_t)nblk_align * p.E * 4);
+  L.blk_base = take((size_t)nblk_align * p.E * 4);
+  L.grp_rows = take((size_t)G * 4);
+  L.grp_off = take((size_t)G * 4);
+  L.mt_start = take((size_t)(G + 1) * 4);
+  L.mt_group = take((size_t)L.max_mt * 4);
+  L.h = take((size_t)L.max_mt * L.BM * p.d_ff * esz);
+  L.ids = take(n * 4);
+  L.gates = take(n * 4);
+  L.prob_sum = take((size_t)p.E * 4);
+  L.counts_pre = take((size_t)p.E * 4);
+  L.counts = take((size_t)p.E * 4);
+  L.offsets = take((size_t)(p.E + 1) * 4);
+  L.sorted_assign = take(n * 4);
+  L.assign_pos = take(n * 4);
+  L.out_rows = take(n * p.d * 4);
+  L.shared_out = take((size_t)p.n_shared * p.T * p.d * 4);
+  L.total = off;
+  return L;
+}
+
+template <typename T>
+T* at(void* ws, size_t off) {
+  return (T*)((char*)ws + off);
+}
+
+Schedule schedule_in(const moe_problem& p, const Layout& L, void* ws) {
+  Schedule sc;
+  sc.grp_rows = at<int32_t>(ws, L.grp_rows);
+  sc.grp_off = at<int32_t>(ws, L.grp_off);
+  sc.mt_start = at<int32_t>(ws, L.mt_start);
+  sc.mt_group = at<int32_t>(ws, L.mt_group);
+  sc.max_mtiles = L.max_mt;
+  sc.G = p.E + p.n_shared;
+  sc.BM = L.BM;
+  return sc;
+}
+
+// cap as used by the kernels: -1 = none; clamped to T*k (an equivalent limit)
+int kernel_cap(const moe_problem& p) {
+  if (!(p.capacity_factor > 0)) return -1;
+  const double c = std::ceil(p.capacity_factor * (double)((long long)p.T * p.k) / (double)p.E);
+  const long long n = (long long)p.T * p.k;
+  return c >= (double)n ? (int)n : (int)c;
+}
+
+moe_status check_ws(const moe_problem& p, const void* ws, size_t ws_bytes) {
+  const size_t need = layout(p).total;
+  if (ws_bytes < need) return MOE_EWORKSPACE;
+  if (!ws) return MOE_EINVAL;
+  return MOE_OK;
+}
+
+inline moe_status hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_EHIP; }
+
+}  // namespace
+}  // namespace moe
+
+using namespace moe;
+
+MOE_API const char* moe_status_str(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_EINVAL: return "invalid argument";
+    case MOE_EUNSUPPORTED: return "unsupported shape";
+    case MOE_EWORKSPACE: return "workspace too small";
+    case MOE_EHIP: return "HIP launch or runtime error";
+    default: return "unknown status";
+  }
+}
+
+MOE_API moe_status moe_validate(const moe_problem* p) {
+  if (!p) return MOE_EINVAL;
+  if (p->T < 0 || p->d <= 0 || p->E <= 0 || p->k <= 0 || p->d_ff <= 0) return MOE_EINVAL;
+  if (p->dtype != MOE_F32 && p->dtype != MOE_BF16) return MOE_EINVAL;
+  if (p->n_shared < 0 || p->d_ff_shared < 0) return MOE_EINVAL;
+  if (!std::isfinite(p->capacity_factor)) return MOE_EINVAL;
+  if (p->E > 256 || p->k > p->E || p->k > 32) return MOE_EUNSUPPORTED;
+  if (p->n_shared > 1) return MOE_EUNSUPPORTED;
+  if (p->n_shared == 1 && p->d_ff_shared != p->d_ff) return MOE_EUNSUPPORTED;
+  if ((long long)p->T * p->k >= (long long)INT_MAX - 4096) return MOE_EUNSUPPORTED;
+  if ((long long)p->T * p->d >= (1ll << 40)) return MOE_EUNSUPPORTED;
+  if (p->dtype == MOE_BF16 && (p->d % 128 || p->d_ff % 128)) return MOE_EUNSUPPORTED;
+  if (p->dtype == MOE_F32 && p->d % 4) return MOE_EUNSUPPORTED;
+  return MOE_OK;
+}
+
+MOE_API moe_status moe_capacity(const moe_problem* p, int32_t* cap_out) {
+  moe_status st = moe_validate(p);
+  if (st != MOE_OK) return st;
+  if (!cap_out) return MOE_EINVAL;
+  if (!(p->capacity_factor > 0)) {
+    *cap_out = -1;
+    return MOE_OK;
+  }
+  const double c = std::ceil(p->capacity_factor * (double)((long long)p->T * p->k) / (double)p->E);
+  *cap_out = c >= (double)INT_MAX ? INT_MAX : (int32_t)c;
+  return MOE_OK;
+}
+
+MOE_API moe_status moe_workspace_bytes(const moe_problem* p, size_t* bytes_out) {
+  moe_status st = moe_validate(p);
+  if (st != MOE_OK) return st;
+  if (!bytes_out) return MOE_EINVAL;
+  *bytes_out = layout(*p).total;
+  return MOE_OK;
+}
+
+MOE_API moe_status moe_route(const moe_problem* p, const void* x, const void* w_gate,
+                             const float* logit_bias, const float* sel_bias, int32_t* topk_ids,
+                             float* topk_w, float* prob_sum, void* ws, size_t ws_bytes,
+                             hipStream_t stream) {
+  moe_status st = moe_validate(p);
+  if (st != MOE_OK) return st;
+  const bool hasT = p->T > 0;
+  if (!w_gate || (hasT && (!x || !topk_ids || !topk_w))) return MOE_EINVAL;
+  if ((st = check_ws(*p, ws, ws_bytes)) != MOE_OK) return st;
+  const Layout L = layout(*p);
+  return hip_status(launch_route(*p, x, w_gate, logit_bias, sel_bias, topk_ids, topk_w, prob_sum,
+                                 at<float>(ws, L.psum_part), stream));
+}
+
+MOE_API moe_status moe_align(const moe_problem* p, const int32_t* topk_ids, int32_t* counts_pre,
+                             int32_t* counts, int32_t* offsets, int32_t* sorted_assign,
+                             int32_t* assign_pos, void* ws, size_t ws_bytes, hipStream_t stream) {
+  moe_status st = moe_validate(p);
+  if (st != MOE_OK) return st;
+  const bool hasT = p->T > 0;
+  if (!counts_pre || !counts || !offsets) return MOE_EINVAL;
+  if (hasT && (!topk_ids || !sorted_assign || !assign_pos)) return MOE_EINVAL;
+  if ((st = check_ws(*p, ws, ws_bytes)) != MOE_OK) return st;
+  const Layout L = layout(*p);
+  return hip_status(launch_align(*p, kernel_cap(*p), topk_ids, counts_pre, counts, offsets,
+                                 sorted_assign, assign_pos, at<int32_t>(ws, L.blk_counts),
+                                 at<int32_t>(ws, L.blk_base), stream));
+}
+
+MOE_API moe_status moe_expert_ffn(const moe_problem* p, const void* x, const void* w1,
+                                  const void* w3, const void* w2, const void* ws1, const void* ws3,
+                                  const void* ws2, const int32_t* sorted_assign,
+                                  const int32_t* offsets, float* out_rows, float* shared_out,
+                                  void* ws, size_t ws_bytes, hipStream_t stream) {
+  moe_status st = moe_validate(p);
+  if (st != MOE_OK) return st;
+  const bool hasT = p->T > 0;
+  if (!w1 || !w3 || !w2 || !offsets) return MOE_EINVAL;
+  if (hasT && (!x || !sorted_assign || !out_rows)) return MOE_EINVAL;
+  if (p->n_shared && (!ws1 || !ws3 || !ws2 || (hasT && !shared_out))) return MOE_EINVAL;
+  if ((st = check_ws(*p, ws, ws_bytes)) != MOE_OK) return st;
+  const Layout L = layout(*p);
+  const Schedule sc = schedule_in(*p, L, ws);
+  hipError_t e = launch_schedule(*p, offsets, sc, stream);
+  if (e != hipSuccess) return MOE_EHIP;
+  return hip_status(launch_expert_ffn(*p, x, w1, w3, w2, ws1, ws3, ws2, sorted_assign, sc,
+                                      at<void>(ws, L.h), out_rows, shared_out, stream));
+}
+
+MOE_API moe_status moe_combine(const moe_problem* p, const float* out_rows,
+                               const int32_t* assign_pos, const float* topk_w,
+                               const float* shared_out, float* y, hipStream_t stream) {
+  moe_status st = moe_validate(p);
+  if (st != MOE_OK) return st;
+  if (p->T > 0 && (!out_rows || !assign_pos || !topk_w || !y)) return MOE_EINVAL;
+  if (p->T > 0 && p->n_shared && !shared_out) return MOE_EINVAL;
+  return hip_status(launch_combine(*p, out_rows, assign_pos, topk_w, shared_out, y, stream));
+}
+
+MOE_API moe_status moe_balance(const moe_problem* p, const int32_t* counts_pre,
+                               const float* prob_sum, float alpha, float* f, float* P, float* L,
+                               hipStream_t stream) {
+  moe_status st = moe_validate(p);
+  if (st != MOE_OK) return st;
+  if (!counts_pre || !prob_sum || !f || !P || !L) return MOE_EINVAL;
+  if (!std::isfinite(alpha)) return MOE_EINVAL;
+  return hip_status(launch_balance(*p, counts_pre, prob_sum, alpha, f, P, L, stream));
+}
+
+namespace {
+
+moe_status forward_impl(const moe_problem* p, const void* x, const void* w_gate,
+                        const float* logit_bias, const float* sel_bias, const void* w1,
+                        const void* w3, const void* w2, const void* ws1, const void* ws3,
+                        const void* ws2, float* y, int32_t* topk_ids, float* topk_w,
+                        float* prob_sum, int32_t* counts_pre, int32_t* counts, int32_t* offsets,
+                        int32_t* sorted_assign, int32_t* assign_pos, void* ws, size_t ws_bytes,
+                        hipStream_t stream, hipEvent_t* ev) {
+  moe_status st = moe_validate(p);
+  if (st != MOE_OK) return st;
+  const bool hasT = p->T > 0;
+  if (!w_gate || !w1 || !w3 || !w2 || (hasT && (!x || !y))) return MOE_EINVAL;
+  if (p->n_shared && (!ws1 || !ws3 || !ws2)) return MOE_EINVAL;
+  if ((st = check_ws(*p, ws, ws_bytes)) != MOE_OK) return st;
+  const Layout L = layout(*p);
+  int32_t* ids = topk_ids ? topk_ids : at<int32_t>(ws, L.ids);
+  float* gates = topk_w ? topk_w : at<float>(ws, L.gates);
+  int32_t* cpre = counts_pre ? counts_pre : at<int32_t>(ws, L.counts_pre);
+  int32_t* cnt = counts ? counts : at<int32_t>(ws, L.counts);
+  int32_t* offs = offsets ? offsets : at<int32_t>(ws, L.offsets);
+  int32_t* sa = sorted_assign ? sorted_assign : at<int32_t>(ws, L.sorted_assign);
+  int32_t* ap = assign_pos ? assign_pos : at<int32_t>(ws, L.assign_pos);
+  float* out_rows = at<float>(ws, L.out_rows);
+  float* shared_out = p->n_shared ? at<float>(ws, L.shared_out) : nullptr;
+  auto mark = [&](int i) { return ev ? hipEventRecord(ev[i], stream) : hipSuccess; };
+  if (mark(0) != hipSuccess) return MOE_EHIP;
+  hipError_t e = launch_route(*p, x, w_gate, logit_bias, sel_bias, ids, gates, prob_sum,
+                              at<float>(ws, L.psum_part), stream);
+  if (e != hipSuccess || mark(1) != hipSuccess) return MOE_EHIP;
+  e = launch_align(*p, kernel_cap(*p), ids, cpre, cnt, offs, sa, ap, at<int32_t>(ws, L.blk_counts),
+                   at<int32_t>(ws, L.blk_base), stream);
+  if (e != hipSuccess || mark(2) != hipSuccess) return MOE_EHIP;
+  const Schedule sc = schedule_in(*p, L, ws);
+  if (launch_schedule(*p, offs, sc, stream) != hipSuccess || mark(3) != hipSuccess)
+    return MOE_EHIP;
+  e = launch_expert_ffn(*p, x, w1, w3, w2, ws1, ws3, ws2, sa, sc, at<void>(ws, L.h), out_rows,
+                        shared_out, stream, ev ? ev[4] : nullptr);
+  if (e != hipSuccess || mark(5) != hipSuccess) return MOE_EHIP;
+  e = launch_combine(*p, out_rows, ap, gates, shared_out, y, stream);
+  if (e != hipSuccess || mark(6) != hipSuccess) return MOE_EHIP;
+  return MOE_OK;
+}
+
+}  // namespace
+
+MOE_API moe_status moe_forward(const moe_problem* p, const void* x, const void* w_gate,
+                               const float* logit_bias, const float* sel_bias, const void* w1,
+                               const void* w3, const void* w2, const void* ws1, const void* ws3,
+                               const void* ws2, float* y, int32_t* topk_ids, float* topk_w,
+                               float* prob_sum, int32_t* counts_pre, int32_t* counts,
+                               int32_t* offsets, int32_t* sorted_assign, int32_t* assign_pos,
+                               void* ws, size_t ws_bytes, hipStream_t stream) {
+  return forward_impl(p, x, w_gate, logit_bias, sel_bias, w1, w3, w2, ws1, ws3, ws2, y, topk_ids,
+                      topk_w, prob_sum, counts_pre, counts, offsets, sorted_assign, assign_pos, ws,
+                      ws_bytes, stream, nullptr);
+}
+
+MOE_API moe_status moe_forward_staged(const moe_problem* p, const void* x, const void* w_gate,
+                                      const float* logit_bias, const float* sel_bias,
+                                      const void* w1, const void* w3, const void* w2,
+                                      const void* ws1, const void* ws3, const void* ws2, float* y,
+                                      void* ws, size_t ws_bytes, hipStream_t stream,
+                                      hipEvent_t* stage_events) {
+  if (!stage_events) return MOE_EINVAL;
+  for (int i = 0; i < MOE_STAGE_EVENTS; ++i)
+    if (!stage_events[i]) return MOE_EINVAL;
+  return forward_impl(p, x, w_gate, logit_bias, sel_bias, w1, w3, w2, ws1, ws3, ws2, y, nullptr,
+                      nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, ws, ws_bytes,
+                      stream, stage_events);
+}

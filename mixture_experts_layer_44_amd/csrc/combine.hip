@@ -1,0 +1,91 @@
+// Gate-weighted combine back to token order, and the balance statistics.
+//
+// Pages: "MoE Architecture" §1 (y is the sum over the chosen experts of gate times expert
+// output) and §3 "Shared Experts (DeepSeek)" (shared experts are added to the routed sum);
+// "Mixture of experts (MoE)" handbook, "Implementation" (results are scattered back to
+// their original positions with their weights); "MoE Architecture" §2 "Load Balancing"
+// (L = alpha * E * sum_i f_i p_i).
+//
+// combine: one workgroup per token row, 16-byte loads/stores along d; slots are added in
+// slot order after the shared row, so y is bit-reproducible from run to run.
+#include "moe_internal.h"
+
+namespace moe {
+
+namespace {
+
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ out_rows,
+                                                      const int32_t* __restrict__ assign_pos,
+                                                      const float* __restrict__ topk_w,
+                                                      const float* __restrict__ shared_out, int d,
+                                                      int k, float* __restrict__ y) {
+  const int t = blockIdx.x;
+  const int n = gridDim.x * k;   // rows of out_rows that can exist: T*k
+  __shared__ int pos[32];
+  __shared__ float wt[32];
+  if (threadIdx.x < k) {
+    pos[threadIdx.x] = assign_pos[(size_t)t * k + threadIdx.x];
+    wt[threadIdx.x] = topk_w[(size_t)t * k + threadIdx.x];
+  }
+  __syncthreads();
+  const int d4 = d >> 2;
+  for (int c = threadIdx.x; c < d4; c += 256) {
+    f32x4 acc = shared_out ? *(const f32x4*)(shared_out + (size_t)t * d + 4 * c)
+                           : f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < k; ++j) {
+      const int r = pos[j];
+      if (r >= 0 && r < n) {
+        const f32x4 v = *(const f32x4*)(out_rows + (size_t)r * d + 4 * c);
+        const float g = wt[j];
+        acc[0] = fmaf(g, v[0], acc[0]);
+        acc[1] = fmaf(g, v[1], acc[1]);
+        acc[2] = fmaf(g, v[2], acc[2]);
+        acc[3] = fmaf(g, v[3], acc[3]);
+      }
+    }
+    *(f32x4*)(y + (size_t)t * d + 4 * c) = acc;
+  }
+}
+
+__global__ __launch_bounds__(256) void balance_kernel(const int32_t* __restrict__ counts_pre,
+                                                      const float* __restrict__ prob_sum, int T,
+                                                      int k, int E, float alpha,
+                                                      float* __restrict__ f, float* __restrict__ P,
+                                                      float* __restrict__ L) {
+  __shared__ double part[256];
+  const int e = threadIdx.x;
+  double fp = 0.0;
+  if (e < E) {
+    const double fe = T > 0 ? (double)counts_pre[e] / ((double)T * k) : 0.0;
+    const double pe = T > 0 ? (double)prob_sum[e] / (double)T : 0.0;
+    f[e] = (float)fe;
+    P[e] = (float)pe;
+    fp = fe * pe;
+  }
+  part[e] = fp;
+  __syncthreads();
+  for (int o = 128; o > 0; o >>= 1) {
+    if (e < o) part[e] += part[e + o];
+    __syncthreads();
+  }
+  if (e == 0) L[0] = (float)((double)alpha * E * part[0]);
+}
+
+}  // namespace
+
+hipError_t launch_combine(const moe_problem& p, const float* out_rows, const int32_t* assign_pos,
+                          const float* topk_w, const float* shared_out, float* y, hipStream_t s) {
+  if (p.T == 0) return hipSuccess;
+  hipLaunchKernelGGL(combine_kernel, dim3(p.T), dim3(256), 0, s, out_rows, assign_pos, topk_w,
+                     shared_out, p.d, p.k, y);
+  return hipGetLastError();
+}
+
+hipError_t launch_balance(const moe_problem& p, const int32_t* counts_pre, const float* prob_sum,
+                          float alpha, float* f, float* P, float* L, hipStream_t s) {
+  hipLaunchKernelGGL(balance_kernel, dim3(1), dim3(256), 0, s, counts_pre, prob_sum, p.T, p.k, p.E,
+                     alpha, f, P, L);
+  return hipGetLastError();
+}
+
+}  // namespace moe

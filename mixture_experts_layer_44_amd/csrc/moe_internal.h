@@ -1,0 +1,77 @@
+// Internal declarations shared by the HIP translation units of libmoe_mi355x.
+// Not part of the C ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/moe_mi355x.h"
+
+namespace moe {
+
+typedef uint16_t bf16_t;  // raw bf16 storage
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t v) { return __uint_as_float((uint32_t)v << 16); }
+
+// fp32 -> bf16, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (bf16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (bf16_t)(u >> 16);
+}
+
+// ---------------------------------------------------------------- tiling constants
+constexpr int kRouteTok = 16;        // tokens per router workgroup
+constexpr int kAlignChunk = 1024;    // assignments per align workgroup
+constexpr int kGemmBM = 128;         // rows per grouped-GEMM m-tile (bf16 path)
+constexpr int kGemmBM32 = 64;        // rows per m-tile (fp32 path)
+
+inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// ---------------------------------------------------------------- schedule
+// Grouped-GEMM work list built on the device from the align offsets. Groups
+// 0..E-1 are the routed experts, group E the shared expert (if any).
+struct Schedule {
+  int32_t* grp_rows;   // [G]   rows (kept assignments, or T for the shared expert)
+  int32_t* grp_off;    // [G]   first row in sorted order (routed), 0 for shared
+  int32_t* mt_start;   // [G+1] exclusive prefix of ceil(rows/BM); mt_start[G] = total m-tiles
+  int32_t* mt_group;   // [max_mtiles] group of each m-tile
+  int max_mtiles;
+  int G;
+  int BM;
+};
+
+int max_mtiles(int T, int k, int E, int n_shared, int BM);
+
+// ---------------------------------------------------------------- launchers
+hipError_t launch_route(const moe_problem& p, const void* x, const void* w_gate,
+                        const float* logit_bias, const float* sel_bias, int32_t* ids,
+                        float* gates, float* prob_sum, float* psum_part, hipStream_t s);
+
+hipError_t launch_align(const moe_problem& p, int cap, const int32_t* ids, int32_t* counts_pre,
+                        int32_t* counts, int32_t* offsets, int32_t* sorted_assign,
+                        int32_t* assign_pos, int32_t* blk_counts, int32_t* blk_base, hipStream_t s);
+
+hipError_t launch_schedule(const moe_problem& p, const int32_t* offsets, const Schedule& sc,
+                           hipStream_t s);
+
+hipError_t launch_expert_ffn(const moe_problem& p, const void* x, const void* w1, const void* w3,
+                             const void* w2, const void* ws1, const void* ws3, const void* ws2,
+                             const int32_t* sorted_assign, const Schedule& sc, void* h,
+                             float* out_rows, float* shared_out, hipStream_t s,
+                             hipEvent_t between = nullptr);
+
+hipError_t launch_combine(const moe_problem& p, const float* out_rows, const int32_t* assign_pos,
+                          const float* topk_w, const float* shared_out, float* y, hipStream_t s);
+
+hipError_t launch_balance(const moe_problem& p, const int32_t* counts_pre, const float* prob_sum,
+                          float alpha, float* f, float* P, float* L, hipStream_t s);
+
+}  // namespace moe

@@ -42,7 +42,7 @@ import numpy as np
 __all__ = [
     "router_logits", "softmax", "selection_keys", "select_topk", "renormalised_gates",
     "route", "capacity", "align", "silu", "swiglu_expert", "moe_forward",
-    "moe_forward_naive", "token_output", "balance", "expert_table",
+    "moe_forward_naive", "token_output", "token_outputs", "balance", "expert_table",
 ]
 
 ExpertFn = Callable[[int], Tuple[np.ndarray, np.ndarray, np.ndarray]]
@@ -249,6 +249,25 @@ def token_output(x_t: np.ndarray, ids_t, gates_t, kept_t, experts: ExpertFn,
         if kept_t[j]:
             y += float(gates_t[j]) * swiglu_expert(x_t, *experts(int(ids_t[j])))[0]
     y += _shared_sum(x_t, shared)[0]
+    return y
+
+
+def token_outputs(x_rows: np.ndarray, ids_rows, gates_rows, kept_rows, experts: ExpertFn,
+                  shared: Sequence = ()) -> np.ndarray:
+    """Outputs of a chosen subset of tokens, given each one's routing (ids,
+    gates, kept flags): the same weighted sum as token_output, visiting each
+    expert once for all the rows that chose it (so one expert's weights are
+    fetched once). Used to check sampled rows of a full-size layer."""
+    x_rows = np.asarray(x_rows, dtype=np.float64)
+    ids_rows = np.asarray(ids_rows, dtype=np.int64)
+    gates_rows = np.asarray(gates_rows, dtype=np.float64)
+    kept_rows = np.asarray(kept_rows, dtype=bool)
+    y = np.zeros_like(x_rows)
+    for e in np.unique(ids_rows[kept_rows]):
+        rows, slots = np.nonzero((ids_rows == e) & kept_rows)   # a row chooses e at most once
+        out = swiglu_expert(x_rows[rows], *experts(int(e)))
+        y[rows] += gates_rows[rows, slots][:, None] * out
+    y += _shared_sum(x_rows, shared)
     return y
 
 

@@ -1,0 +1,42 @@
+"""Pins for the benchmark's algorithmic work model (CPU only)."""
+import bench
+import workloads
+from util import golden
+
+
+def test_expert_params_handbook_exercise():
+    """Handbook exercise 1: 64 experts of 3*2048*1408, top-8, 24 layers ->
+    13.29B expert parameters in total, 1.66B activated per token."""
+    g = golden("param_accounting_handbook.json")
+    per = bench.expert_params(g["d"], g["d_ff"])
+    assert per == 3 * 2048 * 1408 == 8_650_752
+    assert round(g["E"] * per * g["layers"] / 1e9, 2) == g["expected_total_billions"]
+    assert round(g["k"] * per * g["layers"] / 1e9, 2) == g["expected_active_billions"]
+
+
+def test_sparsity_ratio_arch():
+    """MoE Architecture §1: k=2 of E=64 experts is about 3% of expert parameters per token."""
+    g = golden("sparsity_ratio_arch.json")
+    per = bench.expert_params(4096, 1024)
+    assert round(100 * g["k"] * per / (g["E"] * per)) == g["expected_percent_rounded"]
+
+
+def test_algorithmic_work_mixtral_shape():
+    w = workloads.get("mixtral_prefill")
+    counts = [1024] * 8                       # every assignment kept, 8 experts touched
+    a = bench.algorithmic_work(w, counts)
+    assert a["flops"] == 2 * 4096 * 4096 * 8 + 6 * 4096 * 14336 * 8192
+    assert a["bytes"] == 4096 * 4096 * 2 + 8 * 4096 * 2 + 8 * 3 * 4096 * 14336 * 2 + 4096 * 4096 * 4
+    k = bench.kernel_work(w, counts, "gate_up")
+    assert k["flops"] == 4 * 4096 * 14336 * 8192
+    # only touched experts' weights count
+    b = bench.algorithmic_work(w, [2048, 0, 0, 0, 2048, 2048, 2048, 0])
+    assert b["touched"] == 4 and b["bytes"] < a["bytes"]
+
+
+def test_decode_t1_bytes():
+    """Decode T=1 reads 8 experts' full weights: 8 x 3 x 2048 x 768 x 2 B = 75.5 MB."""
+    w = workloads.get("decode_T1")
+    a = bench.algorithmic_work(w, [1] * 8 + [0] * 120)
+    assert a["touched"] == 8
+    assert abs(a["bytes"] - (8 * 3 * 2048 * 768 * 2 + 2048 * 2 + 128 * 2048 * 2 + 2048 * 4)) == 0

@@ -1,0 +1,219 @@
+"""HIP path vs the fp64 oracle, through the C ABI (needs an MI355X).
+
+Small problems are compared on every output row; the full-size workloads on
+every routing output (ids by the gap rule, grouping bit-exact) and on sampled
+rows of y, in the same launch configuration the benchmark times."""
+import dataclasses
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads
+from parity import run_parity
+from util import f64
+
+pytestmark = pytest.mark.gpu
+
+W = workloads.Workload
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+SMALL = [
+    workloads.get("tiny_fp32"),
+    workloads.get("handbook_fp32"),
+    W("bf16_ragged", T=300, d=256, E=16, k=4, d_ff=384, seed=101),
+    W("bf16_shared_selbias", T=257, d=384, E=32, k=8, d_ff=256, seed=102, n_shared=1,
+      d_ff_shared=256, sel_bias=True),
+    W("bf16_cap_zipf", T=500, d=256, E=16, k=2, d_ff=256, seed=103, capacity_factor=1.0, zipf_s=1.1),
+    W("bf16_dense_E1", T=200, d=256, E=1, k=1, d_ff=512, seed=104),
+    W("bf16_k_eq_E", T=100, d=128, E=8, k=8, d_ff=128, seed=105),
+    W("bf16_E256_T1", T=1, d=256, E=256, k=8, d_ff=128, seed=106),
+    W("bf16_empty", T=0, d=256, E=8, k=2, d_ff=256, seed=107),
+    W("bf16_cap1", T=64, d=128, E=4, k=2, d_ff=128, seed=108, capacity_factor=0.01),
+    W("bf16_many_tiles", T=1500, d=512, E=4, k=2, d_ff=640, seed=109, n_shared=1, d_ff_shared=640),
+    W("f32_ragged", T=77, d=100, E=5, k=3, d_ff=70, seed=110, dtype="f32", capacity_factor=0.9,
+      n_shared=1, d_ff_shared=70),
+]
+
+
+@pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
+def test_small_parity(w):
+    _say(f"[parity] {w}")
+    rep = run_parity(w, gen_device="cpu")
+    _say(str(rep))
+    assert rep.ok(w.dtype), str(rep)
+
+
+DECODE = [workloads.get(f"decode_T{T}") for T in (1, 8, 32, 128)]
+
+
+@pytest.mark.parametrize("w", DECODE, ids=[w.name for w in DECODE])
+def test_decode_parity(w):
+    _say(f"[parity] {w}")
+    rep = run_parity(w, gen_device="cuda")
+    _say(str(rep))
+    assert rep.ok(w.dtype), str(rep)
+
+
+FULL = [("mixtral_prefill", 48), ("skew_cap", 48), ("dsv3_fine", 12)]
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name,sample", FULL, ids=[f[0] for f in FULL])
+def test_full_size_parity(name, sample):
+    w = workloads.get(name)
+    _say(f"[parity] full {w} sample={sample}")
+    rep = run_parity(w, gen_device="cuda", sample=sample)
+    _say(str(rep) + f" timings={ {k: round(v, 1) for k, v in rep.timings.items()} }")
+    assert rep.rows_checked >= sample
+    assert rep.ok(w.dtype), str(rep)
+    if w.capacity_factor:
+        assert rep.dropped > 0
+    torch.cuda.empty_cache()
+
+
+# ---------------------------------------------------------------------------- align alone
+ALIGN_CASES = [
+    # (T, E, k, capacity_factor, skew)
+    (64, 8, 2, 0.0, 0.0),
+    (4096, 8, 2, 0.0, 0.0),
+    (4096, 256, 8, 0.0, 0.0),
+    (4096, 256, 8, 1.25, 1.0),
+    (1, 128, 8, 0.0, 0.0),
+    (8, 128, 8, 0.0, 0.0),
+    (128, 128, 8, 1.0, 0.5),
+    (16384, 64, 2, 1.25, 1.1),
+    (16384, 64, 2, 0.05, 1.1),
+    (1000, 1, 1, 0.0, 0.0),
+    (777, 13, 5, 0.7, 0.8),
+    (3, 256, 1, 0.0, 0.0),
+]
+
+
+def _ids(T, E, k, skew, seed):
+    rng = np.random.default_rng(seed)
+    pr = (np.arange(1, E + 1, dtype=np.float64) ** -skew)
+    pr /= pr.sum()
+    # distinct experts per token drawn from a skewed prior (Gumbel top-k)
+    g = np.log(pr)[None, :] + rng.gumbel(size=(T, E))
+    return np.argsort(-g, axis=1, kind="stable")[:, :k].astype(np.int32)
+
+
+@pytest.mark.parametrize("case", ALIGN_CASES, ids=[str(c) for c in ALIGN_CASES])
+def test_align_bit_exact_given_ids(case):
+    import mixture_experts_layer_44_amd as moe
+    T, E, k, cf, skew = case
+    _say(f"[align] T={T} E={E} k={k} cf={cf} skew={skew}")
+    ids = _ids(T, E, k, skew, seed=T * 31 + E)
+    p = moe.make_problem(T, 128, E, k, 128, capacity_factor=cf)
+    got = moe.align(p, torch.from_numpy(ids).cuda())
+    want = O.align(ids, E, O.capacity(cf, T, k, E))
+    n_kept = int(want["offsets"][-1])
+    for key in want:
+        a = got[key].cpu().numpy().astype(np.int64)
+        if key == "sorted_assign":          # only the first offsets[E] entries are defined
+            a = a[:n_kept]
+        assert np.array_equal(a, want[key]), (key, a[:10], want[key][:10])
+    # determinism: repeated runs give identical bytes
+    for _ in range(4):
+        again = moe.align(p, torch.from_numpy(ids).cuda())
+        for key in got:
+            a, b = again[key], got[key]
+            if key == "sorted_assign":
+                a, b = a[:n_kept], b[:n_kept]
+            assert torch.equal(a, b)
+
+
+def test_align_ignores_out_of_range_ids():
+    """An id outside [0, E) is documented as dropped and counted nowhere."""
+    import mixture_experts_layer_44_amd as moe
+    T, E, k = 300, 16, 2
+    ids = _ids(T, E, k, 0.0, seed=5)
+    bad = ids.copy()
+    bad[::7, 1] = E + 3
+    bad[::11, 0] = -1
+    p = moe.make_problem(T, 128, E, k, 128)
+    got = moe.align(p, torch.from_numpy(bad).cuda())
+    flat = bad.reshape(-1)
+    valid = (flat >= 0) & (flat < E)
+    ap = got["assign_pos"].cpu().numpy()
+    assert (ap[~valid] == -1).all()
+    assert got["offsets"][-1].item() == int(valid.sum())
+    # the valid assignments are grouped exactly as if the invalid ones were absent
+    cnt = np.bincount(flat[valid], minlength=E)
+    assert np.array_equal(got["counts_pre"].cpu().numpy(), cnt)
+    sa = got["sorted_assign"].cpu().numpy()[:valid.sum()]
+    assert np.array_equal(flat[sa], np.repeat(np.arange(E), cnt))
+    assert all((np.diff(sa[o:o2]) > 0).all() for o, o2 in zip(np.r_[0, np.cumsum(cnt)[:-1]], np.cumsum(cnt)))
+
+
+# ---------------------------------------------------------------------------- composition
+def test_entry_points_compose_to_forward():
+    """route -> align -> expert_ffn -> combine gives the same bits as moe_forward."""
+    import mixture_experts_layer_44_amd as moe
+    w = W("compose", T=333, d=256, E=24, k=3, d_ff=384, seed=201, n_shared=1, d_ff_shared=384,
+          sel_bias=True, capacity_factor=1.1)
+    inp = {k: (None if v is None else v.cuda()) for k, v in workloads.generate(w).items()}
+    p = moe.problem_for(w)
+    y, r = moe.forward(p, inp["x"], inp["w_gate"], inp["w1"], inp["w3"], inp["w2"],
+                       sel_bias=inp["sel_bias"], ws1=inp["ws1"], ws3=inp["ws3"], ws2=inp["ws2"],
+                       return_routing=True)
+    ids, gates, psum = moe.route(p, inp["x"], inp["w_gate"], sel_bias=inp["sel_bias"])
+    al = moe.align(p, ids)
+    out_rows, shared_out = moe.expert_ffn(p, inp["x"], inp["w1"], inp["w3"], inp["w2"],
+                                          al["sorted_assign"], al["offsets"], inp["ws1"], inp["ws3"],
+                                          inp["ws2"])
+    y2 = moe.combine(p, out_rows, al["assign_pos"], gates, shared_out)
+    torch.cuda.synchronize()
+    assert torch.equal(ids, r["topk_ids"]) and torch.equal(gates, r["topk_w"])
+    assert torch.equal(psum, r["prob_sum"])
+    n_kept = int(al["offsets"][-1].item())
+    assert n_kept < w.T * w.k                     # the capacity limit dropped something
+    for key in al:
+        a, b = al[key], r[key]
+        if key == "sorted_assign":                # only the first offsets[E] entries are defined
+            a, b = a[:n_kept], b[:n_kept]
+        assert torch.equal(a, b), key
+    assert torch.equal(y, y2)
+
+
+def test_balance_statistics():
+    import mixture_experts_layer_44_amd as moe
+    w = W("balance", T=2000, d=256, E=64, k=2, d_ff=128, seed=202, capacity_factor=1.25, zipf_s=1.1)
+    inp = workloads.generate(w)
+    g = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
+    p = moe.problem_for(w)
+    _, r = moe.forward(p, g["x"], g["w_gate"], g["w1"], g["w3"], g["w2"], logit_bias=g["logit_bias"],
+                       return_routing=True)
+    f, P, L = moe.balance(p, r["counts_pre"], r["prob_sum"], 0.01)
+    _, _, probs, _ = O.route(f64(inp["x"]), f64(inp["w_gate"]), w.k, f64(inp["logit_bias"]))
+    f_o, P_o, L_o = O.balance(O.align(r["topk_ids"].cpu().numpy(), w.E)["counts_pre"], probs, w.T,
+                              w.k, 0.01)
+    np.testing.assert_allclose(f.cpu().numpy(), f_o, rtol=1e-6, atol=1e-7)
+    np.testing.assert_allclose(P.cpu().numpy(), P_o, rtol=1e-4, atol=1e-6)
+    assert abs(L.item() - L_o) <= 1e-4 * abs(L_o)
+    assert L_o > 0.01        # a skewed router is above the balanced value alpha
+
+
+def test_workspace_reuse_across_shapes():
+    """One workspace sized for a large problem serves a smaller one; stale contents are ignored."""
+    import mixture_experts_layer_44_amd as moe
+    big = W("ws_big", T=600, d=256, E=16, k=4, d_ff=256, seed=203)
+    small = W("ws_small", T=37, d=256, E=16, k=4, d_ff=256, seed=204)
+    ws = torch.full((moe.workspace_bytes(moe.problem_for(big)),), 0xAB, dtype=torch.uint8,
+                    device="cuda")
+    for w in (big, small, big):
+        inp = {k: (None if v is None else v.cuda()) for k, v in workloads.generate(w).items()}
+        y = moe.forward(moe.problem_for(w), inp["x"], inp["w_gate"], inp["w1"], inp["w3"], inp["w2"],
+                        ws=ws)
+        y_ref = moe.forward(moe.problem_for(w), inp["x"], inp["w_gate"], inp["w1"], inp["w3"],
+                            inp["w2"])
+        assert torch.equal(y, y_ref)

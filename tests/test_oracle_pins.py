@@ -334,7 +334,29 @@ def pin_equivariance_and_scaling():
     np.testing.assert_allclose(yc, 2.5 * y, rtol=1e-13, atol=1e-15)
 
 
-PINS = [pin_gates_worked_example, pin_gates_flowchart, pin_topk_brute_force, pin_zero_input,
+def pin_token_outputs_equal_grouped():
+    """The per-subset combine used for sampled rows equals the grouped forward
+    (with a capacity limit, a shared expert and a selection bias)."""
+    rng = np.random.default_rng(41)
+    E, k, d, d_ff, T = 7, 3, 6, 5, 40
+    w1, w3, w2 = _experts(rng, E, d, d_ff)
+    s1, s3, s2 = _experts(rng, 1, d, d_ff)
+    wg, x = rng.normal(0, 1, (E, d)), rng.normal(0, 1, (T, d))
+    sb = rng.uniform(-0.5, 0.5, E)
+    ex = O.expert_table(w1, w3, w2)
+    shared = [(s1[0], s3[0], s2[0])]
+    y, info = O.moe_forward(x, wg, ex, E, k, sel_bias=sb, shared=shared, capacity_factor=0.8)
+    kept = (info["assign_pos"] >= 0).reshape(T, k)
+    assert not kept.all()
+    sub = np.array([0, 3, 17, 39, 22])
+    ys = O.token_outputs(x[sub], info["ids"][sub], info["gates"][sub], kept[sub], ex, shared)
+    np.testing.assert_allclose(ys, y[sub], rtol=1e-13, atol=1e-15)
+    for t in sub:
+        yt = O.token_output(x[t], info["ids"][t], info["gates"][t], kept[t], ex, shared)
+        np.testing.assert_allclose(yt, y[t], rtol=1e-13, atol=1e-15)
+
+
+PINS = [pin_token_outputs_equal_grouped, pin_gates_worked_example, pin_gates_flowchart, pin_topk_brute_force, pin_zero_input,
         pin_gates_sum_to_one, pin_softmax_library, pin_selection_bias_only_selects,
         pin_logit_bias_enters_softmax, pin_dense_swiglu_E1, pin_k_equals_E,
         pin_naive_equals_grouped_handbook, pin_naive_equals_grouped_capacity,

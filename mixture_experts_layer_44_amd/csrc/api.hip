@@ -31,7 +31,7 @@ Layout layout(const moe_problem& p) {
   const int G = p.E + p.n_shared;
   const int nblk_route = ceil_div(p.T, kRouteTok);
   const int nblk_align = ceil_div((int)n, kAlignChunk);
-  L.BM = p.dtype == MOE_BF16 ? kGemmBM : kGemmBM32;
+  L.BM = gemm_bm(p);
   L.max_mt = max_mtiles(p.T, p.k, p.E, p.n_shared, L.BM);
   const size_t esz = p.dtype == MOE_BF16 ? 2 : 4;
   L.psum_part = take((size_t)nblk_route * p.E * 4);

@@ -5,18 +5,34 @@
 // GEMM covers all experts, and an empty group must be handled); "MoE Architecture" §3
 // "Standard MoE" (SwiGLU experts: down(SiLU(gate x) * up x)).
 //
-// gate-up: for m-tile (group g, rows r0..r0+BM) and n-tile (features n0..n0+BN):
+// gate-up: for m-tile (group g, rows r0..r0+BM) and n-tile (features n0..n0+BNB/2):
 //   u = X_g W1_g^T, v = X_g W3_g^T over the tile, h = SiLU(u) * v -> bf16 H[m-tile rows].
 //   X rows are gathered from x by token (sorted_assign / k; identity for the shared group).
-// down:    out = H W2_g^T -> fp32 rows in sorted order (routed) or token order (shared).
+// down:    out = H W2_g^T (n-tile = BNB features) -> fp32 rows in sorted order (routed) or
+//          token order (shared).
 //
-// bf16 tiles: BM = 128 rows x BN = 128 features, BK = 64, 4 waves (2 x 2), each wave a
-// 64 x 64 sub-tile of 32x32 MFMA blocks (v_mfma_f32_32x32x16_bf16, fp32 accumulate).
-// The gate-up B tile holds the W1 and W3 rows of the same 128 features, so the SwiGLU
-// epilogue has u and v of an output in the same lane. Operands are staged through LDS
-// with a padded row stride (72 bf16) so the 16-byte fragment reads of 32 consecutive rows
-// fall in distinct banks. The next K tile is loaded into registers while the current one
-// feeds the MFMAs.
+// One template, tile shapes chosen on the host per problem:
+//   wide   BM=256, BNB=256, BK=64, 2 stages: 8 waves (4x2), each a 64x128 block of 32x32
+//          MFMA tiles (8 accumulators, 128 fp32 per lane). For experts with ~1000 rows each.
+//   narrow BM=128, BNB=256 (gate-up) / 128 (down), BK=32, 6 stages: 8 waves (2x4), each 64
+//          rows. For small segments.
+// Two waves per SIMD: while one waits for its LDS fragments the other issues MFMAs.
+// BNB counts B rows: the gate-up B tile holds the W1 rows and then the W3 rows of the same
+// BNB/2 features, and each wave reads the u and v fragments of the same features, so the
+// SwiGLU epilogue has u and v of an output in the same lane.
+//
+// Main loop: a ring of STAGES LDS buffers, each one K step of BK for all BM + BNB rows,
+// filled by direct global->LDS loads (global_load_lds_dwordx4, 16 bytes per lane, 1 KB per
+// instruction) with no register staging. STAGES-1 steps are in flight while the MFMAs
+// consume one; each step is one wait for this wave's loads of the step, one barrier, the
+// loads of step kt+STAGES-1 into the buffer freed by step kt-1, and the MFMAs of step kt.
+// Past the last step the loads repeat the last step into a buffer nobody reads again, so
+// the loop has no branches. Each LDS row is BK*2 bytes (BK/8 chunks of 16); chunk c of row r
+// sits in a swizzled slot (see swz) so 16 consecutive rows at one logical chunk cover all 16
+// 16-byte bank groups of a 256-byte LDS cycle.
+//
+// Rows of an m-tile past the end of its segment are loaded from the segment's first row;
+// their results land only in padding rows of H (gate-up) or are not stored (down).
 //
 // Work order: tiles are numbered group-major, then n-tile, then m-tile, so neighbouring
 // tiles share a weight tile (B) or a row block (A). Workgroups are dealt round-robin to
@@ -28,7 +44,11 @@ namespace moe {
 
 namespace {
 
-constexpr int BM = kGemmBM, BN = 128, BK = 64, LDK = BK + 8;
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// s_waitcnt immediate that waits until at most n vector-memory ops are outstanding
+// (expcnt and lgkmcnt left unconstrained)
+constexpr int wait_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 
 struct GemmArgs {
   const bf16_t* A;      // gate-up: x [T,K]; down: H [mtiles*BM, K]
@@ -48,7 +68,7 @@ struct TileCoord {
   int g, m_local, n0, mt_global, rows, off;
 };
 
-// Tile for this workgroup, or false if it has none. Must be uniform across the workgroup.
+// Tile for this workgroup, or false if it has none. Uniform across the workgroup.
 __device__ __forceinline__ bool tile_coord(const Schedule& sc, int NT, int bn, TileCoord& tc) {
   const int total = sc.mt_start[sc.G] * NT;
   const int bid = blockIdx.x;
@@ -73,132 +93,176 @@ __device__ __forceinline__ bool tile_coord(const Schedule& sc, int NT, int bn, T
 
 __device__ __forceinline__ float silu_f(float u) { return u / (1.0f + __expf(-u)); }
 
-template <bool GATEUP>
-__global__ __launch_bounds__(256) void gemm_bf16_kernel(GemmArgs args) {
-  constexpr int BNB = GATEUP ? 2 * BN : BN;     // B rows per tile
-  constexpr int A_LD = BM * BK / 8 / 256;      // 16-byte chunks per thread: 4
-  constexpr int B_LD = BNB * BK / 8 / 256;     // 8 (gate-up) or 4 (down)
-  __shared__ __attribute__((aligned(16))) bf16_t As[BM * LDK];
-  __shared__ __attribute__((aligned(16))) bf16_t Bs[BNB * LDK];
+// Element offset of (row, 16-byte chunk) in a swizzled [rows][BK] bf16 stage. A 256-byte
+// LDS cycle spans W = 128/BK rows; chunk c of row r goes to slot c ^ ((r / W) % (BK/8)), so
+// 16 consecutive rows read at one logical chunk hit 16 distinct 16-byte bank groups.
+template <int BK>
+__device__ __forceinline__ int swz(int r, int c) {
+  constexpr int CH = BK / 8, W = 128 / BK;
+  return r * BK + ((c ^ ((r / W) & (CH - 1))) << 3);
+}
+
+template <int BM, int BNB, int WM, int WN, int BK, int STAGES, bool GATEUP>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs args) {
+  constexpr int NW = WM * WN;
+  constexpr int CHUNKS = BK / 8;                   // 16-byte chunks per row per stage
+  constexpr int RPI = 64 / CHUNKS;                 // rows covered by one 1 KB load
+  constexpr int TM = BM / WM, TNB = BNB / WN;      // wave tile: rows x B rows
+  constexpr int FM = TM / 32, FN = TNB / 32;       // 32x32 fragments per wave
+  constexpr int ROWS = BM + BNB;                   // A rows then B rows in one stage
+  constexpr int STAGE = ROWS * BK;                 // bf16 elements per stage
+  constexpr int DMA_WAVE = ROWS * CHUNKS / 64 / NW; // 1 KB loads per wave per stage
+  static_assert(DMA_WAVE * 64 * NW == ROWS * CHUNKS, "loads split evenly over the waves");
+  constexpr int FEAT = GATEUP ? BNB / 2 : BNB;     // output features per n-tile
+  static_assert(!GATEUP || FN % 2 == 0, "u and v fragments pair up");
+  static_assert(BM % RPI == 0 && (BNB / 2) % RPI == 0, "a 1 KB load covers rows of one matrix");
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[STAGES * STAGE];
 
   TileCoord tc;
-  if (!tile_coord(args.sc, args.N / BN, BN, tc)) return;
+  if (!tile_coord(args.sc, args.N / FEAT, FEAT, tc)) return;
   const bool shared_grp = tc.g >= args.E;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int K = args.K, N = args.N;
 
-  // ---- per-thread global source rows
-  const int crow = tid >> 3, ccol = (tid & 7) * 8;
-  const bf16_t* a_src[A_LD];
-  bool a_ok[A_LD];
+  // ---- load sources. Load i of this wave fills stage rows q*RPI .. q*RPI+RPI-1 with
+  // q = wave*DMA_WAVE+i; lane l writes 16-byte slot l of the 1 KB: row q*RPI + l/CHUNKS,
+  // physical slot l%CHUNKS, so it fetches the logical chunk that the swizzle puts there.
+  const bf16_t* src_base[DMA_WAVE];
+  uint32_t src_off[DMA_WAVE];
 #pragma unroll
-  for (int i = 0; i < A_LD; ++i) {
-    const int lr = crow + 32 * i;
-    if (GATEUP) {
-      const int r = tc.m_local * BM + lr;
-      int tok = -1;
-      if (r < tc.rows) tok = shared_grp ? r : args.sorted_assign[tc.off + r] / args.k;
-      a_ok[i] = (unsigned)tok < (unsigned)args.T;   // rows past the segment (or bad entries) are zero
-      a_src[i] = args.A + (size_t)(a_ok[i] ? tok : 0) * K + ccol;
+  for (int i = 0; i < DMA_WAVE; ++i) {
+    const int q = wave * DMA_WAVE + i;
+    const int row = q * RPI + lane / CHUNKS;
+    const int lchunk = (swz<BK>(row, lane % CHUNKS) - row * BK) >> 3;  // the swizzle is an involution
+    if (q * RPI < BM) {
+      int srow;
+      if (GATEUP) {
+        const int r = tc.m_local * BM + row;
+        const int rr = r < tc.rows ? r : 0;             // padding rows repeat the first row
+        int tok = shared_grp ? rr : args.sorted_assign[tc.off + rr] / args.k;
+        srow = (unsigned)tok < (unsigned)args.T ? tok : 0;
+      } else {
+        srow = tc.mt_global * BM + row;
+      }
+      src_base[i] = args.A;
+      src_off[i] = (uint32_t)srow * (uint32_t)K + lchunk * 8;
     } else {
-      a_ok[i] = true;
-      a_src[i] = args.A + (size_t)(tc.mt_global * BM + lr) * K + ccol;
+      const int br = row - BM;
+      const bool second = GATEUP && br >= BNB / 2;
+      const bf16_t* mat;
+      if (GATEUP)
+        mat = shared_grp ? (second ? args.S1 : args.S0)
+                         : (second ? args.B1 : args.B0) + (size_t)tc.g * N * K;
+      else
+        mat = shared_grp ? args.S0 : args.B0 + (size_t)tc.g * N * K;
+      src_base[i] = mat + (size_t)tc.n0 * K;
+      src_off[i] = (uint32_t)(second ? br - BNB / 2 : br) * (uint32_t)K + lchunk * 8;
     }
   }
-  const bf16_t* b_src[B_LD];
+  auto issue = [&](int kt, int st) {
+    bf16_t* dst = smem + st * STAGE;
 #pragma unroll
-  for (int i = 0; i < B_LD; ++i) {
-    const int br = crow + 32 * i;
-    const bf16_t* base;
-    int row;
-    if (GATEUP) {
-      const bool up = br >= BN;
-      base = shared_grp ? (up ? args.S1 : args.S0)
-                        : (up ? args.B1 : args.B0) + (size_t)tc.g * N * K;
-      row = tc.n0 + (up ? br - BN : br);
-    } else {
-      base = shared_grp ? args.S0 : args.B0 + (size_t)tc.g * N * K;
-      row = tc.n0 + br;
+    for (int i = 0; i < DMA_WAVE; ++i) {
+      const int q = wave * DMA_WAVE + i;
+      __builtin_amdgcn_global_load_lds((const void*)(src_base[i] + src_off[i] + kt * BK),
+                                       (lds_ptr_t)(dst + q * RPI * BK), 16, 0, 0);
     }
-    b_src[i] = base + (size_t)row * K + ccol;
+  };
+
+  const int wm = wave / WN, wn = wave % WN;
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // stage rows of this lane's fragments
+  const int fr = lane & 31, fkc = lane >> 5;
+  int arow[FM], brow[FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) arow[i] = wm * TM + i * 32 + fr;
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    if (GATEUP) {
+      const int fw = BNB / 2 / WN;   // features per wave
+      const int jj = j % (FN / 2);
+      brow[j] = BM + (j < FN / 2 ? 0 : BNB / 2) + wn * fw + jj * 32 + fr;
+    } else {
+      brow[j] = BM + wn * TNB + j * 32 + fr;
+    }
   }
 
-  u32x4 ra[A_LD], rb[B_LD];
-  const u32x4 zero4 = {0u, 0u, 0u, 0u};
-  auto gload = [&](int k0) {
+  // One K stage of MFMAs. Fragments are double-buffered across the k16 steps so the reads for
+  // step ks+1 can be in flight while the MFMAs of step ks run; iglp_opt(1) asks the backend
+  // scheduler for its DS-read/MFMA interleaving strategy (measured best of the options).
+  auto compute = [&](const bf16_t* buf) {
+    constexpr int NKS = BK / 16;
+    __builtin_amdgcn_iglp_opt(1);
+    bf16x8 af[2][FM], bfr[2][FN];
 #pragma unroll
-    for (int i = 0; i < A_LD; ++i) ra[i] = a_ok[i] ? *(const u32x4*)(a_src[i] + k0) : zero4;
+    for (int i = 0; i < FM; ++i) af[0][i] = *(const bf16x8*)&buf[swz<BK>(arow[i], fkc)];
 #pragma unroll
-    for (int i = 0; i < B_LD; ++i) rb[i] = *(const u32x4*)(b_src[i] + k0);
-  };
-  auto lstore = [&]() {
+    for (int j = 0; j < FN; ++j) bfr[0][j] = *(const bf16x8*)&buf[swz<BK>(brow[j], fkc)];
 #pragma unroll
-    for (int i = 0; i < A_LD; ++i) *(u32x4*)&As[(crow + 32 * i) * LDK + ccol] = ra[i];
+    for (int ks = 0; ks < NKS; ++ks) {
+      const int cur = ks & 1, nxt = cur ^ 1;
+      if (ks + 1 < NKS) {
 #pragma unroll
-    for (int i = 0; i < B_LD; ++i) *(u32x4*)&Bs[(crow + 32 * i) * LDK + ccol] = rb[i];
+        for (int i = 0; i < FM; ++i)
+          af[nxt][i] = *(const bf16x8*)&buf[swz<BK>(arow[i], 2 * (ks + 1) + fkc)];
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          bfr[nxt][j] = *(const bf16x8*)&buf[swz<BK>(brow[j], 2 * (ks + 1) + fkc)];
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bfr[cur][j], acc[i][j],
+                                                              0, 0, 0);
+    }
   };
 
-  const int wm = wave >> 1, wn = wave & 1;
-  constexpr int NACC = GATEUP ? 2 : 1;
-  f32x16 acc[NACC][2][2];
-#pragma unroll
-  for (int q = 0; q < NACC; ++q)
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[q][i][j][r] = 0.f;
-
-  const int fr = lane & 31, fk = (lane >> 5) * 8;
   const int KT = K / BK;
-  gload(0);
+#pragma unroll
+  for (int s = 0; s < STAGES - 1; ++s) issue(s < KT ? s : KT - 1, s);
   for (int kt = 0; kt < KT; ++kt) {
-    __syncthreads();
-    lstore();
-    __syncthreads();
-    if (kt + 1 < KT) gload((kt + 1) * BK);
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8 af[2], bf[NACC][2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        af[i] = *(const bf16x8*)&As[(wm * 64 + i * 32 + fr) * LDK + ks * 16 + fk];
-#pragma unroll
-      for (int q = 0; q < NACC; ++q)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          bf[q][j] = *(const bf16x8*)&Bs[(q * BN + wn * 64 + j * 32 + fr) * LDK + ks * 16 + fk];
-#pragma unroll
-      for (int q = 0; q < NACC; ++q)
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            acc[q][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bf[q][j], acc[q][i][j], 0, 0, 0);
-    }
+    // this wave's loads of step kt are done once at most STAGES-2 steps remain in flight;
+    // then one barrier makes every wave's part visible and retires step kt-1's buffer. (A
+    // bare s_barrier: a release fence here would also drain the loads still in flight.)
+    __builtin_amdgcn_s_waitcnt(wait_vm((STAGES - 2) * DMA_WAVE));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    const int nxt = kt + STAGES - 1;
+    issue(nxt < KT ? nxt : KT - 1, nxt % STAGES);
+    compute(smem + (kt % STAGES) * STAGE);
   }
+  __builtin_amdgcn_s_waitcnt(wait_vm(0));
 
   // ---- epilogue. 32x32 accumulator layout: lane holds column lane%32 and rows
   // 8*(r/4) + 4*(lane/32) + r%4 for r = 0..15.
+  constexpr int FO = GATEUP ? FN / 2 : FN;   // output fragments along n
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const int col = tc.n0 + wn * 64 + j * 32 + fr;
+    for (int j = 0; j < FO; ++j) {
+      const int col = tc.n0 + wn * (FEAT / WN) + j * 32 + fr;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int lr = wm * 64 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int lr = wm * TM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         if (GATEUP) {
-          const float u = acc[0][i][j][r];
-          const float v = acc[NACC - 1][i][j][r];
+          const float u = acc[i][j][r];
+          const float v = acc[i][j + FN / 2][r];
           args.H[(size_t)(tc.mt_global * BM + lr) * N + col] = f32_to_bf16(silu_f(u) * v);
         } else {
           const int rg = tc.m_local * BM + lr;
           if (rg < tc.rows) {
             float* dst = shared_grp ? args.shared_out + (size_t)rg * N
                                     : args.out_rows + (size_t)(tc.off + rg) * N;
-            dst[col] = acc[0][i][j][r];
+            dst[col] = acc[i][j][r];
           }
         }
       }
@@ -293,12 +357,40 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs32 args) {
   }
 }
 
-inline int grid_for(int mtiles, int nt) {
+}  // namespace
+
+int grid_for(int mtiles, int nt) {
   long long g = (long long)mtiles * nt;
   return (int)((g + 7) / 8 * 8);
 }
 
-}  // namespace
+int gemm_bm(const moe_problem& p) {
+  if (p.dtype != MOE_BF16) return kGemmBM32;
+  return gemm_wide(p) ? 256 : 128;
+}
+
+bool gemm_wide(const moe_problem& p) {
+  if (p.dtype != MOE_BF16 || p.d % 256) return false;
+  // expected kept rows per expert: T*k/E, or the capacity if that is smaller
+  double rows = (double)p.T * p.k / p.E;
+  if (p.capacity_factor > 0) rows = std::min(rows, std::ceil(p.capacity_factor * rows));
+  return rows >= 768.0;
+}
+
+template <int BM, int BNB_UP, int WM_UP, int WN_UP, int BNB_DN, int WM_DN, int WN_DN, int BK, int ST>
+hipError_t launch_bf16(const moe_problem& p, const GemmArgs& a, const GemmArgs& b, hipStream_t s,
+                       hipEvent_t between) {
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BNB_UP, WM_UP, WN_UP, BK, ST, true>),
+                     dim3(grid_for(a.sc.max_mtiles, p.d_ff / (BNB_UP / 2))), dim3(WM_UP * WN_UP * 64),
+                     0, s, a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  if (between && (err = hipEventRecord(between, s)) != hipSuccess) return err;
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BNB_DN, WM_DN, WN_DN, BK, ST, false>),
+                     dim3(grid_for(b.sc.max_mtiles, p.d / BNB_DN)), dim3(WM_DN * WN_DN * 64), 0, s,
+                     b);
+  return hipGetLastError();
+}
 
 hipError_t launch_expert_ffn(const moe_problem& p, const void* x, const void* w1, const void* w3,
                              const void* w2, const void* ws1, const void* ws3, const void* ws2,
@@ -320,11 +412,6 @@ hipError_t launch_expert_ffn(const moe_problem& p, const void* x, const void* w1
     a.sorted_assign = sorted_assign;
     a.sc = sc;
     a.H = (bf16_t*)h;
-    hipLaunchKernelGGL(gemm_bf16_kernel<true>, dim3(grid_for(sc.max_mtiles, p.d_ff / BN)),
-                       dim3(256), 0, s, a);
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    if (between && (err = hipEventRecord(between, s)) != hipSuccess) return err;
     GemmArgs b{};
     b.A = (const bf16_t*)h;
     b.B0 = (const bf16_t*)w2;
@@ -338,9 +425,8 @@ hipError_t launch_expert_ffn(const moe_problem& p, const void* x, const void* w1
     b.sc = sc;
     b.out_rows = out_rows;
     b.shared_out = shared_out;
-    hipLaunchKernelGGL(gemm_bf16_kernel<false>, dim3(grid_for(sc.max_mtiles, p.d / BN)), dim3(256),
-                       0, s, b);
-    return hipGetLastError();
+    if (sc.BM == 256) return launch_bf16<256, 256, 4, 2, 256, 4, 2, 64, 2>(p, a, b, s, between);
+    return launch_bf16<128, 256, 2, 4, 128, 2, 4, 32, 6>(p, a, b, s, between);
   }
   GemmArgs32 a{};
   a.A = (const float*)x;

@@ -4,6 +4,8 @@
 
 #include <hip/hip_runtime.h>
 #include <stddef.h>
+#include <algorithm>
+#include <cmath>
 #include <stdint.h>
 
 #include "../../include/moe_mi355x.h"
@@ -49,6 +51,10 @@ struct Schedule {
 };
 
 int max_mtiles(int T, int k, int E, int n_shared, int BM);
+// grouped-GEMM tile shape class: wide (256-row m-tiles) for experts with many rows each
+bool gemm_wide(const moe_problem& p);
+int gemm_bm(const moe_problem& p);
+int grid_for(int mtiles, int nt);
 
 // ---------------------------------------------------------------- launchers
 hipError_t launch_route(const moe_problem& p, const void* x, const void* w_gate,

@@ -154,7 +154,7 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mixtral_prefill")
-    ap.add_argument("--cpu-sample", type=int, default=64,
+    ap.add_argument("--cpu-sample", type=int, default=512,
                     help="tokens of the workload the CPU oracle baseline runs on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     args = ap.parse_args(argv)

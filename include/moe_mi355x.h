@@ -153,7 +153,8 @@ moe_status moe_balance(const moe_problem* p, const int32_t* counts_pre, const fl
 /* The whole layer in one call: route -> align -> expert FFNs -> combine.
    y [T,d] fp32 out (required). Every routing output pointer may be NULL, in
    which case it lives in ws; when given, it receives the same values the
-   separate calls above would produce. */
+   separate calls above would produce (prob_sum: the same sum, possibly added
+   in a different order when T*k <= 1024, where routing runs in one launch). */
 moe_status moe_forward(const moe_problem* p, const void* x, const void* w_gate,
                        const float* logit_bias, const float* sel_bias,
                        const void* w1, const void* w3, const void* w2,

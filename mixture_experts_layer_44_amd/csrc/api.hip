@@ -12,7 +12,7 @@ namespace moe {
 namespace {
 
 struct Layout {
-  size_t psum_part, blk_counts, blk_base, grp_rows, grp_off, mt_start, mt_group, h;
+  size_t logits_part, psum_part, blk_counts, blk_base, grp_rows, grp_off, mt_start, mt_group, h;
   size_t ids, gates, prob_sum, counts_pre, counts, offsets, sorted_assign, assign_pos;
   size_t out_rows, shared_out;
   size_t total;
@@ -29,11 +29,12 @@ Layout layout(const moe_problem& p) {
   };
   const size_t n = (size_t)p.T * p.k;
   const int G = p.E + p.n_shared;
-  const int nblk_route = ceil_div(p.T, kRouteTok);
+  const int nblk_route = route_topk_blocks(p);
   const int nblk_align = ceil_div((int)n, kAlignChunk);
   L.BM = gemm_bm(p);
   L.max_mt = max_mtiles(p.T, p.k, p.E, p.n_shared, L.BM);
   const size_t esz = p.dtype == MOE_BF16 ? 2 : 4;
+  L.logits_part = take(route_partial_bytes(p));
   L.psum_part = take((size_t)nblk_route * p.E * 4);
   L.blk_counts = take((size_t)nblk_align * p.E * 4);
   L.blk_base = take((size_t)nblk_align * p.E * 4);
@@ -154,7 +155,7 @@ MOE_API moe_status moe_route(const moe_problem* p, const void* x, const void* w_
   if ((st = check_ws(*p, ws, ws_bytes)) != MOE_OK) return st;
   const Layout L = layout(*p);
   return hip_status(launch_route(*p, x, w_gate, logit_bias, sel_bias, topk_ids, topk_w, prob_sum,
-                                 at<float>(ws, L.psum_part), stream));
+                                 at<float>(ws, L.logits_part), at<float>(ws, L.psum_part), stream));
 }
 
 MOE_API moe_status moe_align(const moe_problem* p, const int32_t* topk_ids, int32_t* counts_pre,
@@ -239,15 +240,26 @@ moe_status forward_impl(const moe_problem* p, const void* x, const void* w_gate,
   float* shared_out = p->n_shared ? at<float>(ws, L.shared_out) : nullptr;
   auto mark = [&](int i) { return ev ? hipEventRecord(ev[i], stream) : hipSuccess; };
   if (mark(0) != hipSuccess) return MOE_EHIP;
-  hipError_t e = launch_route(*p, x, w_gate, logit_bias, sel_bias, ids, gates, prob_sum,
-                              at<float>(ws, L.psum_part), stream);
-  if (e != hipSuccess || mark(1) != hipSuccess) return MOE_EHIP;
-  e = launch_align(*p, kernel_cap(*p), ids, cpre, cnt, offs, sa, ap, at<int32_t>(ws, L.blk_counts),
-                   at<int32_t>(ws, L.blk_base), stream);
-  if (e != hipSuccess || mark(2) != hipSuccess) return MOE_EHIP;
   const Schedule sc = schedule_in(*p, L, ws);
-  if (launch_schedule(*p, offs, sc, stream) != hipSuccess || mark(3) != hipSuccess)
-    return MOE_EHIP;
+  hipError_t e;
+  if (small_routing(*p)) {
+    // decode-sized: logits, then top-k + grouping + schedule in one launch
+    e = launch_route_logits(*p, x, w_gate, at<float>(ws, L.logits_part), stream);
+    if (e != hipSuccess || mark(1) != hipSuccess) return MOE_EHIP;
+    e = launch_route_align_small(*p, kernel_cap(*p), at<float>(ws, L.logits_part), logit_bias,
+                                 sel_bias, ids, gates, prob_sum, cpre, cnt, offs, sa, ap, sc,
+                                 stream);
+    if (e != hipSuccess || mark(2) != hipSuccess || mark(3) != hipSuccess) return MOE_EHIP;
+  } else {
+    e = launch_route(*p, x, w_gate, logit_bias, sel_bias, ids, gates, prob_sum,
+                     at<float>(ws, L.logits_part), at<float>(ws, L.psum_part), stream);
+    if (e != hipSuccess || mark(1) != hipSuccess) return MOE_EHIP;
+    e = launch_align(*p, kernel_cap(*p), ids, cpre, cnt, offs, sa, ap,
+                     at<int32_t>(ws, L.blk_counts), at<int32_t>(ws, L.blk_base), stream);
+    if (e != hipSuccess || mark(2) != hipSuccess) return MOE_EHIP;
+    if (launch_schedule(*p, offs, sc, stream) != hipSuccess || mark(3) != hipSuccess)
+      return MOE_EHIP;
+  }
   e = launch_expert_ffn(*p, x, w1, w3, w2, ws1, ws3, ws2, sa, sc, at<void>(ws, L.h), out_rows,
                         shared_out, stream, ev ? ev[4] : nullptr);
   if (e != hipSuccess || mark(5) != hipSuccess) return MOE_EHIP;

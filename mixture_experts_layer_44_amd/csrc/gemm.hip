@@ -15,7 +15,9 @@
 //   wide   BM=256, BNB=256, BK=64, 2 stages: 8 waves (4x2), each a 64x128 block of 32x32
 //          MFMA tiles (8 accumulators, 128 fp32 per lane). For experts with ~1000 rows each.
 //   narrow BM=128, BNB=256 (gate-up) / 128 (down), BK=32, 6 stages: 8 waves (2x4), each 64
-//          rows. For small segments.
+//          rows. For segments of ~50-700 rows.
+//   small  BM=32, BNB=256 / 128, BK=64, 4 stages: 4 waves (1x4), one 32-row fragment each.
+//          For decode-sized segments: many workgroups stream the touched experts' weights.
 // Two waves per SIMD: while one waits for its LDS fragments the other issues MFMAs.
 // BNB counts B rows: the gate-up B tile holds the W1 rows and then the W3 rows of the same
 // BNB/2 features, and each wave reads the u and v fragments of the same features, so the
@@ -160,12 +162,14 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs args) 
       src_off[i] = (uint32_t)(second ? br - BNB / 2 : br) * (uint32_t)K + lchunk * 8;
     }
   }
+  const int KT = K / BK;
   auto issue = [&](int kt, int st) {
     bf16_t* dst = smem + st * STAGE;
+    const int kk = kt * BK;
 #pragma unroll
     for (int i = 0; i < DMA_WAVE; ++i) {
       const int q = wave * DMA_WAVE + i;
-      __builtin_amdgcn_global_load_lds((const void*)(src_base[i] + src_off[i] + kt * BK),
+      __builtin_amdgcn_global_load_lds((const void*)(src_base[i] + src_off[i] + kk),
                                        (lds_ptr_t)(dst + q * RPI * BK), 16, 0, 0);
     }
   };
@@ -226,7 +230,6 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs args) 
     }
   };
 
-  const int KT = K / BK;
 #pragma unroll
   for (int s = 0; s < STAGES - 1; ++s) issue(s < KT ? s : KT - 1, s);
   for (int kt = 0; kt < KT; ++kt) {
@@ -366,16 +369,21 @@ int grid_for(int mtiles, int nt) {
 
 int gemm_bm(const moe_problem& p) {
   if (p.dtype != MOE_BF16) return kGemmBM32;
-  return gemm_wide(p) ? 256 : 128;
+  return gemm_wide(p) ? 256 : gemm_small(p) ? 32 : 128;
+}
+
+// expected kept rows per expert: T*k/E, or the capacity if that is smaller
+static double expected_rows(const moe_problem& p) {
+  double rows = (double)p.T * p.k / p.E;
+  if (p.capacity_factor > 0) rows = std::min(rows, std::ceil(p.capacity_factor * rows));
+  return rows;
 }
 
 bool gemm_wide(const moe_problem& p) {
-  if (p.dtype != MOE_BF16 || p.d % 256) return false;
-  // expected kept rows per expert: T*k/E, or the capacity if that is smaller
-  double rows = (double)p.T * p.k / p.E;
-  if (p.capacity_factor > 0) rows = std::min(rows, std::ceil(p.capacity_factor * rows));
-  return rows >= 768.0;
+  return p.dtype == MOE_BF16 && p.d % 256 == 0 && expected_rows(p) >= 768.0;
 }
+
+bool gemm_small(const moe_problem& p) { return p.dtype == MOE_BF16 && expected_rows(p) <= 48.0; }
 
 template <int BM, int BNB_UP, int WM_UP, int WN_UP, int BNB_DN, int WM_DN, int WN_DN, int BK, int ST>
 hipError_t launch_bf16(const moe_problem& p, const GemmArgs& a, const GemmArgs& b, hipStream_t s,
@@ -426,6 +434,7 @@ hipError_t launch_expert_ffn(const moe_problem& p, const void* x, const void* w1
     b.out_rows = out_rows;
     b.shared_out = shared_out;
     if (sc.BM == 256) return launch_bf16<256, 256, 4, 2, 256, 4, 2, 64, 2>(p, a, b, s, between);
+    if (sc.BM == 32) return launch_bf16<32, 256, 1, 4, 128, 1, 4, 64, 4>(p, a, b, s, between);
     return launch_bf16<128, 256, 2, 4, 128, 2, 4, 32, 6>(p, a, b, s, between);
   }
   GemmArgs32 a{};

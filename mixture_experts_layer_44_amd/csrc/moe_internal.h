@@ -29,7 +29,6 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
 }
 
 // ---------------------------------------------------------------- tiling constants
-constexpr int kRouteTok = 16;        // tokens per router workgroup
 constexpr int kAlignChunk = 1024;    // assignments per align workgroup
 constexpr int kGemmBM = 128;         // rows per grouped-GEMM m-tile (bf16 path)
 constexpr int kGemmBM32 = 64;        // rows per m-tile (fp32 path)
@@ -51,15 +50,36 @@ struct Schedule {
 };
 
 int max_mtiles(int T, int k, int E, int n_shared, int BM);
-// grouped-GEMM tile shape class: wide (256-row m-tiles) for experts with many rows each
+// grouped-GEMM tile shape class from the expected rows per expert: wide (256-row m-tiles),
+// narrow (128) or small (32)
 bool gemm_wide(const moe_problem& p);
+bool gemm_small(const moe_problem& p);
 int gemm_bm(const moe_problem& p);
 int grid_for(int mtiles, int nt);
 
 // ---------------------------------------------------------------- launchers
+// router: d-slices of the logits GEMM, scratch bytes for its fp32 partial logits, and the
+// number of top-k workgroups (rows of the per-workgroup probability sums)
+int route_ksplit(const moe_problem& p);
+size_t route_partial_bytes(const moe_problem& p);
+int route_topk_blocks(const moe_problem& p);
+
+hipError_t launch_route_logits(const moe_problem& p, const void* x, const void* w_gate,
+                               float* logits_part, hipStream_t s);
+
+// small batches (T*k <= 1024): top-k, probability sums, grouping and GEMM schedule in one
+// single-workgroup launch after the logits
+bool small_routing(const moe_problem& p);
+hipError_t launch_route_align_small(const moe_problem& p, int cap, const float* logits_part,
+                                    const float* logit_bias, const float* sel_bias, int32_t* ids,
+                                    float* gates, float* prob_sum, int32_t* counts_pre,
+                                    int32_t* counts, int32_t* offsets, int32_t* sorted_assign,
+                                    int32_t* assign_pos, const Schedule& sc, hipStream_t s);
+
 hipError_t launch_route(const moe_problem& p, const void* x, const void* w_gate,
                         const float* logit_bias, const float* sel_bias, int32_t* ids,
-                        float* gates, float* prob_sum, float* psum_part, hipStream_t s);
+                        float* gates, float* prob_sum, float* logits_part, float* psum_part,
+                        hipStream_t s);
 
 hipError_t launch_align(const moe_problem& p, int cap, const int32_t* ids, int32_t* counts_pre,
                         int32_t* counts, int32_t* offsets, int32_t* sorted_assign,

@@ -6,210 +6,183 @@
 // Sum Output" (kept probabilities divided by their sum); "Mixture of experts (MoE)"
 // handbook, "Load balancing" (the balancing bias only chooses experts).
 //
-// One workgroup = 16 tokens x all E experts (E <= 256), 4 waves of 64 lanes.
-// bf16: v_mfma_f32_16x16x32_bf16 tiles of 16 tokens x 16 experts; the fp32 logits stay in
-// LDS (never rounded to bf16). With >= 4 expert tiles each wave owns whole tiles over the
-// full d; with fewer, the 4 waves split d and their partial logits are summed in a fixed
-// order. Then each wave takes 4 tokens: softmax and k rounds of a 64-lane arg-max
-// (larger key first, lower expert index on equal keys) with shuffles.
-#include "moe_internal.h"
+// Two launches:
+//  logits: grid (token tiles of 32) x (expert groups of 64) x (KS slices of d). A workgroup
+//          of 4 waves computes a 32 x 64 block of partial logits over its d slice with
+//          v_mfma_f32_16x16x32_bf16 (fp32 accumulate); waves take 16-expert tiles and, when
+//          the group has fewer than 4 tiles, split the slice further, their partials summed
+//          in a fixed order through LDS. Loads are issued four k-steps ahead of the MFMAs.
+//          KS is chosen on the host so that the grid has >= ~512 workgroups; the fp32
+//          partials [KS][T][E_pad] never round to bf16.
+//  topk:   one wave per token. Sums the KS partials in slice order (run-to-run identical),
+//          adds logit_bias, softmax, keys = logits (+ sel_bias), k rounds of a 64-lane
+//          arg-max (larger key first, lower expert index on equal keys), gates = kept p /
+//          their sum; per-workgroup sums of p for prob_sum.
+#include "topk.h"
 
 namespace moe {
 
 namespace {
 
-constexpr int kWaves = 4;
-constexpr int kMaxNT = 16;  // 256 experts / 16
+constexpr int TM = 32;        // tokens per logits workgroup
+constexpr int EN = 64;        // experts per logits workgroup
+constexpr int UNROLL = 4;     // k-steps of loads in flight per wave
+constexpr int TOPK_TOK = 16;  // tokens per top-k workgroup (4 waves x 4)
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
-  return v;
-}
-__device__ __forceinline__ float wave_sum(float v) {
-  // xor butterfly: every lane adds the same pairs, so all lanes get identical bits
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
-}
-
+// partial logits of a 32-token x 64-expert block over the d slice blockIdx.z
 template <bool BF16>
-__global__ __launch_bounds__(256) void route_kernel(
-    const void* __restrict__ xv, const void* __restrict__ wv, const float* __restrict__ logit_bias,
-    const float* __restrict__ sel_bias, int T, int d, int E, int k, int32_t* __restrict__ ids,
-    float* __restrict__ gates, float* __restrict__ psum_part) {
-  const int n_tiles = (E + 15) / 16;
-  const int E_pad = n_tiles * 16;
-  const bool ksplit = n_tiles < kWaves;            // small E: waves split d instead of experts
-  // part[s][tok][e]: s < 4 partial logits (ksplit) or s = 0 only
-  extern __shared__ float lds[];
-  float* part = lds;
+__global__ __launch_bounds__(256) void route_logits_kernel(const void* __restrict__ xv,
+                                                           const void* __restrict__ wv, int T,
+                                                           int d, int E, int E_pad, int KS,
+                                                           float* __restrict__ part) {
+  __shared__ float red[4][TM][16];   // per-wave partials when waves split the slice
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int tok0 = blockIdx.x * kRouteTok;
+  const int tok0 = blockIdx.x * TM;
+  const int e0 = blockIdx.y * EN;
+  const int ntiles = min(EN, E_pad - e0) / 16;      // 1..4 expert tiles in this group
+  const int wsplit = 4 / ntiles >= 4 ? 4 : (4 / ntiles >= 2 ? 2 : 1);   // waves per tile
+  const int slice = d / KS, k_begin = blockIdx.z * slice;
+  float* out = part + (size_t)blockIdx.z * T * E_pad;
 
   if constexpr (BF16) {
     const bf16_t* x = (const bf16_t*)xv;
     const bf16_t* w = (const bf16_t*)wv;
-    // this wave's expert tiles and d range
-    int nt_first = ksplit ? 0 : wave, nt_step = ksplit ? 1 : kWaves;
-    int kb0 = ksplit ? wave * (d / kWaves) : 0;
-    int kb1 = ksplit ? kb0 + d / kWaves : d;
+    const int tile = wave / wsplit, sub = wave % wsplit;   // this wave's expert tile, sub-slice
+    const bool active = tile < ntiles;
+    const int sub_len = slice / wsplit;
+    const int kb0 = k_begin + sub * sub_len;
     const int r = lane & 15, kq = (lane >> 4) * 8;
-    const int trow = tok0 + r;
-    const bool a_ok = trow < T;
-    const bf16_t* a_ptr = x + (size_t)(a_ok ? trow : 0) * d + kq;
-    f32x4 acc[4];
-    const bf16_t* b_ptr[4];
-    bool b_ok[4];
-    int nt_list[4];
-    int nn = 0;
+    const int e = e0 + tile * 16 + r;
+    const bool b_ok = active && e < E;
+    const bf16_t* bp = w + (size_t)(b_ok ? e : 0) * d + kq;
+    const bool a0_ok = tok0 + r < T, a1_ok = tok0 + 16 + r < T;
+    const bf16_t* ap0 = x + (size_t)(a0_ok ? tok0 + r : 0) * d + kq;
+    const bf16_t* ap1 = x + (size_t)(a1_ok ? tok0 + 16 + r : 0) * d + kq;
+    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
+    const bf16x8 z8 = {};
+    if (active) {
+      // walk the slice starting at a per-workgroup offset (wrapping): rows are d*2 bytes
+      // apart, and workgroups reading the same k offset at once collide on memory channels
+      const int nsteps = sub_len / 32;
+      const int rot = (blockIdx.x + blockIdx.y * 7) % nsteps;
+      auto kpos = [&](int step) { return kb0 + ((step + rot) % nsteps) * 32; };
+      int st = 0;
+      for (; st + UNROLL <= nsteps; st += UNROLL) {
+        bf16x8 a0[UNROLL], a1[UNROLL], b[UNROLL];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      acc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
-      int nt = nt_first + i * nt_step;
-      nt_list[i] = nt;
-      bool have = nt < n_tiles && (ksplit ? (i < n_tiles) : true);
-      if (have) nn = i + 1;
-      int e = nt * 16 + r;
-      b_ok[i] = have && e < E;
-      b_ptr[i] = w + (size_t)(b_ok[i] ? e : 0) * d + kq;
-    }
-    const bf16x8 zero8 = {};
-    for (int kb = kb0; kb < kb1; kb += 32) {
-      bf16x8 a = a_ok ? *(const bf16x8*)(a_ptr + kb) : zero8;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (i < nn) {
-          bf16x8 b = b_ok[i] ? *(const bf16x8*)(b_ptr[i] + kb) : zero8;
-          acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[i], 0, 0, 0);
+        for (int u = 0; u < UNROLL; ++u) {
+          const int kb = kpos(st + u);
+          a0[u] = *(const bf16x8*)(ap0 + kb);
+          a1[u] = *(const bf16x8*)(ap1 + kb);
+          b[u] = *(const bf16x8*)(bp + kb);
         }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < UNROLL; ++u) {
+          const bf16x8 bb = b_ok ? b[u] : z8;
+          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0_ok ? a0[u] : z8, bb, acc0, 0, 0, 0);
+          acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1_ok ? a1[u] : z8, bb, acc1, 0, 0, 0);
+        }
+      }
+      for (; st < nsteps; ++st) {
+        const int kb = kpos(st);
+        const bf16x8 bb = b_ok ? *(const bf16x8*)(bp + kb) : z8;
+        const bf16x8 x0 = a0_ok ? *(const bf16x8*)(ap0 + kb) : z8;
+        const bf16x8 x1 = a1_ok ? *(const bf16x8*)(ap1 + kb) : z8;
+        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x0, bb, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x1, bb, acc1, 0, 0, 0);
       }
     }
     // C layout (16x16): lane holds column (expert) lane%16, rows (tokens) 4*(lane/16)+j
-    const int slot = ksplit ? wave : 0;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (i < nn) {
-        int e = nt_list[i] * 16 + (lane & 15);
+    if (wsplit > 1) {
+      if (active) {
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
-          int tr = (lane >> 4) * 4 + j;
-          part[(slot * kRouteTok + tr) * E_pad + e] = acc[i][j];
+          red[wave][(lane >> 4) * 4 + j][lane & 15] = acc0[j];
+          red[wave][16 + (lane >> 4) * 4 + j][lane & 15] = acc1[j];
         }
+      }
+      __syncthreads();
+      // thread -> (token, expert) of this group; sum the sub-slices of its tile in order
+      for (int idx = tid; idx < TM * ntiles * 16; idx += 256) {
+        const int tr = idx / (ntiles * 16), ec = idx % (ntiles * 16);
+        const int t_ = ec / 16, c = ec % 16;
+        float s = 0.f;
+        for (int q = 0; q < wsplit; ++q) s += red[t_ * wsplit + q][tr][c];
+        if (tok0 + tr < T) out[(size_t)(tok0 + tr) * E_pad + e0 + ec] = s;
+      }
+    } else if (active) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int t0 = tok0 + (lane >> 4) * 4 + j, t1 = t0 + 16;
+        if (t0 < T) out[(size_t)t0 * E_pad + e0 + tile * 16 + (lane & 15)] = acc0[j];
+        if (t1 < T) out[(size_t)t1 * E_pad + e0 + tile * 16 + (lane & 15)] = acc1[j];
       }
     }
   } else {
     const float* x = (const float*)xv;
     const float* w = (const float*)wv;
-    for (int idx = tid; idx < kRouteTok * E_pad; idx += 256) {
-      int tr = idx / E_pad, e = idx - tr * E_pad;
-      int t = tok0 + tr;
+    const int ecount = min(EN, E_pad - e0);
+    for (int idx = tid; idx < TM * ecount; idx += 256) {
+      const int tr = idx / ecount, e = e0 + idx % ecount;
+      const int t = tok0 + tr;
+      if (t >= T) continue;
       float s = 0.f;
-      if (t < T && e < E) {
-        const float* xr = x + (size_t)t * d;
-        const float* wr = w + (size_t)e * d;
-        for (int i = 0; i < d; ++i) s = fmaf(xr[i], wr[i], s);
+      if (e < E) {
+        const float* xr = x + (size_t)t * d + k_begin;
+        const float* wr = w + (size_t)e * d + k_begin;
+        for (int i = 0; i < slice; ++i) s = fmaf(xr[i], wr[i], s);
       }
-      part[tr * E_pad + e] = s;
+      out[(size_t)t * E_pad + e] = s;
     }
   }
-  __syncthreads();
+}
 
-  const bool split_sum = BF16 && ksplit;
-  // softmax + top-k: wave w handles tokens 4w..4w+3
-  for (int tt = 0; tt < kRouteTok / kWaves; ++tt) {
-    const int tr = wave * (kRouteTok / kWaves) + tt;
-    const int t = tok0 + tr;
-    float lg[4], key[4];
+__global__ __launch_bounds__(256) void route_topk_kernel(
+    const float* __restrict__ part, int KS, int T, int E, int E_pad, int k,
+    const float* __restrict__ logit_bias, const float* __restrict__ sel_bias,
+    int32_t* __restrict__ ids, float* __restrict__ gates, float* __restrict__ psum_part) {
+  __shared__ float prob[TOPK_TOK][256];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int tt = 0; tt < TOPK_TOK / 4; ++tt) {
+    const int tr = wave * (TOPK_TOK / 4) + tt;
+    const int t = blockIdx.x * TOPK_TOK + tr;
+    if (t >= T) {                     // uniform across the wave
+#pragma unroll
+      for (int i = 0; i < 4; ++i) prob[tr][lane + 64 * i] = 0.f;
+      continue;
+    }
+    float lg[4], pr[4];
     bool live[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      int e = lane + 64 * i;
+      const int e = lane + 64 * i;
       live[i] = e < E;
       float v = -INFINITY;
-      if (live[i]) {
-        v = part[tr * E_pad + e];
-        if (split_sum) {
-          v += part[(1 * kRouteTok + tr) * E_pad + e];
-          v += part[(2 * kRouteTok + tr) * E_pad + e];
-          v += part[(3 * kRouteTok + tr) * E_pad + e];
-        }
-        if (logit_bias) v += logit_bias[e];
-      }
+      if (live[i]) v = sum_partials(part, KS, T, E_pad, t, e) + (logit_bias ? logit_bias[e] : 0.f);
       lg[i] = v;
-      key[i] = live[i] ? (sel_bias ? v + sel_bias[e] : v) : -INFINITY;
     }
-    float m = wave_max(fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3])));
-    float ex[4], loc = 0.f;
+    int my_e;
+    float my_g;
+    token_topk(lg, live, sel_bias, k, lane, pr, my_e, my_g);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      ex[i] = live[i] ? expf(lg[i] - m) : 0.f;
-      loc += ex[i];
-    }
-    const float s = wave_sum(loc);
-    const float inv = 1.0f / s;
-    float pr[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) pr[i] = ex[i] * inv;
-    // keep probabilities for the per-workgroup sums (slot 0 entries of this token;
-    // each lane overwrites only what it alone has read)
-    if (t < T) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (live[i]) part[tr * E_pad + lane + 64 * i] = pr[i];
-    } else {
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (live[i]) part[tr * E_pad + lane + 64 * i] = 0.f;
-    }
-    if (t >= T) continue;  // uniform across the wave
-    bool taken[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) taken[i] = !live[i];
-    int my_e = 0;
-    float my_p = 0.f;
-    for (int j = 0; j < k; ++j) {
-      float bk = -INFINITY;
-      int be = 0x7fffffff;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        int e = lane + 64 * i;
-        if (!taken[i] && (key[i] > bk || (key[i] == bk && e < be))) { bk = key[i]; be = e; }
-      }
-#pragma unroll
-      for (int o = 32; o > 0; o >>= 1) {
-        float ok = __shfl_xor(bk, o);
-        int oe = __shfl_xor(be, o);
-        if (ok > bk || (ok == bk && oe < be)) { bk = ok; be = oe; }
-      }
-      const int owner = be & 63, sl = be >> 6;
-      float cand = sl == 0 ? pr[0] : sl == 1 ? pr[1] : sl == 2 ? pr[2] : pr[3];
-      float pw = __shfl(cand, owner);
-      if (lane == owner) {
-        if (sl == 0) taken[0] = true;
-        else if (sl == 1) taken[1] = true;
-        else if (sl == 2) taken[2] = true;
-        else taken[3] = true;
-      }
-      if (lane == j) { my_e = be; my_p = pw; }
-    }
-    const float psel = wave_sum(lane < k ? my_p : 0.f);
+    for (int i = 0; i < 4; ++i) prob[tr][lane + 64 * i] = pr[i];
     if (lane < k) {
       ids[(size_t)t * k + lane] = my_e;
-      gates[(size_t)t * k + lane] = my_p / psel;
+      gates[(size_t)t * k + lane] = my_g;
     }
   }
   if (psum_part) {
     __syncthreads();
     for (int e = tid; e < E; e += 256) {
       float s = 0.f;
-      for (int tr = 0; tr < kRouteTok; ++tr) s += part[tr * E_pad + e];
+      for (int tr = 0; tr < TOPK_TOK; ++tr) s += prob[tr][e];
       psum_part[(size_t)blockIdx.x * E + e] = s;
     }
   }
 }
 
-// prob_sum[e] = sum over router workgroups (in order) of their partial sums
+// prob_sum[e] = sum over top-k workgroups (in order) of their partial sums
 __global__ __launch_bounds__(256) void psum_reduce_kernel(const float* __restrict__ part, int nblk,
                                                           int E, float* __restrict__ out) {
   for (int e = threadIdx.x; e < E; e += 256) {
@@ -221,25 +194,56 @@ __global__ __launch_bounds__(256) void psum_reduce_kernel(const float* __restric
 
 }  // namespace
 
+int route_ksplit(const moe_problem& p) {
+  const int E_pad = ceil_div(p.E, 16) * 16;
+  const long long base = (long long)ceil_div(p.T, TM) * ceil_div(E_pad, EN);
+  int ks = 1;
+  // split d while the grid is small and each slice keeps >= 256 columns (whole 32-column
+  // k-steps for every wave of a workgroup that also splits its slice 4 ways)
+  while (base * ks < 512 && ks < 16 && p.d % (ks * 2 * 128) == 0 && p.d / (ks * 2) >= 256)
+    ks *= 2;
+  return ks;
+}
+
+size_t route_partial_bytes(const moe_problem& p) {
+  const int E_pad = ceil_div(p.E, 16) * 16;
+  return (size_t)route_ksplit(p) * p.T * E_pad * sizeof(float);
+}
+
+int route_topk_blocks(const moe_problem& p) { return ceil_div(p.T, TOPK_TOK); }
+
+hipError_t launch_route_logits(const moe_problem& p, const void* x, const void* w_gate,
+                               float* logits_part, hipStream_t s) {
+  if (p.T == 0) return hipSuccess;
+  const int E_pad = ceil_div(p.E, 16) * 16;
+  const int KS = route_ksplit(p);
+  dim3 grid(ceil_div(p.T, TM), ceil_div(E_pad, EN), KS);
+  if (p.dtype == MOE_BF16)
+    hipLaunchKernelGGL(route_logits_kernel<true>, grid, dim3(256), 0, s, x, w_gate, p.T, p.d, p.E,
+                       E_pad, KS, logits_part);
+  else
+    hipLaunchKernelGGL(route_logits_kernel<false>, grid, dim3(256), 0, s, x, w_gate, p.T, p.d,
+                       p.E, E_pad, KS, logits_part);
+  return hipGetLastError();
+}
+
 hipError_t launch_route(const moe_problem& p, const void* x, const void* w_gate,
                         const float* logit_bias, const float* sel_bias, int32_t* ids,
-                        float* gates, float* prob_sum, float* psum_part, hipStream_t s) {
-  const int nblk = ceil_div(p.T, kRouteTok);
-  const int n_tiles = ceil_div(p.E, 16);
-  const int E_pad = n_tiles * 16;
-  const bool ksplit = p.dtype == MOE_BF16 && n_tiles < kWaves;
-  const size_t lds = (size_t)(ksplit ? 4 : 1) * kRouteTok * E_pad * sizeof(float);
-  float* part = prob_sum ? psum_part : nullptr;
-  if (nblk == 0) {
-    if (!prob_sum) return hipSuccess;
-  } else if (p.dtype == MOE_BF16)
-    hipLaunchKernelGGL(route_kernel<true>, dim3(nblk), dim3(256), lds, s, x, w_gate, logit_bias,
-                       sel_bias, p.T, p.d, p.E, p.k, ids, gates, part);
-  else
-    hipLaunchKernelGGL(route_kernel<false>, dim3(nblk), dim3(256), lds, s, x, w_gate, logit_bias,
-                       sel_bias, p.T, p.d, p.E, p.k, ids, gates, part);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess || !prob_sum) return err;
+                        float* gates, float* prob_sum, float* logits_part, float* psum_part,
+                        hipStream_t s) {
+  const int E_pad = ceil_div(p.E, 16) * 16;
+  const int KS = route_ksplit(p);
+  const int nblk = route_topk_blocks(p);
+  hipError_t err = launch_route_logits(p, x, w_gate, logits_part, s);
+  if (err != hipSuccess) return err;
+  if (p.T > 0) {
+    hipLaunchKernelGGL(route_topk_kernel, dim3(nblk), dim3(256), 0, s, logits_part, KS, p.T, p.E,
+                       E_pad, p.k, logit_bias, sel_bias, ids, gates,
+                       prob_sum ? psum_part : nullptr);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  if (!prob_sum) return hipSuccess;
   hipLaunchKernelGGL(psum_reduce_kernel, dim3(1), dim3(256), 0, s, psum_part, nblk, p.E, prob_sum);
   return hipGetLastError();
 }

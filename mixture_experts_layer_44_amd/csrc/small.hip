@@ -1,0 +1,170 @@
+// Small-batch routing in one launch: top-k + probability sums + grouping by expert (with the
+// capacity limit) + grouped-GEMM schedule, for T*k <= 1024 (decode-sized batches).
+//
+// Same definitions as route.hip (top-k, renormalised gates: "MoE Architecture" §2 "Gating
+// Function"; "MoE (Mixture of Experts) Deep Dive", "Weighted Sum Output") and align.hip
+// (histogram, prefix sum, stable order by expert, first-come capacity dropping: "Mixture of
+// experts (MoE)" handbook, "Implementation"; "MoE Architecture" §2 "Expert capacity and
+// token dropping"); the outputs are bit-identical to those launches. At decode sizes each
+// of those steps is a few microseconds of launch latency and almost no work, so a single
+// 1024-thread workgroup does them back to back out of LDS.
+#include "topk.h"
+
+namespace moe {
+
+namespace {
+
+constexpr int NWAVE = 16;
+
+// exclusive scan of v over the first 512 threads (others pass 0); all 1024 threads call it
+__device__ int scan512(int v, int* tmp, int* total) {
+  const int tid = threadIdx.x;
+  if (tid < 512) tmp[tid] = v;
+  __syncthreads();
+  for (int o = 1; o < 512; o <<= 1) {
+    int add = (tid < 512 && tid >= o) ? tmp[tid - o] : 0;
+    __syncthreads();
+    if (tid < 512) tmp[tid] += add;
+    __syncthreads();
+  }
+  const int incl = tid < 512 ? tmp[tid] : 0;
+  *total = tmp[511];
+  __syncthreads();
+  return incl - v;
+}
+
+__global__ __launch_bounds__(1024) void route_align_small_kernel(
+    const float* __restrict__ part, int KS, int T, int E, int E_pad, int k,
+    const float* __restrict__ logit_bias, const float* __restrict__ sel_bias, int cap,
+    int32_t* __restrict__ ids, float* __restrict__ gates, float* __restrict__ prob_sum,
+    int32_t* __restrict__ counts_pre, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ sorted_assign, int32_t* __restrict__ assign_pos, int n_shared,
+    Schedule sc) {
+  __shared__ int s_ids[1024];
+  __shared__ int wcnt[NWAVE][256];    // assignments of expert e in wave w
+  __shared__ float wpsum[NWAVE][256]; // per-wave probability sums
+  __shared__ int s_off[257];
+  __shared__ int tmp[512];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = T * k;
+
+  // ---- top-k: wave w takes tokens w, w+16, ...
+  float ps[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int t = wave; t < T; t += NWAVE) {
+    float lg[4], pr[4];
+    bool live[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = lane + 64 * i;
+      live[i] = e < E;
+      float v = -INFINITY;
+      if (live[i]) v = sum_partials(part, KS, T, E_pad, t, e) + (logit_bias ? logit_bias[e] : 0.f);
+      lg[i] = v;
+    }
+    int my_e;
+    float my_g;
+    token_topk(lg, live, sel_bias, k, lane, pr, my_e, my_g);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) ps[i] += pr[i];
+    if (lane < k) {
+      ids[(size_t)t * k + lane] = my_e;
+      gates[(size_t)t * k + lane] = my_g;
+      s_ids[t * k + lane] = my_e;
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) wpsum[wave][lane + 64 * i] = ps[i];
+  for (int i = tid; i < NWAVE * 256; i += 1024) (&wcnt[0][0])[i] = 0;
+  __syncthreads();
+  if (prob_sum && tid < E) {
+    float s = 0.f;
+    for (int w = 0; w < NWAVE; ++w) s += wpsum[w][tid];
+    prob_sum[tid] = s;
+  }
+
+  // ---- grouping: one assignment per thread, ranks from ballots + per-wave counts
+  const int a = tid;
+  const int e = a < n ? s_ids[a] : -1;
+  const bool valid = e >= 0;
+  const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  int my_rank = 0;
+  uint64_t active = __ballot(valid);
+  while (active) {
+    const int leader = __ffsll((unsigned long long)active) - 1;
+    const int le = __shfl(e, leader);
+    const uint64_t msk = __ballot(valid && e == le);
+    if (valid && e == le) {
+      my_rank = __popcll(msk & lt_mask);
+      if (lane == leader) wcnt[wave][e] = __popcll(msk);
+    }
+    active &= ~msk;
+  }
+  __syncthreads();
+  int c = 0, kept = 0;
+  if (tid < E) {
+    for (int w = 0; w < NWAVE; ++w) c += wcnt[w][tid];
+    kept = (cap >= 0 && c > cap) ? cap : c;
+  }
+  int total;
+  const int off = scan512(tid < E ? kept : 0, tmp, &total);
+  if (tid < E) {
+    counts_pre[tid] = c;
+    counts[tid] = kept;
+    offsets[tid] = off;
+    s_off[tid] = off;
+  }
+  if (tid == 0) {
+    offsets[E] = total;
+    s_off[E] = total;
+  }
+  __syncthreads();
+  if (a < n) {
+    int pos = -1;
+    if (valid) {
+      int rank = my_rank;
+      for (int w = 0; w < wave; ++w) rank += wcnt[w][e];
+      if (cap < 0 || rank < cap) {
+        pos = s_off[e] + rank;
+        sorted_assign[pos] = a;
+      }
+    }
+    assign_pos[a] = pos;
+  }
+
+  // ---- grouped-GEMM schedule (same as schedule_kernel)
+  const int G = E + n_shared;
+  int rows = 0;
+  if (tid < E) rows = s_off[tid + 1] - s_off[tid];
+  else if (tid < G) rows = T;
+  const int mts = (rows + sc.BM - 1) / sc.BM;
+  int mt_total;
+  const int base = scan512(tid < G ? mts : 0, tmp, &mt_total);
+  if (tid < G) {
+    const int m0 = min(base, sc.max_mtiles);
+    const int m1 = min(base + mts, sc.max_mtiles);
+    sc.grp_rows[tid] = min(rows, (m1 - m0) * sc.BM);
+    sc.grp_off[tid] = tid < E ? s_off[tid] : 0;
+    sc.mt_start[tid] = m0;
+    for (int m = m0; m < m1; ++m) sc.mt_group[m] = tid;
+  }
+  if (tid == 0) sc.mt_start[G] = min(mt_total, sc.max_mtiles);
+}
+
+}  // namespace
+
+bool small_routing(const moe_problem& p) { return (long long)p.T * p.k <= 1024; }
+
+hipError_t launch_route_align_small(const moe_problem& p, int cap, const float* logits_part,
+                                    const float* logit_bias, const float* sel_bias, int32_t* ids,
+                                    float* gates, float* prob_sum, int32_t* counts_pre,
+                                    int32_t* counts, int32_t* offsets, int32_t* sorted_assign,
+                                    int32_t* assign_pos, const Schedule& sc, hipStream_t s) {
+  const int E_pad = ceil_div(p.E, 16) * 16;
+  hipLaunchKernelGGL(route_align_small_kernel, dim3(1), dim3(1024), 0, s, logits_part,
+                     route_ksplit(p), p.T, p.E, E_pad, p.k, logit_bias, sel_bias, cap, ids, gates,
+                     prob_sum, counts_pre, counts, offsets, sorted_assign, assign_pos, p.n_shared,
+                     sc);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -19,9 +19,11 @@ Only one GPU: --gpus N > 1 exits with a message.
 from __future__ import annotations
 
 import argparse
+import csv
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -35,9 +37,11 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)   # flop per byte
 KERNEL_SOURCES = {"gate_up": "gemm.hip", "down": "gemm.hip", "route": "route.hip",
                   "align": "align.hip", "schedule": "align.hip", "combine": "combine.hip"}
-KERNEL_NAMES = {"gate_up": "gemm_bf16_kernel<true>", "down": "gemm_bf16_kernel<false>",
-                "route": "route_kernel", "align": "align_*_kernel", "schedule": "schedule_kernel",
-                "combine": "combine_kernel"}
+KERNEL_NAMES = {"gate_up": "gemm_bf16_kernel<..., true> (gate-up + SwiGLU)",
+                "down": "gemm_bf16_kernel<..., false> (down projection)"}
+# rocprofv3 kernel-name patterns of the two grouped GEMMs and of the copy used for calibration
+KERNEL_PATTERNS = {"gate_up": r"gemm_(bf16|f32)_kernel<.*true>", "down": r"gemm_(bf16|f32)_kernel<.*false>"}
+COPY_PATTERN = r"copyBuffer"
 
 
 def log(*a):
@@ -109,6 +113,63 @@ def traffic_from_profile(stage: str, workload: str):
     return rec.get("traffic_bytes_per_launch")
 
 
+def _counter_rows(csv_path: str, counter: str):
+    """(kernel name, value) of every dispatch in a rocprofv3 counter_collection CSV."""
+    with open(csv_path) as f:
+        return [(r["Kernel_Name"], float(r["Counter_Value"])) for r in csv.DictReader(f)
+                if r["Counter_Name"] == counter]
+
+
+def write_traffic(fetch_csv: str, write_csv: str, workload: str, calib_mib: int, command: str):
+    """Turn two rocprofv3 --pmc passes (FETCH_SIZE, then WRITE_SIZE; KiB per dispatch) over
+    `bench.py --calib-copy-mib M` into HBM bytes per launch of each grouped GEMM.
+
+    Each counter is scaled by what it reads for the plain device-to-device copy of M MiB that
+    the same run makes (M MiB read, M MiB written), so a counter that over- or under-counts
+    by a constant factor is corrected. Writes profiles/traffic_<stage>_<workload>.json."""
+    res = {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = _counter_rows(path, counter)
+        copies = [v for n, v in rows if re.search(COPY_PATTERN, n)]
+        if not copies:
+            raise SystemExit(f"no copy-kernel dispatch in {path}: run bench.py with --calib-copy-mib")
+        # the blit may be split over several dispatches: use the largest (the bulk of the copy)
+        calib = calib_mib * 1024.0 / max(copies)        # true KiB / counted KiB
+        for stage, pat in KERNEL_PATTERNS.items():
+            vals = [v for n, v in rows if re.search(pat, n)]
+            if vals:
+                res.setdefault(stage, {})[counter] = dict(
+                    kib_per_dispatch=sum(vals) / len(vals), dispatches=len(vals), scale=calib,
+                    bytes_per_launch=sum(vals) / len(vals) * calib * 1024.0)
+    os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
+    for stage, c in res.items():
+        if "FETCH_SIZE" not in c or "WRITE_SIZE" not in c:
+            continue
+        rec = {"stage": stage, "workload": workload, "kernel": KERNEL_NAMES[stage],
+               "source_sha": source_sha(stage),
+               "traffic_bytes_per_launch": c["FETCH_SIZE"]["bytes_per_launch"]
+               + c["WRITE_SIZE"]["bytes_per_launch"],
+               "fetch": c["FETCH_SIZE"], "write": c["WRITE_SIZE"],
+               "calibration": f"device-to-device copy of {calib_mib} MiB in the same run",
+               "command": command}
+        path = os.path.join(ROOT, "profiles", f"traffic_{stage}_{workload}.json")
+        with open(path, "w") as f:
+            json.dump(rec, f, indent=1)
+        log(f"[bench] wrote {path}: {rec['traffic_bytes_per_launch'] / 1e9:.3f} GB per launch")
+
+
+def calibration_copy(mib: int, dev, reps: int = 3):
+    """A plain device-to-device copy of `mib` MiB (torch issues it as the runtime's blit
+    kernel), for scaling the memory counters."""
+    import torch
+    src = torch.empty(mib << 20, dtype=torch.uint8, device=dev).fill_(1)
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 # ----------------------------------------------------------------------------- CPU baseline
 def cpu_baseline(w, inp, sample_tokens: int):
     """The fp64 oracle, as it stands, on the first `sample_tokens` tokens of the
@@ -154,10 +215,21 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mixtral_prefill")
-    ap.add_argument("--cpu-sample", type=int, default=512,
+    ap.add_argument("--cpu-sample", type=int, default=2048,
                     help="tokens of the workload the CPU oracle baseline runs on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="first run a plain copy of this many MiB (counter calibration)")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="post-process two rocprofv3 --pmc counter CSVs into "
+                         "profiles/traffic_<stage>_<workload>.json and exit (no GPU)")
+    ap.add_argument("--traffic-command", default="", help="command recorded with --write-traffic")
     args = ap.parse_args(argv)
+
+    if args.write_traffic:
+        write_traffic(args.write_traffic[0], args.write_traffic[1], args.workload,
+                      args.calib_copy_mib, args.traffic_command)
+        return 0
 
     if args.gpus != 1:
         print(f"bench.py measures one GPU only; --gpus {args.gpus} is not supported "
@@ -176,6 +248,8 @@ def main(argv=None):
     inp = workloads.generate(w, device=dev)
     torch.cuda.synchronize()
     log(f"[bench] inputs generated in {time.time() - t0:.1f} s")
+    if args.calib_copy_mib:
+        calibration_copy(args.calib_copy_mib, dev)
     p = moe.problem_for(w)
     ws = torch.empty(moe.workspace_bytes(p), dtype=torch.uint8, device=dev)
     y = torch.empty((w.T, w.d), dtype=torch.float32, device=dev)
@@ -238,6 +312,7 @@ def main(argv=None):
     roof["frac"] = roof["achieved"] / roof["peak"]
     roof["traffic"] = traffic_from_profile(dom, w.name)
     roof["kernel"] = KERNEL_NAMES[dom]
+    roof["launch_stream"] = "torch current stream (HIP events recorded around the launch)"
     roof["avg_launch_ms"] = stage_ms[dom]
     roof["algorithmic_per_launch"] = {"flops": kwk["flops"], "bytes": kwk["bytes"]}
 

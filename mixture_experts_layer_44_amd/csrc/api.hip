@@ -14,7 +14,7 @@ namespace {
 struct Layout {
   size_t logits_part, psum_part, blk_counts, blk_base, grp_rows, grp_off, mt_start, mt_group, h;
   size_t ids, gates, prob_sum, counts_pre, counts, offsets, sorted_assign, assign_pos;
-  size_t out_rows, shared_out;
+  size_t out_rows, out_rows_b, shared_out;
   size_t total;
   int max_mt, BM;
 };
@@ -52,6 +52,7 @@ Layout layout(const moe_problem& p) {
   L.sorted_assign = take(n * 4);
   L.assign_pos = take(n * 4);
   L.out_rows = take(n * p.d * 4);
+  L.out_rows_b = take(down_ksplit(p) == 2 ? n * p.d * 4 : 0);
   L.shared_out = take((size_t)p.n_shared * p.T * p.d * 4);
   L.total = off;
   return L;
@@ -189,8 +190,11 @@ MOE_API moe_status moe_expert_ffn(const moe_problem* p, const void* x, const voi
   const Schedule sc = schedule_in(*p, L, ws);
   hipError_t e = launch_schedule(*p, offsets, sc, stream);
   if (e != hipSuccess) return MOE_EHIP;
-  return hip_status(launch_expert_ffn(*p, x, w1, w3, w2, ws1, ws3, ws2, sorted_assign, sc,
-                                      at<void>(ws, L.h), out_rows, shared_out, stream));
+  float* out_b = down_ksplit(*p) == 2 ? at<float>(ws, L.out_rows_b) : nullptr;
+  e = launch_expert_ffn(*p, x, w1, w3, w2, ws1, ws3, ws2, sorted_assign, sc, at<void>(ws, L.h),
+                        out_rows, out_b, shared_out, stream);
+  if (e == hipSuccess && out_b) e = launch_add_rows(*p, out_rows, out_b, offsets, stream);
+  return hip_status(e);
 }
 
 MOE_API moe_status moe_combine(const moe_problem* p, const float* out_rows,
@@ -200,7 +204,7 @@ MOE_API moe_status moe_combine(const moe_problem* p, const float* out_rows,
   if (st != MOE_OK) return st;
   if (p->T > 0 && (!out_rows || !assign_pos || !topk_w || !y)) return MOE_EINVAL;
   if (p->T > 0 && p->n_shared && !shared_out) return MOE_EINVAL;
-  return hip_status(launch_combine(*p, out_rows, assign_pos, topk_w, shared_out, y, stream));
+  return hip_status(launch_combine(*p, out_rows, nullptr, assign_pos, topk_w, shared_out, y, stream));
 }
 
 MOE_API moe_status moe_balance(const moe_problem* p, const int32_t* counts_pre,
@@ -237,6 +241,7 @@ moe_status forward_impl(const moe_problem* p, const void* x, const void* w_gate,
   int32_t* sa = sorted_assign ? sorted_assign : at<int32_t>(ws, L.sorted_assign);
   int32_t* ap = assign_pos ? assign_pos : at<int32_t>(ws, L.assign_pos);
   float* out_rows = at<float>(ws, L.out_rows);
+  float* out_b = down_ksplit(*p) == 2 ? at<float>(ws, L.out_rows_b) : nullptr;
   float* shared_out = p->n_shared ? at<float>(ws, L.shared_out) : nullptr;
   auto mark = [&](int i) { return ev ? hipEventRecord(ev[i], stream) : hipSuccess; };
   if (mark(0) != hipSuccess) return MOE_EHIP;
@@ -261,9 +266,9 @@ moe_status forward_impl(const moe_problem* p, const void* x, const void* w_gate,
       return MOE_EHIP;
   }
   e = launch_expert_ffn(*p, x, w1, w3, w2, ws1, ws3, ws2, sa, sc, at<void>(ws, L.h), out_rows,
-                        shared_out, stream, ev ? ev[4] : nullptr);
+                        out_b, shared_out, stream, ev ? ev[4] : nullptr);
   if (e != hipSuccess || mark(5) != hipSuccess) return MOE_EHIP;
-  e = launch_combine(*p, out_rows, ap, gates, shared_out, y, stream);
+  e = launch_combine(*p, out_rows, out_b, ap, gates, shared_out, y, stream);
   if (e != hipSuccess || mark(6) != hipSuccess) return MOE_EHIP;
   return MOE_OK;
 }

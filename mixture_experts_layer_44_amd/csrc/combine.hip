@@ -15,6 +15,7 @@ namespace moe {
 namespace {
 
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ out_rows,
+                                                      const float* __restrict__ out_rows_b,
                                                       const int32_t* __restrict__ assign_pos,
                                                       const float* __restrict__ topk_w,
                                                       const float* __restrict__ shared_out, int d,
@@ -35,7 +36,14 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     for (int j = 0; j < k; ++j) {
       const int r = pos[j];
       if (r >= 0 && r < n) {
-        const f32x4 v = *(const f32x4*)(out_rows + (size_t)r * d + 4 * c);
+        f32x4 v = *(const f32x4*)(out_rows + (size_t)r * d + 4 * c);
+        if (out_rows_b) {   // the down GEMM's two K halves
+          const f32x4 vb = *(const f32x4*)(out_rows_b + (size_t)r * d + 4 * c);
+          v[0] += vb[0];
+          v[1] += vb[1];
+          v[2] += vb[2];
+          v[3] += vb[3];
+        }
         const float g = wt[j];
         acc[0] = fmaf(g, v[0], acc[0]);
         acc[1] = fmaf(g, v[1], acc[1]);
@@ -44,6 +52,24 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
       }
     }
     *(f32x4*)(y + (size_t)t * d + 4 * c) = acc;
+  }
+}
+
+// out_rows[r] += out_rows_b[r] over the kept rows (offsets[E] of them), 16 bytes per lane
+__global__ __launch_bounds__(256) void add_rows_kernel(float* __restrict__ out_rows,
+                                                       const float* __restrict__ out_rows_b,
+                                                       const int32_t* __restrict__ offsets, int E,
+                                                       int d) {
+  const long long n4 = (long long)offsets[E] * (d >> 2);
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n4;
+       i += (long long)gridDim.x * 256) {
+    f32x4 a = ((f32x4*)out_rows)[i];
+    const f32x4 b = ((const f32x4*)out_rows_b)[i];
+    a[0] += b[0];
+    a[1] += b[1];
+    a[2] += b[2];
+    a[3] += b[3];
+    ((f32x4*)out_rows)[i] = a;
   }
 }
 
@@ -73,11 +99,20 @@ __global__ __launch_bounds__(256) void balance_kernel(const int32_t* __restrict_
 
 }  // namespace
 
-hipError_t launch_combine(const moe_problem& p, const float* out_rows, const int32_t* assign_pos,
-                          const float* topk_w, const float* shared_out, float* y, hipStream_t s) {
+hipError_t launch_combine(const moe_problem& p, const float* out_rows, const float* out_rows_b,
+                          const int32_t* assign_pos, const float* topk_w, const float* shared_out,
+                          float* y, hipStream_t s) {
   if (p.T == 0) return hipSuccess;
-  hipLaunchKernelGGL(combine_kernel, dim3(p.T), dim3(256), 0, s, out_rows, assign_pos, topk_w,
-                     shared_out, p.d, p.k, y);
+  hipLaunchKernelGGL(combine_kernel, dim3(p.T), dim3(256), 0, s, out_rows, out_rows_b, assign_pos,
+                     topk_w, shared_out, p.d, p.k, y);
+  return hipGetLastError();
+}
+
+hipError_t launch_add_rows(const moe_problem& p, float* out_rows, const float* out_rows_b,
+                           const int32_t* offsets, hipStream_t s) {
+  if (p.T == 0) return hipSuccess;
+  hipLaunchKernelGGL(add_rows_kernel, dim3(1024), dim3(256), 0, s, out_rows, out_rows_b, offsets,
+                     p.E, p.d);
   return hipGetLastError();
 }
 

@@ -64,6 +64,8 @@ struct GemmArgs {
   bf16_t* H;            // gate-up output
   float* out_rows;      // down output, routed rows (sorted order)
   float* shared_out;    // down output, shared rows (token order)
+  float* out_rows_b;    // down with K split in two: the second half's routed rows
+  int ksplit;           // 1, or 2 for the down GEMM (routed groups only, no shared expert)
 };
 
 struct TileCoord {
@@ -71,14 +73,17 @@ struct TileCoord {
 };
 
 // Tile for this workgroup, or false if it has none. Uniform across the workgroup.
-__device__ __forceinline__ bool tile_coord(const Schedule& sc, int NT, int bn, TileCoord& tc) {
+__device__ __forceinline__ bool tile_coord(const Schedule& sc, int NT, int bn, TileCoord& tc,
+                                           int S = 1, int* half = nullptr) {
   const int total = sc.mt_start[sc.G] * NT;
   const int bid = blockIdx.x;
   const int xcd = bid & 7, slot = bid >> 3;
-  const int per = (total + 7) >> 3;
+  const int per = (total * S + 7) >> 3;
   if (slot >= per) return false;
-  const int L = xcd * per + slot;
-  if (L >= total) return false;
+  int L = xcd * per + slot;
+  if (L >= total * S) return false;
+  if (half) *half = L / total;   // work unit L = half * total + tile
+  L %= total;
   const int g = sc.mt_group[L / NT];
   const int ms = sc.mt_start[g];
   const int mtg = sc.mt_start[g + 1] - ms;
@@ -93,7 +98,11 @@ __device__ __forceinline__ bool tile_coord(const Schedule& sc, int NT, int bn, T
   return true;
 }
 
-__device__ __forceinline__ float silu_f(float u) { return u / (1.0f + __expf(-u)); }
+// SiLU(u) = u * sigmoid(u) with the hardware exp and reciprocal (a few ulp; the result is
+// rounded to bf16 right after). exp(-u) overflows to inf for u < -88: u * rcp(inf) = -0.
+__device__ __forceinline__ float silu_f(float u) {
+  return u * __builtin_amdgcn_rcpf(1.0f + __expf(-u));
+}
 
 // Element offset of (row, 16-byte chunk) in a swizzled [rows][BK] bf16 stage. A 256-byte
 // LDS cycle spans W = 128/BK rows; chunk c of row r goes to slot c ^ ((r / W) % (BK/8)), so
@@ -272,6 +281,199 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs args) 
     }
 }
 
+// ------------------------------------------------------------------ wide tiles, staggered rings
+// For experts with ~1000 rows, a 256x256 tile with one 64 KB K step in flight is paced by its
+// loads: under full load 64 KB per CU does not land within one step's MFMAs, while 32 KB does,
+// and a third 64 KB stage does not fit in 160 KB of LDS. Here both operands still go straight
+// to LDS, but in two rings of different depth: A (gathered x rows / H rows) in 3 slots, issued
+// two steps ahead, and B (weights) in 2 slots, issued one step ahead:
+//   step kt: wait until only this wave's A loads of step kt+1 are outstanding (so A(kt) and
+//            B(kt) have landed); barrier; issue B(kt+1) -> B slot (kt+1)%2 and then
+//            A(kt+2) -> A slot (kt+2)%3; MFMAs of step kt on A slot kt%3 and B slot kt%2.
+// Every slot written in step kt was last read in step kt-1, which all waves finished before
+// this step's barrier.
+template <int BM, int BNB, int WM, int WN, bool GATEUP>
+__global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_st_kernel(GemmArgs args) {
+  constexpr int BK = 64, NKS = BK / 16;
+  constexpr int NW = WM * WN;
+  constexpr int CHUNKS = BK / 8, RPI = 64 / CHUNKS;
+  constexpr int TM = BM / WM, TNB = BNB / WN;
+  constexpr int FM = TM / 32, FN = TNB / 32;
+  constexpr int ASLOT = BM * BK, BSLOT = BNB * BK;   // bf16 elements
+  constexpr int DMA_A = BM * CHUNKS / 64 / NW;       // 1 KB A loads per wave per step
+  constexpr int DMA_B = BNB * CHUNKS / 64 / NW;      // 1 KB B loads per wave per step
+  static_assert(DMA_A * 64 * NW == BM * CHUNKS && DMA_B * 64 * NW == BNB * CHUNKS, "even split");
+  constexpr int FEAT = GATEUP ? BNB / 2 : BNB;
+  static_assert(!GATEUP || FN % 2 == 0, "u and v fragments pair up");
+  static_assert((BNB / 2) % RPI == 0, "a B row group stays within one matrix");
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[3 * ASLOT + 2 * BSLOT];
+  bf16_t* const As = smem;
+  bf16_t* const Bs = smem + 3 * ASLOT;
+
+  // with the K range split in two (down GEMM only), work unit = (half, tile): half h runs
+  // steps [h*KT/2, (h+1)*KT/2) and writes its partial rows to its own buffer
+  const int S = GATEUP ? 1 : args.ksplit;
+  TileCoord tc;
+  int half = 0;
+  if (!tile_coord(args.sc, args.N / FEAT, FEAT, tc, S, &half)) return;
+  const bool shared_grp = tc.g >= args.E;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int K = args.K, N = args.N;
+  const int KT = K / BK / S;                          // steps of this work unit
+  const int k0 = half * KT * BK;                      // its first K element
+
+  // A load i of this wave fills slot rows q*RPI.. (q = wave*DMA_A + i): lane l writes physical
+  // 16-byte chunk l%CHUNKS of row q*RPI + l/CHUNKS and so fetches the logical chunk that the
+  // swizzle puts there (the swizzle is an involution).
+  // (32-bit element offsets from the matrix base keep the register count down: every offset
+  // is below 2^31 for the sizes the entry points accept)
+  uint32_t aoff[DMA_A];
+#pragma unroll
+  for (int i = 0; i < DMA_A; ++i) {
+    const int q = wave * DMA_A + i;
+    const int row = q * RPI + lane / CHUNKS;
+    const int lchunk = (swz<BK>(row, lane % CHUNKS) - row * BK) >> 3;
+    int srow;
+    if (GATEUP) {
+      const int r = tc.m_local * BM + row;
+      const int rr = r < tc.rows ? r : 0;             // padding rows repeat the first row
+      const int tok = shared_grp ? rr : args.sorted_assign[tc.off + rr] / args.k;
+      srow = (unsigned)tok < (unsigned)args.T ? tok : 0;
+    } else {
+      srow = tc.mt_global * BM + row;
+    }
+    aoff[i] = (uint32_t)srow * (uint32_t)K + lchunk * 8;
+  }
+  // B load i of this wave fills B slot rows q*RPI.. (q = wave*DMA_B + i) the same way; the
+  // rows of one load lie in one matrix, so its base is wave-uniform.
+  const bf16_t* bmat[DMA_B];
+  uint32_t boff[DMA_B];
+#pragma unroll
+  for (int i = 0; i < DMA_B; ++i) {
+    const int q = wave * DMA_B + i;
+    const int br = q * RPI + lane / CHUNKS;
+    const int lchunk = (swz<BK>(br, lane % CHUNKS) - br * BK) >> 3;
+    const bool second = GATEUP && q * RPI >= BNB / 2;
+    const bf16_t* mat;
+    if (GATEUP)
+      mat = shared_grp ? (second ? args.S1 : args.S0)
+                       : (second ? args.B1 : args.B0) + (size_t)tc.g * N * K;
+    else
+      mat = shared_grp ? args.S0 : args.B0 + (size_t)tc.g * N * K;
+    bmat[i] = mat;
+    boff[i] = (uint32_t)(tc.n0 + (second ? br - BNB / 2 : br)) * (uint32_t)K + lchunk * 8;
+  }
+
+  auto issue_a = [&](int kt, int slot) {
+    bf16_t* dst = As + slot * ASLOT;
+#pragma unroll
+    for (int i = 0; i < DMA_A; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(args.A + aoff[i] + k0 + kt * BK),
+                                       (lds_ptr_t)(dst + (wave * DMA_A + i) * RPI * BK), 16, 0, 0);
+  };
+  auto issue_b = [&](int kt, int slot) {
+    bf16_t* dst = Bs + slot * BSLOT;
+#pragma unroll
+    for (int i = 0; i < DMA_B; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)(bmat[i] + boff[i] + k0 + kt * BK),
+                                       (lds_ptr_t)(dst + (wave * DMA_B + i) * RPI * BK), 16, 0, 0);
+  };
+
+  const int wm = wave / WN, wn = wave % WN;
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  // Fragment reads. Lane l reads row (block base + l%32) at 16-byte chunk 2*ks + l/32. Every
+  // fragment block starts at a multiple of 16 rows, so a lane's swizzle key ((row/2) % 8) is the
+  // same for all its rows: the address is one per-lane offset per sub-step plus a
+  // compile-time offset per fragment.
+  static_assert(BK == 64 && TM % 32 == 0 && (BNB / 2 / WN) % 32 == 0, "swizzle key per lane");
+  const int fr = lane & 31, fkc = lane >> 5;
+  const int sw = (fr >> 1) & (CHUNKS - 1);
+  const int fw = GATEUP ? BNB / 2 / WN : TNB;        // B rows per wave and matrix half
+  int aoffs[NKS], boffs[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    const int ch = ((2 * ks + fkc) ^ sw) << 3;
+    aoffs[ks] = (wm * TM + fr) * BK + ch;
+    boffs[ks] = (wn * fw + fr) * BK + ch;
+  }
+  auto bconst = [](int j) {   // compile-time B row of fragment j relative to the wave's rows
+    return GATEUP ? (j < FN / 2 ? 0 : BNB / 2) + (j % (FN / 2)) * 32 : j * 32;
+  };
+
+  // prologue: B(0), A(0), A(1) in flight
+  issue_b(0, 0);
+  issue_a(0, 0);
+  issue_a(KT > 1 ? 1 : 0, 1);
+  for (int kt = 0; kt < KT; ++kt) {
+    __builtin_amdgcn_s_waitcnt(wait_vm(DMA_A));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    issue_b(kt + 1 < KT ? kt + 1 : KT - 1, (kt + 1) & 1);
+    issue_a(kt + 2 < KT ? kt + 2 : KT - 1, (kt + 2) % 3);
+    const bf16_t* a = As + (kt % 3) * ASLOT;
+    const bf16_t* b = Bs + (kt & 1) * BSLOT;
+    __builtin_amdgcn_iglp_opt(1);
+    bf16x8 af[2][FM], bfr[2][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) af[0][i] = *(const bf16x8*)&a[aoffs[0] + i * 32 * BK];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) bfr[0][j] = *(const bf16x8*)&b[boffs[0] + bconst(j) * BK];
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const int cur = ks & 1, nxt = cur ^ 1;
+      if (ks + 1 < NKS) {
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+          af[nxt][i] = *(const bf16x8*)&a[aoffs[ks + 1] + i * 32 * BK];
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          bfr[nxt][j] = *(const bf16x8*)&b[boffs[ks + 1] + bconst(j) * BK];
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bfr[cur][j], acc[i][j],
+                                                              0, 0, 0);
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(wait_vm(0));
+
+  // ---- epilogue (same accumulator layout and stores as gemm_bf16_kernel)
+  constexpr int FO = GATEUP ? FN / 2 : FN;
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FO; ++j) {
+      const int col = tc.n0 + wn * (FEAT / WN) + j * 32 + fr;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int lr = wm * TM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (GATEUP) {
+          const float u = acc[i][j][r];
+          const float v = acc[i][j + FN / 2][r];
+          args.H[(size_t)(tc.mt_global * BM + lr) * N + col] = f32_to_bf16(silu_f(u) * v);
+        } else {
+          const int rg = tc.m_local * BM + lr;
+          if (rg < tc.rows) {
+            float* dst = shared_grp ? args.shared_out + (size_t)rg * N
+                                    : (half ? args.out_rows_b : args.out_rows) +
+                                          (size_t)(tc.off + rg) * N;
+            dst[col] = acc[i][j][r];
+          }
+        }
+      }
+    }
+}
+
 // ------------------------------------------------------------------ fp32 path (VALU)
 constexpr int BM32 = kGemmBM32, BN32 = 64, BK32 = 16;
 
@@ -383,6 +585,18 @@ bool gemm_wide(const moe_problem& p) {
   return p.dtype == MOE_BF16 && p.d % 256 == 0 && expected_rows(p) >= 768.0;
 }
 
+// The down GEMM of the wide class has few tiles (d/256 per 256-row m-tile); when they fill
+// the 256 CUs in a poor number of rounds (e.g. 576 tiles = 2.25 rounds), split K in two so the
+// half-tiles fill the rounds better. The halves go to two buffers that the combine adds.
+int down_ksplit(const moe_problem& p) {
+  if (!gemm_wide(p) || p.n_shared) return 1;
+  constexpr double kCUs = 256.0;                        // MI355X compute units
+  const double mtiles = p.E * (expected_rows(p) / 256.0 + 0.5);   // +1/2 tile of padding
+  const double tiles = std::ceil(mtiles) * (p.d / 256);
+  const double r1 = std::ceil(tiles / kCUs), r2 = std::ceil(2.0 * tiles / kCUs) / 2.0;
+  return r2 < 0.9 * r1 ? 2 : 1;
+}
+
 bool gemm_small(const moe_problem& p) { return p.dtype == MOE_BF16 && expected_rows(p) <= 48.0; }
 
 template <int BM, int BNB_UP, int WM_UP, int WN_UP, int BNB_DN, int WM_DN, int WN_DN, int BK, int ST>
@@ -400,10 +614,25 @@ hipError_t launch_bf16(const moe_problem& p, const GemmArgs& a, const GemmArgs& 
   return hipGetLastError();
 }
 
+template <int BM, int BNB_UP, int WM_UP, int WN_UP, int BNB_DN, int WM_DN, int WN_DN>
+hipError_t launch_bf16_rs(const moe_problem& p, const GemmArgs& a, const GemmArgs& b,
+                          hipStream_t s, hipEvent_t between) {
+  hipLaunchKernelGGL((gemm_bf16_st_kernel<BM, BNB_UP, WM_UP, WN_UP, true>),
+                     dim3(grid_for(a.sc.max_mtiles, p.d_ff / (BNB_UP / 2))), dim3(WM_UP * WN_UP * 64),
+                     0, s, a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  if (between && (err = hipEventRecord(between, s)) != hipSuccess) return err;
+  hipLaunchKernelGGL((gemm_bf16_st_kernel<BM, BNB_DN, WM_DN, WN_DN, false>),
+                     dim3(grid_for(b.sc.max_mtiles * b.ksplit, p.d / BNB_DN)),
+                     dim3(WM_DN * WN_DN * 64), 0, s, b);
+  return hipGetLastError();
+}
+
 hipError_t launch_expert_ffn(const moe_problem& p, const void* x, const void* w1, const void* w3,
                              const void* w2, const void* ws1, const void* ws3, const void* ws2,
                              const int32_t* sorted_assign, const Schedule& sc, void* h,
-                             float* out_rows, float* shared_out, hipStream_t s,
+                             float* out_rows, float* out_rows_b, float* shared_out, hipStream_t s,
                              hipEvent_t between) {
   if (p.dtype == MOE_BF16) {
     GemmArgs a{};
@@ -433,7 +662,11 @@ hipError_t launch_expert_ffn(const moe_problem& p, const void* x, const void* w1
     b.sc = sc;
     b.out_rows = out_rows;
     b.shared_out = shared_out;
-    if (sc.BM == 256) return launch_bf16<256, 256, 4, 2, 256, 4, 2, 64, 2>(p, a, b, s, between);
+    a.ksplit = 1;
+    b.ksplit = down_ksplit(p);
+    b.out_rows_b = out_rows_b;
+    if (b.ksplit == 2 && !out_rows_b) return hipErrorInvalidValue;
+    if (sc.BM == 256) return launch_bf16_rs<256, 256, 4, 2, 256, 4, 2>(p, a, b, s, between);
     if (sc.BM == 32) return launch_bf16<32, 256, 1, 4, 128, 1, 4, 64, 4>(p, a, b, s, between);
     return launch_bf16<128, 256, 2, 4, 128, 2, 4, 32, 6>(p, a, b, s, between);
   }

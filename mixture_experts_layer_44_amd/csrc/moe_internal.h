@@ -88,14 +88,24 @@ hipError_t launch_align(const moe_problem& p, int cap, const int32_t* ids, int32
 hipError_t launch_schedule(const moe_problem& p, const int32_t* offsets, const Schedule& sc,
                            hipStream_t s);
 
+// 2 when the down GEMM runs with its K range split in two (second half -> out_rows_b)
+int down_ksplit(const moe_problem& p);
+
+// out_rows_b: [T*k, d] second-half partial rows, required when down_ksplit(p) == 2
 hipError_t launch_expert_ffn(const moe_problem& p, const void* x, const void* w1, const void* w3,
                              const void* w2, const void* ws1, const void* ws3, const void* ws2,
                              const int32_t* sorted_assign, const Schedule& sc, void* h,
-                             float* out_rows, float* shared_out, hipStream_t s,
+                             float* out_rows, float* out_rows_b, float* shared_out, hipStream_t s,
                              hipEvent_t between = nullptr);
 
-hipError_t launch_combine(const moe_problem& p, const float* out_rows, const int32_t* assign_pos,
-                          const float* topk_w, const float* shared_out, float* y, hipStream_t s);
+// out_rows_b may be null; when given, each expert row is out_rows + out_rows_b
+hipError_t launch_combine(const moe_problem& p, const float* out_rows, const float* out_rows_b,
+                          const int32_t* assign_pos, const float* topk_w, const float* shared_out,
+                          float* y, hipStream_t s);
+
+// out_rows[r] += out_rows_b[r] for the first offsets[E] rows
+hipError_t launch_add_rows(const moe_problem& p, float* out_rows, const float* out_rows_b,
+                           const int32_t* offsets, hipStream_t s);
 
 hipError_t launch_balance(const moe_problem& p, const int32_t* counts_pre, const float* prob_sum,
                           float alpha, float* f, float* P, float* L, hipStream_t s);

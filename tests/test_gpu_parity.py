@@ -48,6 +48,8 @@ SMALL = [
       zipf_s=1.1),
     # wide tiles (expected >= 768 rows per expert) on a small problem
     W("bf16_wide", T=1600, d=512, E=4, k=2, d_ff=384, seed=113, n_shared=1, d_ff_shared=384),
+    # wide tiles with the down GEMM's K range split in two (few down tiles, no shared expert)
+    W("bf16_wide_ksplit", T=2048, d=1024, E=4, k=2, d_ff=1024, seed=114),
 ]
 
 
@@ -164,11 +166,18 @@ def test_align_ignores_out_of_range_ids():
 
 
 # ---------------------------------------------------------------------------- composition
-def test_entry_points_compose_to_forward():
+COMPOSE = [
+    W("compose", T=333, d=256, E=24, k=3, d_ff=384, seed=201, n_shared=1, d_ff_shared=384,
+      sel_bias=True, capacity_factor=1.1),
+    # wide tiles, down GEMM split in K: expert_ffn sums the halves itself, forward in the combine
+    W("compose_ksplit", T=2048, d=1024, E=4, k=2, d_ff=1024, seed=202, capacity_factor=0.9),
+]
+
+
+@pytest.mark.parametrize("w", COMPOSE, ids=[w.name for w in COMPOSE])
+def test_entry_points_compose_to_forward(w):
     """route -> align -> expert_ffn -> combine gives the same bits as moe_forward."""
     import mixture_experts_layer_44_amd as moe
-    w = W("compose", T=333, d=256, E=24, k=3, d_ff=384, seed=201, n_shared=1, d_ff_shared=384,
-          sel_bias=True, capacity_factor=1.1)
     inp = {k: (None if v is None else v.cuda()) for k, v in workloads.generate(w).items()}
     p = moe.problem_for(w)
     y, r = moe.forward(p, inp["x"], inp["w_gate"], inp["w1"], inp["w3"], inp["w2"],

@@ -281,18 +281,23 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs args) 
     }
 }
 
-// ------------------------------------------------------------------ wide tiles, staggered rings
-// For experts with ~1000 rows, a 256x256 tile with one 64 KB K step in flight is paced by its
-// loads: under full load 64 KB per CU does not land within one step's MFMAs, while 32 KB does,
-// and a third 64 KB stage does not fit in 160 KB of LDS. Here both operands still go straight
-// to LDS, but in two rings of different depth: A (gathered x rows / H rows) in 3 slots, issued
-// two steps ahead, and B (weights) in 2 slots, issued one step ahead:
-//   step kt: wait until only this wave's A loads of step kt+1 are outstanding (so A(kt) and
-//            B(kt) have landed); barrier; issue B(kt+1) -> B slot (kt+1)%2 and then
-//            A(kt+2) -> A slot (kt+2)%3; MFMAs of step kt on A slot kt%3 and B slot kt%2.
-// Every slot written in step kt was last read in step kt-1, which all waves finished before
-// this step's barrier.
-template <int BM, int BNB, int WM, int WN, bool GATEUP>
+// ------------------------------------------------------------------ staggered rings
+// With one K step of loads in flight (a 2-stage ring) a large tile is paced by the latency of
+// its loads under full load, not by its MFMAs, and a third full stage does not fit in 160 KB
+// of LDS. Here both operands still go straight to LDS, but in two rings of different depth:
+// the "shallow" operand in 2 slots, issued one step ahead, and the "deep" operand in 3 slots,
+// issued two steps ahead. Which one is deep depends on where its data lives: the weights
+// (B) when they stream from HBM (small experts, each weight tile read by one m-tile), the
+// gathered rows (A) when the weight tiles are shared in L2 by several m-tiles.
+//   step kt: wait until only this wave's deep loads issued in step kt-1 are outstanding (so the
+//            shallow loads of step kt, issued before them, and the deep loads of step kt,
+//            issued earlier, have landed); barrier; issue shallow(kt+1) and then deep(kt+2);
+//            MFMAs of step kt.
+// Vector-memory loads retire in order, so issuing the shallow operand first is what lets the
+// wait leave the deep loads in flight; the same ordering is why a deeper ring would not help:
+// every wait retires all loads issued before the shallow operand's loads of that step. Every slot written in step kt was last read in step
+// kt-1, which all waves finished before this step's barrier.
+template <int BM, int BNB, int WM, int WN, bool GATEUP, bool DEEPB>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_st_kernel(GemmArgs args) {
   constexpr int BK = 64, NKS = BK / 16;
   constexpr int NW = WM * WN;
@@ -306,9 +311,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_st_kernel(GemmArgs arg
   constexpr int FEAT = GATEUP ? BNB / 2 : BNB;
   static_assert(!GATEUP || FN % 2 == 0, "u and v fragments pair up");
   static_assert((BNB / 2) % RPI == 0, "a B row group stays within one matrix");
-  __shared__ __attribute__((aligned(1024))) bf16_t smem[3 * ASLOT + 2 * BSLOT];
+  constexpr int DS = 3;                                     // slots of the deep ring
+  constexpr int NA = DEEPB ? 2 : DS, NB = DEEPB ? DS : 2;   // ring slots of A and B
+  static_assert((NA * ASLOT + NB * BSLOT) * 2 <= 160 * 1024, "rings fit in LDS");
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[NA * ASLOT + NB * BSLOT];
   bf16_t* const As = smem;
-  bf16_t* const Bs = smem + 3 * ASLOT;
+  bf16_t* const Bs = smem + NA * ASLOT;
 
   // with the K range split in two (down GEMM only), work unit = (half, tile): half h runs
   // steps [h*KT/2, (h+1)*KT/2) and writes its partial rows to its own buffer
@@ -393,7 +401,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_st_kernel(GemmArgs arg
   // fragment block starts at a multiple of 16 rows, so a lane's swizzle key ((row/2) % 8) is the
   // same for all its rows: the address is one per-lane offset per sub-step plus a
   // compile-time offset per fragment.
-  static_assert(BK == 64 && TM % 32 == 0 && (BNB / 2 / WN) % 32 == 0, "swizzle key per lane");
+  static_assert(BK == 64 && TM % 32 == 0 && (GATEUP ? BNB / 2 / WN : TNB) % 32 == 0,
+                "fragment row blocks start at multiples of 32 rows");
   const int fr = lane & 31, fkc = lane >> 5;
   const int sw = (fr >> 1) & (CHUNKS - 1);
   const int fw = GATEUP ? BNB / 2 / WN : TNB;        // B rows per wave and matrix half
@@ -408,18 +417,27 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_st_kernel(GemmArgs arg
     return GATEUP ? (j < FN / 2 ? 0 : BNB / 2) + (j % (FN / 2)) * 32 : j * 32;
   };
 
-  // prologue: B(0), A(0), A(1) in flight
-  issue_b(0, 0);
-  issue_a(0, 0);
-  issue_a(KT > 1 ? 1 : 0, 1);
+  // prologue: shallow(0), deep(0), deep(1)
+  auto issue_shallow = [&](int kt) {
+    if (DEEPB) issue_a(kt, kt & 1);
+    else issue_b(kt, kt & 1);
+  };
+  auto issue_deep = [&](int kt) {
+    if (DEEPB) issue_b(kt, kt % DS);
+    else issue_a(kt, kt % DS);
+  };
+  constexpr int DEEP_OPS = DEEPB ? DMA_B : DMA_A;
+  issue_shallow(0);
+#pragma unroll
+  for (int s = 0; s < DS - 1; ++s) issue_deep(s < KT ? s : KT - 1);
   for (int kt = 0; kt < KT; ++kt) {
-    __builtin_amdgcn_s_waitcnt(wait_vm(DMA_A));
+    __builtin_amdgcn_s_waitcnt(wait_vm(DEEP_OPS));
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    issue_b(kt + 1 < KT ? kt + 1 : KT - 1, (kt + 1) & 1);
-    issue_a(kt + 2 < KT ? kt + 2 : KT - 1, (kt + 2) % 3);
-    const bf16_t* a = As + (kt % 3) * ASLOT;
-    const bf16_t* b = Bs + (kt & 1) * BSLOT;
+    issue_shallow(kt + 1 < KT ? kt + 1 : KT - 1);
+    issue_deep(kt + DS - 1 < KT ? kt + DS - 1 : KT - 1);
+    const bf16_t* a = As + (kt % NA) * ASLOT;
+    const bf16_t* b = Bs + (kt % NB) * BSLOT;
     __builtin_amdgcn_iglp_opt(1);
     bf16x8 af[2][FM], bfr[2][FN];
 #pragma unroll
@@ -602,6 +620,7 @@ bool gemm_small(const moe_problem& p) { return p.dtype == MOE_BF16 && expected_r
 template <int BM, int BNB_UP, int WM_UP, int WN_UP, int BNB_DN, int WM_DN, int WN_DN, int BK, int ST>
 hipError_t launch_bf16(const moe_problem& p, const GemmArgs& a, const GemmArgs& b, hipStream_t s,
                        hipEvent_t between) {
+  if (p.d_ff % (BNB_UP / 2) || p.d % BNB_DN) return hipErrorInvalidValue;   // n-tiles cover N
   hipLaunchKernelGGL((gemm_bf16_kernel<BM, BNB_UP, WM_UP, WN_UP, BK, ST, true>),
                      dim3(grid_for(a.sc.max_mtiles, p.d_ff / (BNB_UP / 2))), dim3(WM_UP * WN_UP * 64),
                      0, s, a);
@@ -614,16 +633,17 @@ hipError_t launch_bf16(const moe_problem& p, const GemmArgs& a, const GemmArgs& 
   return hipGetLastError();
 }
 
-template <int BM, int BNB_UP, int WM_UP, int WN_UP, int BNB_DN, int WM_DN, int WN_DN>
-hipError_t launch_bf16_rs(const moe_problem& p, const GemmArgs& a, const GemmArgs& b,
+template <int BM, int BNB_UP, int WM_UP, int WN_UP, int BNB_DN, int WM_DN, int WN_DN, bool DEEPB>
+hipError_t launch_bf16_st(const moe_problem& p, const GemmArgs& a, const GemmArgs& b,
                           hipStream_t s, hipEvent_t between) {
-  hipLaunchKernelGGL((gemm_bf16_st_kernel<BM, BNB_UP, WM_UP, WN_UP, true>),
+  if (p.d_ff % (BNB_UP / 2) || p.d % BNB_DN) return hipErrorInvalidValue;   // n-tiles cover N
+  hipLaunchKernelGGL((gemm_bf16_st_kernel<BM, BNB_UP, WM_UP, WN_UP, true, DEEPB>),
                      dim3(grid_for(a.sc.max_mtiles, p.d_ff / (BNB_UP / 2))), dim3(WM_UP * WN_UP * 64),
                      0, s, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   if (between && (err = hipEventRecord(between, s)) != hipSuccess) return err;
-  hipLaunchKernelGGL((gemm_bf16_st_kernel<BM, BNB_DN, WM_DN, WN_DN, false>),
+  hipLaunchKernelGGL((gemm_bf16_st_kernel<BM, BNB_DN, WM_DN, WN_DN, false, DEEPB>),
                      dim3(grid_for(b.sc.max_mtiles * b.ksplit, p.d / BNB_DN)),
                      dim3(WM_DN * WN_DN * 64), 0, s, b);
   return hipGetLastError();
@@ -666,9 +686,11 @@ hipError_t launch_expert_ffn(const moe_problem& p, const void* x, const void* w1
     b.ksplit = down_ksplit(p);
     b.out_rows_b = out_rows_b;
     if (b.ksplit == 2 && !out_rows_b) return hipErrorInvalidValue;
-    if (sc.BM == 256) return launch_bf16_rs<256, 256, 4, 2, 256, 4, 2>(p, a, b, s, between);
+    if (sc.BM == 256) return launch_bf16_st<256, 256, 4, 2, 256, 4, 2, false>(p, a, b, s, between);
     if (sc.BM == 32) return launch_bf16<32, 256, 1, 4, 128, 1, 4, 64, 4>(p, a, b, s, between);
-    return launch_bf16<128, 256, 2, 4, 128, 2, 4, 32, 6>(p, a, b, s, between);
+    // down tiles of 256 output features need d % 256 == 0 (the entry points accept d % 128)
+    if (p.d % 256 == 0) return launch_bf16<128, 256, 2, 4, 256, 2, 4, 64, 3>(p, a, b, s, between);
+    return launch_bf16<128, 256, 2, 4, 128, 2, 4, 64, 3>(p, a, b, s, between);
   }
   GemmArgs32 a{};
   a.A = (const float*)x;

@@ -22,7 +22,7 @@ __all__ = [
     "Problem", "MoEError", "lib", "make_problem", "validate", "capacity", "workspace_bytes",
     "route", "align", "expert_ffn", "combine", "balance", "forward", "LIB_PATH",
     "MOE_OK", "MOE_EINVAL", "MOE_EUNSUPPORTED", "MOE_EWORKSPACE", "MOE_EHIP", "forward_staged",
-    "STAGES", "problem_for",
+    "STAGES", "problem_for", "PreparedForward",
 ]
 
 # stage names of moe_forward_staged, in event order (events 1..6 close these stages)
@@ -289,6 +289,49 @@ def forward(p: Problem, x, w_gate, w1, w3, w2, logit_bias=None, sel_bias=None, w
     r["sorted_assign"] = r["sorted_assign"][:n]
     r["assign_pos"] = r["assign_pos"][:n]
     return y, r
+
+
+class PreparedForward:
+    """moe_forward with its arguments checked and marshalled once.
+
+    Calling the object enqueues one forward on the current stream (the stream
+    that is current at the call, so it can be captured into a HIP graph) and
+    returns y. There are no per-call checks: the tensors passed here must stay
+    alive, and every call reads their current contents. For decode-sized
+    layers the per-call host work of forward() is comparable to the GPU time
+    of the layer; this keeps it to one foreign call."""
+
+    def __init__(self, p: Problem, x, w_gate, w1, w3, w2, logit_bias=None, sel_bias=None,
+                 ws1=None, ws3=None, ws2=None, ws=None, y=None):
+        dev, dt = x.device, _dt(p)
+        _need(x, "x", (p.T, p.d), dt, dev)
+        _need(w_gate, "w_gate", (p.E, p.d), dt, dev)
+        _need(w1, "w1", (p.E, p.d_ff, p.d), dt, dev)
+        _need(w3, "w3", (p.E, p.d_ff, p.d), dt, dev)
+        _need(w2, "w2", (p.E, p.d, p.d_ff), dt, dev)
+        _need(logit_bias, "logit_bias", (p.E,), torch.float32, dev, optional=True)
+        _need(sel_bias, "sel_bias", (p.E,), torch.float32, dev, optional=True)
+        if p.n_shared:
+            _need(ws1, "ws1", (1, p.d_ff_shared, p.d), dt, dev)
+            _need(ws3, "ws3", (1, p.d_ff_shared, p.d), dt, dev)
+            _need(ws2, "ws2", (1, p.d, p.d_ff_shared), dt, dev)
+        if y is None:
+            y = torch.empty((p.T, p.d), dtype=torch.float32, device=dev)
+        else:
+            _need(y, "y", (p.T, p.d), torch.float32, dev)
+        ws = _workspace(p, dev, ws)
+        self.p, self.y, self.ws, self.dev = p, y, ws, dev
+        self._keep = (x, w_gate, w1, w3, w2, logit_bias, sel_bias, ws1, ws3, ws2)
+        self._args = (ctypes.byref(p), _ptr(x), _ptr(w_gate), _ptr(logit_bias), _ptr(sel_bias),
+                      _ptr(w1), _ptr(w3), _ptr(w2), _ptr(ws1), _ptr(ws3), _ptr(ws2), _ptr(y),
+                      None, None, None, None, None, None, None, None, _ptr(ws), ws.numel())
+        self._fn = _lib.moe_forward
+
+    def __call__(self):
+        st = self._fn(*self._args, torch.cuda.current_stream(self.dev).cuda_stream)
+        if st != MOE_OK:
+            raise MoEError("moe_forward", st)
+        return self.y
 
 
 def forward_staged(p: Problem, x, w_gate, w1, w3, w2, events, logit_bias=None, sel_bias=None,

@@ -252,8 +252,8 @@ moe_status forward_impl(const moe_problem* p, const void* x, const void* w_gate,
     e = launch_route_logits(*p, x, w_gate, at<float>(ws, L.logits_part), stream);
     if (e != hipSuccess || mark(1) != hipSuccess) return MOE_EHIP;
     e = launch_route_align_small(*p, kernel_cap(*p), at<float>(ws, L.logits_part), logit_bias,
-                                 sel_bias, ids, gates, prob_sum, cpre, cnt, offs, sa, ap, sc,
-                                 stream);
+                                 sel_bias, ids, gates, prob_sum, at<float>(ws, L.psum_part), cpre,
+                                 cnt, offs, sa, ap, sc, stream);
     if (e != hipSuccess || mark(2) != hipSuccess || mark(3) != hipSuccess) return MOE_EHIP;
   } else {
     e = launch_route(*p, x, w_gate, logit_bias, sel_bias, ids, gates, prob_sum,

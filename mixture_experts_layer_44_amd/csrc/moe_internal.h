@@ -72,9 +72,16 @@ hipError_t launch_route_logits(const moe_problem& p, const void* x, const void* 
 bool small_routing(const moe_problem& p);
 hipError_t launch_route_align_small(const moe_problem& p, int cap, const float* logits_part,
                                     const float* logit_bias, const float* sel_bias, int32_t* ids,
-                                    float* gates, float* prob_sum, int32_t* counts_pre,
-                                    int32_t* counts, int32_t* offsets, int32_t* sorted_assign,
-                                    int32_t* assign_pos, const Schedule& sc, hipStream_t s);
+                                    float* gates, float* prob_sum, float* psum_part,
+                                    int32_t* counts_pre, int32_t* counts, int32_t* offsets,
+                                    int32_t* sorted_assign, int32_t* assign_pos, const Schedule& sc,
+                                    hipStream_t s);
+
+// top-k of every token from the logits partials; per-workgroup probability sums to psum_part
+// (when not null)
+hipError_t launch_route_topk(const moe_problem& p, const float* logits_part,
+                             const float* logit_bias, const float* sel_bias, int32_t* ids,
+                             float* gates, float* psum_part, hipStream_t s);
 
 hipError_t launch_route(const moe_problem& p, const void* x, const void* w_gate,
                         const float* logit_bias, const float* sel_bias, int32_t* ids,

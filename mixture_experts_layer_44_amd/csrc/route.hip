@@ -138,15 +138,17 @@ __global__ __launch_bounds__(256) void route_logits_kernel(const void* __restric
   }
 }
 
+// TOK tokens per workgroup of 4 waves (TOK/4 per wave, one after the other)
+template <int TOK>
 __global__ __launch_bounds__(256) void route_topk_kernel(
     const float* __restrict__ part, int KS, int T, int E, int E_pad, int k,
     const float* __restrict__ logit_bias, const float* __restrict__ sel_bias,
     int32_t* __restrict__ ids, float* __restrict__ gates, float* __restrict__ psum_part) {
-  __shared__ float prob[TOPK_TOK][256];
+  __shared__ float prob[TOK][256];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int tt = 0; tt < TOPK_TOK / 4; ++tt) {
-    const int tr = wave * (TOPK_TOK / 4) + tt;
-    const int t = blockIdx.x * TOPK_TOK + tr;
+  for (int tt = 0; tt < TOK / 4; ++tt) {
+    const int tr = wave * (TOK / 4) + tt;
+    const int t = blockIdx.x * TOK + tr;
     if (t >= T) {                     // uniform across the wave
 #pragma unroll
       for (int i = 0; i < 4; ++i) prob[tr][lane + 64 * i] = 0.f;
@@ -176,7 +178,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
     __syncthreads();
     for (int e = tid; e < E; e += 256) {
       float s = 0.f;
-      for (int tr = 0; tr < TOPK_TOK; ++tr) s += prob[tr][e];
+      for (int tr = 0; tr < TOK; ++tr) s += prob[tr][e];
       psum_part[(size_t)blockIdx.x * E + e] = s;
     }
   }
@@ -210,7 +212,25 @@ size_t route_partial_bytes(const moe_problem& p) {
   return (size_t)route_ksplit(p) * p.T * E_pad * sizeof(float);
 }
 
-int route_topk_blocks(const moe_problem& p) { return ceil_div(p.T, TOPK_TOK); }
+// small batches take one token per wave (4 per workgroup) so the top-k spreads over more CUs
+int route_topk_tokens(const moe_problem& p) { return small_routing(p) ? 4 : TOPK_TOK; }
+int route_topk_blocks(const moe_problem& p) { return ceil_div(p.T, route_topk_tokens(p)); }
+
+hipError_t launch_route_topk(const moe_problem& p, const float* logits_part,
+                             const float* logit_bias, const float* sel_bias, int32_t* ids,
+                             float* gates, float* psum_part, hipStream_t s) {
+  if (p.T == 0) return hipSuccess;
+  const int E_pad = ceil_div(p.E, 16) * 16;
+  const int KS = route_ksplit(p);
+  const int nblk = route_topk_blocks(p);
+  if (route_topk_tokens(p) == 4)
+    hipLaunchKernelGGL(route_topk_kernel<4>, dim3(nblk), dim3(256), 0, s, logits_part, KS, p.T,
+                       p.E, E_pad, p.k, logit_bias, sel_bias, ids, gates, psum_part);
+  else
+    hipLaunchKernelGGL(route_topk_kernel<TOPK_TOK>, dim3(nblk), dim3(256), 0, s, logits_part, KS,
+                       p.T, p.E, E_pad, p.k, logit_bias, sel_bias, ids, gates, psum_part);
+  return hipGetLastError();
+}
 
 hipError_t launch_route_logits(const moe_problem& p, const void* x, const void* w_gate,
                                float* logits_part, hipStream_t s) {
@@ -231,18 +251,12 @@ hipError_t launch_route(const moe_problem& p, const void* x, const void* w_gate,
                         const float* logit_bias, const float* sel_bias, int32_t* ids,
                         float* gates, float* prob_sum, float* logits_part, float* psum_part,
                         hipStream_t s) {
-  const int E_pad = ceil_div(p.E, 16) * 16;
-  const int KS = route_ksplit(p);
   const int nblk = route_topk_blocks(p);
   hipError_t err = launch_route_logits(p, x, w_gate, logits_part, s);
   if (err != hipSuccess) return err;
-  if (p.T > 0) {
-    hipLaunchKernelGGL(route_topk_kernel, dim3(nblk), dim3(256), 0, s, logits_part, KS, p.T, p.E,
-                       E_pad, p.k, logit_bias, sel_bias, ids, gates,
-                       prob_sum ? psum_part : nullptr);
-    err = hipGetLastError();
-    if (err != hipSuccess) return err;
-  }
+  err = launch_route_topk(p, logits_part, logit_bias, sel_bias, ids, gates,
+                          prob_sum ? psum_part : nullptr, s);
+  if (err != hipSuccess) return err;
   if (!prob_sum) return hipSuccess;
   hipLaunchKernelGGL(psum_reduce_kernel, dim3(1), dim3(256), 0, s, psum_part, nblk, p.E, prob_sum);
   return hipGetLastError();

@@ -1,5 +1,6 @@
-// Small-batch routing in one launch: top-k + probability sums + grouping by expert (with the
-// capacity limit) + grouped-GEMM schedule, for T*k <= 1024 (decode-sized batches).
+// Small-batch grouping in one launch: probability sums + grouping by expert (with the capacity
+// limit) + grouped-GEMM schedule, for T*k <= 1024 (decode-sized batches). The top-k before it
+// runs one token per wave over many workgroups (route.hip).
 //
 // Same definitions as route.hip (top-k, renormalised gates: "MoE Architecture" §2 "Gating
 // Function"; "MoE (Mixture of Experts) Deep Dive", "Weighted Sum Output") and align.hip
@@ -33,59 +34,33 @@ __device__ int scan512(int v, int* tmp, int* total) {
   return incl - v;
 }
 
-__global__ __launch_bounds__(1024) void route_align_small_kernel(
-    const float* __restrict__ part, int KS, int T, int E, int E_pad, int k,
-    const float* __restrict__ logit_bias, const float* __restrict__ sel_bias, int cap,
-    int32_t* __restrict__ ids, float* __restrict__ gates, float* __restrict__ prob_sum,
-    int32_t* __restrict__ counts_pre, int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
+__global__ __launch_bounds__(1024) void align_small_kernel(
+    const int32_t* __restrict__ ids, const float* __restrict__ psum_part, int nblk, int T, int E,
+    int k, int cap, float* __restrict__ prob_sum, int32_t* __restrict__ counts_pre,
+    int32_t* __restrict__ counts, int32_t* __restrict__ offsets,
     int32_t* __restrict__ sorted_assign, int32_t* __restrict__ assign_pos, int n_shared,
     Schedule sc) {
   __shared__ int s_ids[1024];
   __shared__ int wcnt[NWAVE][256];    // assignments of expert e in wave w
-  __shared__ float wpsum[NWAVE][256]; // per-wave probability sums
   __shared__ int s_off[257];
   __shared__ int tmp[512];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = T * k;
 
-  // ---- top-k: wave w takes tokens w, w+16, ...
-  float ps[4] = {0.f, 0.f, 0.f, 0.f};
-  for (int t = wave; t < T; t += NWAVE) {
-    float lg[4], pr[4];
-    bool live[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int e = lane + 64 * i;
-      live[i] = e < E;
-      float v = -INFINITY;
-      if (live[i]) v = sum_partials(part, KS, T, E_pad, t, e) + (logit_bias ? logit_bias[e] : 0.f);
-      lg[i] = v;
-    }
-    int my_e;
-    float my_g;
-    token_topk(lg, live, sel_bias, k, lane, pr, my_e, my_g);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) ps[i] += pr[i];
-    if (lane < k) {
-      ids[(size_t)t * k + lane] = my_e;
-      gates[(size_t)t * k + lane] = my_g;
-      s_ids[t * k + lane] = my_e;
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) wpsum[wave][lane + 64 * i] = ps[i];
-  for (int i = tid; i < NWAVE * 256; i += 1024) (&wcnt[0][0])[i] = 0;
-  __syncthreads();
+  // probability sums: the top-k workgroups' partials, added in workgroup order
   if (prob_sum && tid < E) {
     float s = 0.f;
-    for (int w = 0; w < NWAVE; ++w) s += wpsum[w][tid];
+    for (int b = 0; b < nblk; ++b) s += psum_part[(size_t)b * E + tid];
     prob_sum[tid] = s;
   }
+  if (tid < n) s_ids[tid] = ids[tid];
+  for (int i = tid; i < NWAVE * 256; i += 1024) (&wcnt[0][0])[i] = 0;
+  __syncthreads();
 
   // ---- grouping: one assignment per thread, ranks from ballots + per-wave counts
   const int a = tid;
   const int e = a < n ? s_ids[a] : -1;
-  const bool valid = e >= 0;
+  const bool valid = e >= 0 && e < E;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   int my_rank = 0;
   uint64_t active = __ballot(valid);
@@ -156,14 +131,16 @@ bool small_routing(const moe_problem& p) { return (long long)p.T * p.k <= 1024; 
 
 hipError_t launch_route_align_small(const moe_problem& p, int cap, const float* logits_part,
                                     const float* logit_bias, const float* sel_bias, int32_t* ids,
-                                    float* gates, float* prob_sum, int32_t* counts_pre,
-                                    int32_t* counts, int32_t* offsets, int32_t* sorted_assign,
-                                    int32_t* assign_pos, const Schedule& sc, hipStream_t s) {
-  const int E_pad = ceil_div(p.E, 16) * 16;
-  hipLaunchKernelGGL(route_align_small_kernel, dim3(1), dim3(1024), 0, s, logits_part,
-                     route_ksplit(p), p.T, p.E, E_pad, p.k, logit_bias, sel_bias, cap, ids, gates,
-                     prob_sum, counts_pre, counts, offsets, sorted_assign, assign_pos, p.n_shared,
-                     sc);
+                                    float* gates, float* prob_sum, float* psum_part,
+                                    int32_t* counts_pre, int32_t* counts, int32_t* offsets,
+                                    int32_t* sorted_assign, int32_t* assign_pos, const Schedule& sc,
+                                    hipStream_t s) {
+  hipError_t err = launch_route_topk(p, logits_part, logit_bias, sel_bias, ids, gates,
+                                     prob_sum ? psum_part : nullptr, s);
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(align_small_kernel, dim3(1), dim3(1024), 0, s, ids, psum_part,
+                     route_topk_blocks(p), p.T, p.E, p.k, cap, prob_sum, counts_pre, counts,
+                     offsets, sorted_assign, assign_pos, p.n_shared, sc);
   return hipGetLastError();
 }
 

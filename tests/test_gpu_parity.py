@@ -235,3 +235,30 @@ def test_workspace_reuse_across_shapes():
         y_ref = moe.forward(moe.problem_for(w), inp["x"], inp["w_gate"], inp["w1"], inp["w3"],
                             inp["w2"])
         assert torch.equal(y, y_ref)
+
+
+def test_prepared_forward_and_graph_replay():
+    """A prepared forward and its captured HIP graph give the eager forward's bits; the graph is
+    replayed several times with new inputs and eager work in between, each replay checked."""
+    import mixture_experts_layer_44_amd as moe
+    w = workloads.get("decode_T8")
+    inp = {k: (None if v is None else v.cuda()) for k, v in workloads.generate(w).items()}
+    p = moe.problem_for(w)
+    x = inp["x"].clone()
+    fwd = moe.PreparedForward(p, x, inp["w_gate"], inp["w1"], inp["w3"], inp["w2"])
+    y_eager = moe.forward(p, x, inp["w_gate"], inp["w1"], inp["w3"], inp["w2"])
+    assert torch.equal(fwd(), y_eager)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        fwd()
+    torch.cuda.synchronize()
+    gen = torch.Generator(device="cuda")
+    for i in range(4):
+        gen.manual_seed(1000 + i)
+        x.copy_(torch.randn(x.shape, generator=gen, device="cuda").to(x.dtype))
+        want = moe.forward(p, x, inp["w_gate"], inp["w1"], inp["w3"], inp["w2"])   # eager work
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(fwd.y, want), f"replay {i}"

@@ -39,9 +39,21 @@ KERNEL_SOURCES = {"gate_up": "gemm.hip", "down": "gemm.hip", "route": "route.hip
                   "align": "align.hip", "schedule": "align.hip", "combine": "combine.hip"}
 KERNEL_NAMES = {"gate_up": "gemm_bf16_kernel<..., true> (gate-up + SwiGLU)",
                 "down": "gemm_bf16_kernel<..., false> (down projection)"}
-# rocprofv3 kernel-name patterns of the two grouped GEMMs and of the copy used for calibration
-KERNEL_PATTERNS = {"gate_up": r"gemm_(bf16|f32)_kernel<.*true>", "down": r"gemm_(bf16|f32)_kernel<.*false>"}
-COPY_PATTERN = r"copyBuffer"
+COPY_PATTERN = r"copyBuffer"   # the runtime's blit kernel (the calibration copy)
+
+
+def gemm_stage(kernel_name: str):
+    """'gate_up' / 'down' for a grouped-GEMM kernel name as rocprofv3 prints it, else None.
+    The gate-up flag is the 7th template argument of gemm_bf16_kernel, the 5th of
+    gemm_bf16_st_kernel and the only one of gemm_f32_kernel."""
+    m = re.search(r"gemm_(bf16_st|bf16|f32)_kernel<([^>]*)>", kernel_name)
+    if not m:
+        return None
+    args = [a.strip() for a in m.group(2).split(",")]
+    pos = {"bf16": 6, "bf16_st": 4, "f32": 0}[m.group(1)]
+    if len(args) <= pos or args[pos] not in ("true", "false"):
+        return None
+    return "gate_up" if args[pos] == "true" else "down"
 
 
 def log(*a):
@@ -135,12 +147,14 @@ def write_traffic(fetch_csv: str, write_csv: str, workload: str, calib_mib: int,
             raise SystemExit(f"no copy-kernel dispatch in {path}: run bench.py with --calib-copy-mib")
         # the blit may be split over several dispatches: use the largest (the bulk of the copy)
         calib = calib_mib * 1024.0 / max(copies)        # true KiB / counted KiB
-        for stage, pat in KERNEL_PATTERNS.items():
-            vals = [v for n, v in rows if re.search(pat, n)]
+        for stage in ("gate_up", "down"):
+            vals = [v for n, v in rows if gemm_stage(n) == stage]
             if vals:
                 res.setdefault(stage, {})[counter] = dict(
                     kib_per_dispatch=sum(vals) / len(vals), dispatches=len(vals), scale=calib,
                     bytes_per_launch=sum(vals) / len(vals) * calib * 1024.0)
+    if not res:
+        raise SystemExit("no grouped-GEMM dispatch found in the counter files")
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
     for stage, c in res.items():
         if "FETCH_SIZE" not in c or "WRITE_SIZE" not in c:

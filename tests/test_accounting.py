@@ -40,3 +40,16 @@ def test_decode_t1_bytes():
     a = bench.algorithmic_work(w, [1] * 8 + [0] * 120)
     assert a["touched"] == 8
     assert abs(a["bytes"] - (8 * 3 * 2048 * 768 * 2 + 2048 * 2 + 128 * 2048 * 2 + 2048 * 4)) == 0
+
+
+def test_gemm_stage_names():
+    """The counter post-processing finds the gate-up / down flag in each GEMM kernel family."""
+    import bench
+    assert bench.gemm_stage("void moe::(anonymous namespace)::gemm_bf16_st_kernel<256, 256, 4, 2, "
+                            "true, false>(moe::(anonymous namespace)::GemmArgs)") == "gate_up"
+    assert bench.gemm_stage("moe::gemm_bf16_st_kernel<256, 256, 4, 2, false, false>(x)") == "down"
+    assert bench.gemm_stage("moe::gemm_bf16_kernel<128, 256, 2, 4, 64, 3, true>(x)") == "gate_up"
+    assert bench.gemm_stage("moe::gemm_bf16_kernel<32, 128, 1, 4, 64, 4, false>(x)") == "down"
+    assert bench.gemm_stage("moe::gemm_f32_kernel<false>(x)") == "down"
+    assert bench.gemm_stage("__amd_rocclr_copyBuffer") is None
+    assert bench.gemm_stage("moe::combine_kernel(float const*)") is None

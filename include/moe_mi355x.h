@@ -150,6 +150,19 @@ moe_status moe_combine(const moe_problem* p, const float* out_rows, const int32_
 moe_status moe_balance(const moe_problem* p, const int32_t* counts_pre, const float* prob_sum,
                        float alpha, float* f, float* P, float* L, hipStream_t stream);
 
+/* Auxiliary-loss-free balancing step ("MoE Architecture" §2 "Auxiliary-loss-free
+   balancing"; handbook "Load balancing"): the per-expert selection bias (the sel_bias
+   argument of moe_route / moe_forward, which only chooses experts) is lowered for an
+   overloaded expert and raised for an underloaded one. An expert is overloaded when
+   its count before capacity dropping exceeds the mean load T*k/E (compared exactly as
+   E*counts_pre[e] against T*k) and underloaded when below; at the mean it keeps its
+   bias. In fp32: sel_bias[e] += gamma * sign(T*k - E*counts_pre[e]).
+     counts_pre [E] as produced by moe_align / moe_forward (device);
+     sel_bias [E] fp32, updated in place (device);
+     gamma: step, finite and >= 0 (the pages give no value). EINVAL otherwise. */
+moe_status moe_bias_update(const moe_problem* p, const int32_t* counts_pre, float gamma,
+                           float* sel_bias, hipStream_t stream);
+
 /* The whole layer in one call: route -> align -> expert FFNs -> combine.
    y [T,d] fp32 out (required). Every routing output pointer may be NULL, in
    which case it lives in ws; when given, it receives the same values the

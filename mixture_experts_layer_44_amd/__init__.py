@@ -22,7 +22,7 @@ __all__ = [
     "Problem", "MoEError", "lib", "make_problem", "validate", "capacity", "workspace_bytes",
     "route", "align", "expert_ffn", "combine", "balance", "forward", "LIB_PATH",
     "MOE_OK", "MOE_EINVAL", "MOE_EUNSUPPORTED", "MOE_EWORKSPACE", "MOE_EHIP", "forward_staged",
-    "STAGES", "problem_for", "PreparedForward",
+    "STAGES", "problem_for", "PreparedForward", "bias_update",
 ]
 
 # stage names of moe_forward_staged, in event order (events 1..6 close these stages)
@@ -66,11 +66,13 @@ def _load() -> ctypes.CDLL:
     L.moe_expert_ffn.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     L.moe_combine.argtypes = [P, vp, vp, vp, vp, vp, vp]
     L.moe_balance.argtypes = [P, vp, vp, f32, vp, vp, vp, vp]
+    L.moe_bias_update.argtypes = [P, vp, f32, vp, vp]
     L.moe_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                               vp, vp, vp, vp, sz, vp]
     L.moe_forward_staged.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
     for fn in ("moe_validate", "moe_capacity", "moe_workspace_bytes", "moe_route", "moe_align",
-               "moe_expert_ffn", "moe_combine", "moe_balance", "moe_forward", "moe_forward_staged"):
+               "moe_expert_ffn", "moe_combine", "moe_balance", "moe_forward", "moe_forward_staged",
+               "moe_bias_update"):
         getattr(L, fn).restype = ctypes.c_int
     return L
 
@@ -289,6 +291,17 @@ def forward(p: Problem, x, w_gate, w1, w3, w2, logit_bias=None, sel_bias=None, w
     r["sorted_assign"] = r["sorted_assign"][:n]
     r["assign_pos"] = r["assign_pos"][:n]
     return y, r
+
+
+def bias_update(p: Problem, counts_pre, sel_bias, gamma: float):
+    """One auxiliary-loss-free balancing step on sel_bias (fp32 [E], updated in place) from
+    the pre-drop expert counts (int32 [E]). Returns sel_bias."""
+    dev = sel_bias.device
+    _need(counts_pre, "counts_pre", (p.E,), torch.int32, dev)
+    _need(sel_bias, "sel_bias", (p.E,), torch.float32, dev)
+    _check("moe_bias_update", _lib.moe_bias_update(ctypes.byref(p), _ptr(counts_pre),
+                                                   float(gamma), _ptr(sel_bias), _stream(dev)))
+    return sel_bias
 
 
 class PreparedForward:

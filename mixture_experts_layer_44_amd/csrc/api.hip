@@ -217,6 +217,15 @@ MOE_API moe_status moe_balance(const moe_problem* p, const int32_t* counts_pre,
   return hip_status(launch_balance(*p, counts_pre, prob_sum, alpha, f, P, L, stream));
 }
 
+MOE_API moe_status moe_bias_update(const moe_problem* p, const int32_t* counts_pre, float gamma,
+                                   float* sel_bias, hipStream_t stream) {
+  moe_status st = moe_validate(p);
+  if (st != MOE_OK) return st;
+  if (!counts_pre || !sel_bias) return MOE_EINVAL;
+  if (!std::isfinite(gamma) || gamma < 0.f) return MOE_EINVAL;
+  return hip_status(launch_bias_update(*p, counts_pre, gamma, sel_bias, stream));
+}
+
 namespace {
 
 moe_status forward_impl(const moe_problem* p, const void* x, const void* w_gate,

@@ -97,7 +97,25 @@ __global__ __launch_bounds__(256) void balance_kernel(const int32_t* __restrict_
   if (e == 0) L[0] = (float)((double)alpha * E * part[0]);
 }
 
+// sel_bias[e] += gamma * sign(T*k - E*counts_pre[e]) (64-bit integer comparison, fp32 step)
+__global__ __launch_bounds__(256) void bias_update_kernel(const int32_t* __restrict__ counts_pre,
+                                                          int T, int k, int E, float gamma,
+                                                          float* __restrict__ sel_bias) {
+  const int e = threadIdx.x;
+  if (e >= E) return;
+  const long long load = (long long)E * counts_pre[e], mean = (long long)T * k;
+  const float dir = load < mean ? 1.0f : (load > mean ? -1.0f : 0.0f);
+  sel_bias[e] = sel_bias[e] + gamma * dir;
+}
+
 }  // namespace
+
+hipError_t launch_bias_update(const moe_problem& p, const int32_t* counts_pre, float gamma,
+                              float* sel_bias, hipStream_t s) {
+  hipLaunchKernelGGL(bias_update_kernel, dim3(1), dim3(256), 0, s, counts_pre, p.T, p.k, p.E,
+                     gamma, sel_bias);
+  return hipGetLastError();
+}
 
 hipError_t launch_combine(const moe_problem& p, const float* out_rows, const float* out_rows_b,
                           const int32_t* assign_pos, const float* topk_w, const float* shared_out,

@@ -117,4 +117,7 @@ hipError_t launch_add_rows(const moe_problem& p, float* out_rows, const float* o
 hipError_t launch_balance(const moe_problem& p, const int32_t* counts_pre, const float* prob_sum,
                           float alpha, float* f, float* P, float* L, hipStream_t s);
 
+hipError_t launch_bias_update(const moe_problem& p, const int32_t* counts_pre, float gamma,
+                              float* sel_bias, hipStream_t s);
+
 }  // namespace moe

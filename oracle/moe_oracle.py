@@ -27,6 +27,9 @@ ceil(cf * T*k / E) in IEEE double; overflow dropped first-come in ascending
 flat assignment order a = t*k + j with no gate renormalisation afterwards;
 f_i counted before dropping over T*k assignments; alpha inside L_balance.
 
+bias_update follows the pages' direction rule; its threshold (the mean load)
+and step (a caller parameter) are readings.
+
 Pin status: every function below is pinned by a `-m "not gpu"` test against
 values the pages print, closed forms, library special cases or brute force,
 except the readings themselves (drop order, the Zipf offset, what the
@@ -43,6 +46,7 @@ __all__ = [
     "router_logits", "softmax", "selection_keys", "select_topk", "renormalised_gates",
     "route", "capacity", "align", "silu", "swiglu_expert", "moe_forward",
     "moe_forward_naive", "token_output", "token_outputs", "balance", "expert_table",
+    "bias_update",
 ]
 
 ExpertFn = Callable[[int], Tuple[np.ndarray, np.ndarray, np.ndarray]]
@@ -309,3 +313,26 @@ def balance(counts_pre: np.ndarray, probs: np.ndarray, T: int, k: int, alpha: fl
     P = np.asarray(probs, dtype=np.float64).mean(axis=0)
     L = float(alpha) * E * float(np.sum(f * P))
     return f, P, L
+
+
+# ----------------------------------------------------------------------------- bias update
+def bias_update(counts_pre: np.ndarray, sel_bias: np.ndarray, gamma: float, T: int,
+                k: int) -> np.ndarray:
+    """One step of the auxiliary-loss-free balancing bias.
+
+    [Arch] §2 "Auxiliary-loss-free balancing" and [Handbook] "Load balancing":
+    a per-expert bias that only enters the top-k choice is lowered for an
+    overloaded expert and raised for an idle one, from the observed load.
+    The pages give the direction only. Reading: an expert is overloaded when
+    its assignment count before capacity dropping exceeds the mean load
+    T*k/E and underloaded when it is below it (compared exactly, as
+    E*c_e against T*k); the bias moves by the caller's step gamma, and an
+    expert at exactly the mean keeps its bias. The bias is an fp32 tensor, so
+    the step is taken in fp32: b + gamma * sign(T*k - E*c_e), rounded once.
+    """
+    c = np.asarray(counts_pre, dtype=np.int64)
+    E = c.size
+    direction = np.sign(np.int64(T) * np.int64(k) - np.int64(E) * c)   # +1 under, -1 over
+    b = np.asarray(sel_bias, dtype=np.float32)
+    return (b + np.float32(gamma) * direction.astype(np.float32)).astype(np.float32)
+

@@ -262,3 +262,48 @@ def test_prepared_forward_and_graph_replay():
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(fwd.y, want), f"replay {i}"
+
+
+BIAS_CASES = [(6, 2, 4), (4096, 8, 256), (1, 1, 1), (0, 2, 8), (333, 3, 24), (16384, 2, 64)]
+
+
+@pytest.mark.parametrize("T,k,E", BIAS_CASES, ids=[f"T{t}k{k}E{e}" for t, k, e in BIAS_CASES])
+def test_bias_update_bit_exact(T, k, E):
+    """moe_bias_update against the oracle's fp32 step, on counts that hit the mean, zero and
+    large values; bit for bit."""
+    import mixture_experts_layer_44_amd as moe
+    rng = np.random.default_rng(T * 131 + E)
+    p = moe.make_problem(T, 256, E, k, 256)
+    mean = T * k / E
+    counts = rng.integers(0, max(1, int(3 * mean) + 2), E).astype(np.int32)
+    if E >= 4 and (T * k) % E == 0:
+        counts[:2] = T * k // E          # exactly at the mean: unchanged
+        counts[2] = 0
+    bias = rng.uniform(-0.1, 0.1, E).astype(np.float32)
+    for gamma in (0.001, 0.03125, 0.0):
+        want = O.bias_update(counts, bias, gamma, T, k)
+        got = moe.bias_update(p, torch.from_numpy(counts).cuda(), torch.from_numpy(bias).cuda(),
+                              gamma).cpu().numpy()
+        np.testing.assert_array_equal(got.view(np.uint32), want.view(np.uint32))
+
+
+def test_bias_update_loop_balances_routing():
+    """Routing on the GPU with the selection bias, then moe_bias_update from the GPU's own
+    pre-drop counts, repeated: every step equals the oracle's step on the same counts (bit for
+    bit) and the load of a skewed router evens out."""
+    import mixture_experts_layer_44_amd as moe
+    w = W("bias_loop", T=1024, d=256, E=32, k=4, d_ff=256, seed=301, zipf_s=1.1, sel_bias=True)
+    inp = {k_: (None if v is None else v.cuda()) for k_, v in workloads.generate(w).items()}
+    p = moe.problem_for(w)
+    bias = torch.zeros(w.E, dtype=torch.float32, device="cuda")
+    ratios = []
+    for it in range(120):          # step 0.05: the log-Zipf offset spans ~3.8 logits
+        _, r = moe.forward(p, inp["x"], inp["w_gate"], inp["w1"], inp["w3"], inp["w2"],
+                           logit_bias=inp["logit_bias"], sel_bias=bias, return_routing=True)
+        counts = r["counts_pre"].cpu().numpy()
+        ratios.append(counts.max() / (w.T * w.k / w.E))
+        want = O.bias_update(counts, bias.cpu().numpy(), 0.05, w.T, w.k)
+        moe.bias_update(p, r["counts_pre"], bias, 0.05)
+        np.testing.assert_array_equal(bias.cpu().numpy().view(np.uint32), want.view(np.uint32))
+    _say(f"[bias loop] max/mean load {ratios[0]:.2f} -> {ratios[-1]:.2f}")
+    assert ratios[0] > 2.0 and ratios[-1] < 1.5, (ratios[0], ratios[-1])

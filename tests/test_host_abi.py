@@ -36,7 +36,7 @@ def test_header_declares_the_entry_points():
     d = _declared()
     for n in ("moe_route", "moe_align", "moe_expert_ffn", "moe_combine", "moe_balance",
               "moe_forward", "moe_workspace_bytes", "moe_validate", "moe_capacity",
-              "moe_status_str"):
+              "moe_status_str", "moe_bias_update"):
         assert n in d
 
 
@@ -135,6 +135,10 @@ def test_invalid_calls_return_before_any_launch(moe):
     assert lib.moe_forward(ctypes.byref(pu), *([null] * 20), 0, null) == moe.MOE_EUNSUPPORTED
     assert lib.moe_balance(ctypes.byref(p), fake, fake, ctypes.c_float(float("nan")), fake, fake,
                            fake, null) == moe.MOE_EINVAL
+    # bias step: negative or non-finite step, or a missing pointer -> EINVAL
+    for g in (-0.5, float("nan"), float("inf")):
+        assert lib.moe_bias_update(ctypes.byref(p), fake, ctypes.c_float(g), fake, null) == moe.MOE_EINVAL
+    assert lib.moe_bias_update(ctypes.byref(p), null, ctypes.c_float(0.1), fake, null) == moe.MOE_EINVAL
     # null problem
     assert lib.moe_validate(None) == moe.MOE_EINVAL
 

@@ -356,12 +356,53 @@ def pin_token_outputs_equal_grouped():
         np.testing.assert_allclose(yt, y[t], rtol=1e-13, atol=1e-15)
 
 
+def pin_bias_update_direction():
+    """[Arch] §2 / [Handbook] "Load balancing": an overloaded expert's bias goes down, an idle or
+    underloaded one's goes up; at exactly the mean load (T*k/E) it stays. Hand-computed case:
+    T=6, k=2, E=4 -> mean 3."""
+    counts = np.array([0, 3, 5, 4])
+    b = np.array([0.5, -0.25, 0.0, 1.0], dtype=np.float32)
+    out = O.bias_update(counts, b, 0.125, T=6, k=2)
+    assert out.dtype == np.float32
+    np.testing.assert_array_equal(out, np.array([0.625, -0.25, -0.125, 0.875], dtype=np.float32))
+    # a mean that is not an integer (T*k/E = 2.5): 2 is under, 3 is over
+    out = O.bias_update(np.array([2, 3, 2, 3]), np.zeros(4, np.float32), 1.0, T=5, k=2)
+    np.testing.assert_array_equal(out, np.array([1, -1, 1, -1], dtype=np.float32))
+
+
+def pin_bias_update_balances():
+    """The pages' purpose of the bias: repeated updates from the observed load even out a
+    router that strongly prefers some experts. Routing here is the oracle's own top-k on
+    logits + bias (the bias only selects); a log-Zipf logit offset makes the router skewed."""
+    rng = np.random.default_rng(7)
+    T, d, E, k = 2048, 16, 16, 2
+    x = rng.normal(size=(T, d))
+    w = rng.normal(scale=0.3, size=(E, d))
+    offset = -1.1 * np.log(np.arange(E) + 1.0)
+    bias = np.zeros(E, dtype=np.float32)
+
+    def imbalance(b):
+        logits = O.router_logits(x, w, offset)
+        ids = O.select_topk(O.selection_keys(logits, b.astype(np.float64)), k)
+        counts = np.bincount(ids.reshape(-1), minlength=E)
+        return counts, counts.max() / (T * k / E)
+
+    counts, start = imbalance(bias)
+    for _ in range(300):
+        bias = O.bias_update(counts, bias, 0.02, T, k)
+        counts, _ = imbalance(bias)
+    _, end = imbalance(bias)
+    assert start > 3.0, start
+    assert end < 1.35, end
+
+
 PINS = [pin_token_outputs_equal_grouped, pin_gates_worked_example, pin_gates_flowchart, pin_topk_brute_force, pin_zero_input,
         pin_gates_sum_to_one, pin_softmax_library, pin_selection_bias_only_selects,
         pin_logit_bias_enters_softmax, pin_dense_swiglu_E1, pin_k_equals_E,
         pin_naive_equals_grouped_handbook, pin_naive_equals_grouped_capacity,
         pin_align_brute_force, pin_align_invariants, pin_capacity_values, pin_silu,
-        pin_balance_uniform, pin_balance_handbook, pin_sum_sq, pin_equivariance_and_scaling]
+        pin_balance_uniform, pin_balance_handbook, pin_sum_sq, pin_equivariance_and_scaling,
+        pin_bias_update_direction, pin_bias_update_balances]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -426,8 +467,13 @@ def _mut_softmax_no_shift(logits):
     return e / e.sum(axis=1, keepdims=True)
 
 
+def _mut_bias_sign_flipped(counts_pre, sel_bias, gamma, T, k):
+    return _orig_bias_update(counts_pre, sel_bias, -gamma, T, k)
+
+
 _orig_align = O.align
 _orig_balance = O.balance
+_orig_bias_update = O.bias_update
 
 MUTATIONS = {
     "gates_not_renormalised": ("renormalised_gates", _mut_no_renorm),
@@ -440,6 +486,7 @@ MUTATIONS = {
     "alpha_missing": ("balance", _mut_no_alpha),
     "f_over_tokens_not_assignments": ("balance", _mut_f_over_T),
     "softmax_without_shift": ("softmax", _mut_softmax_no_shift),
+    "bias_update_sign_flipped": ("bias_update", _mut_bias_sign_flipped),
 }
 
 

@@ -46,7 +46,7 @@ __all__ = [
     "router_logits", "softmax", "selection_keys", "select_topk", "renormalised_gates",
     "route", "capacity", "align", "silu", "swiglu_expert", "moe_forward",
     "moe_forward_naive", "token_output", "token_outputs", "balance", "expert_table",
-    "bias_update",
+    "bias_update", "expert_choice_capacity", "expert_choice_route", "moe_forward_expert_choice",
 ]
 
 ExpertFn = Callable[[int], Tuple[np.ndarray, np.ndarray, np.ndarray]]
@@ -335,4 +335,62 @@ def bias_update(counts_pre: np.ndarray, sel_bias: np.ndarray, gamma: float, T: i
     direction = np.sign(np.int64(T) * np.int64(k) - np.int64(E) * c)   # +1 under, -1 over
     b = np.asarray(sel_bias, dtype=np.float32)
     return (b + np.float32(gamma) * direction.astype(np.float32)).astype(np.float32)
+
+
+# ----------------------------------------------------------------------------- expert choice
+def expert_choice_capacity(capacity_factor: float, T: int, k: int, E: int) -> int:
+    """Bucket size C of expert-choice routing.
+
+    [Concept] "Expert Choice -- Reverse Who Selects Whom": experts choose the
+    tokens, with fixed bucket sizes. Reading: the bucket is the capacity of
+    the token-choice layer, ceil(cf * T*k / E) (k = the average number of
+    experts per token), with cf = 1 when no factor is given, and at most T."""
+    cf = 1.0 if capacity_factor is None or capacity_factor <= 0 else float(capacity_factor)
+    return min(T, int(math.ceil(cf * float(T * k) / float(E))))
+
+
+def expert_choice_route(x, w_gate, E: int, C: int, logit_bias=None):
+    """Each expert picks its C tokens ([Concept] "Expert Choice").
+
+    Scores: the router probabilities p = softmax over experts of the logits
+    (the same gate as token choice, [Arch] §2 "Gating Function"). Expert e
+    takes the C tokens with the largest p[t, e], equal scores going to the
+    lower token index; its bucket lists them in ascending token order. The
+    weight of (t, e) is p[t, e] itself: a token may get any number of experts
+    (0 to E) and nothing is renormalised over them. Returns
+    (tokens [E, C], gates [E, C], probs [T, E])."""
+    logits = router_logits(x, w_gate, logit_bias)
+    probs = softmax(logits)
+    T = probs.shape[0]
+    tokens = np.zeros((E, C), dtype=np.int64)
+    gates = np.zeros((E, C), dtype=np.float64)
+    for e in range(E):
+        best = np.argsort(-probs[:, e], kind="stable")[:C]    # stable: ties -> lower t
+        tok = np.sort(best)
+        tokens[e] = tok
+        gates[e] = probs[tok, e]
+    return tokens, gates, probs
+
+
+def moe_forward_expert_choice(x, w_gate, experts: ExpertFn, E: int, C: int, logit_bias=None,
+                              shared: Sequence = (), tokens=None):
+    """y[t] = sum over experts e whose bucket holds t of p[t,e] * Expert_e(x[t]),
+    plus the shared experts, added in expert order. With `tokens` given, the
+    buckets are those ([E, C]) and the weights the oracle's own p.
+    Returns (y [T,d], info dict with tokens, gates, probs)."""
+    x = np.asarray(x, dtype=np.float64)
+    T, d = x.shape
+    r_tok, gates, probs = expert_choice_route(x, w_gate, E, C, logit_bias)
+    if tokens is not None:
+        r_tok = np.asarray(tokens, dtype=np.int64)
+        gates = np.take_along_axis(probs.T, r_tok, axis=1)
+    y = np.zeros((T, d), dtype=np.float64)
+    for e in range(E):
+        if C == 0:
+            break
+        tok = r_tok[e]
+        out = swiglu_expert(x[tok], *experts(e))
+        np.add.at(y, tok, gates[e][:, None] * out)
+    y += _shared_sum(x, shared)
+    return y, dict(tokens=r_tok, gates=gates, probs=probs)
 

@@ -396,13 +396,81 @@ def pin_bias_update_balances():
     assert end < 1.35, end
 
 
+def pin_expert_choice_all_tokens_is_softmax_mixture():
+    """With C = T every expert takes every token: y = sum_e p[t,e] Expert_e(x_t), which is also
+    the token-choice layer with k = E (its renormalised gates are p itself)."""
+    rng = np.random.default_rng(41)
+    T, d, E, d_ff = 9, 6, 4, 5
+    x = rng.normal(size=(T, d))
+    w_gate = rng.normal(size=(E, d))
+    w1, w3, w2 = _experts(rng, E, d, d_ff)
+    ex = O.expert_table(w1, w3, w2)
+    y_ec, info = O.moe_forward_expert_choice(x, w_gate, ex, E, T)
+    y_tc, _ = O.moe_forward(x, w_gate, ex, E, E)
+    np.testing.assert_allclose(y_ec, y_tc, rtol=1e-12, atol=1e-14)
+    assert (info["tokens"] == np.arange(T)[None, :]).all()
+
+
+def pin_expert_choice_brute_force():
+    """Buckets against a plain sort key (-p, t) per expert, with exact ties (repeated tokens),
+    and y against a direct per-token sum over the experts that chose the token."""
+    rng = np.random.default_rng(42)
+    T, d, E, d_ff, C = 8, 5, 3, 4, 3
+    x = rng.normal(size=(T, d))
+    x[5] = x[1]                                    # tokens 1 and 5 tie for every expert
+    x[7] = x[2]
+    w_gate = rng.normal(size=(E, d))
+    w1, w3, w2 = _experts(rng, E, d, d_ff)
+    ex = O.expert_table(w1, w3, w2)
+    y, info = O.moe_forward_expert_choice(x, w_gate, ex, E, C)
+    p = info["probs"]
+    for e in range(E):
+        want = sorted(sorted(range(T), key=lambda t: (-p[t, e], t))[:C])
+        assert list(info["tokens"][e]) == want, (e, list(info["tokens"][e]), want)
+        np.testing.assert_array_equal(info["gates"][e], p[want, e])
+    for t in range(T):
+        acc = np.zeros(d)
+        for e in range(E):
+            if t in info["tokens"][e]:
+                acc += p[t, e] * O.swiglu_expert(x[t:t + 1], w1[e], w3[e], w2[e])[0]
+        np.testing.assert_allclose(y[t], acc, rtol=1e-12, atol=1e-14)
+    # fixed buckets: E*C slots, variable experts per token
+    per_token = np.bincount(info["tokens"].reshape(-1), minlength=T)
+    assert per_token.sum() == E * C
+
+
+def pin_expert_choice_single_expert():
+    """E = 1: p = 1 for every token, so the bucket is the first C tokens (ties -> lower t) and
+    only they get the expert's output."""
+    rng = np.random.default_rng(43)
+    T, d, d_ff, C = 6, 4, 3, 4
+    x = rng.normal(size=(T, d))
+    w_gate = rng.normal(size=(1, d))
+    w1, w3, w2 = _experts(rng, 1, d, d_ff)
+    y, info = O.moe_forward_expert_choice(x, w_gate, O.expert_table(w1, w3, w2), 1, C)
+    assert list(info["tokens"][0]) == [0, 1, 2, 3]
+    np.testing.assert_allclose(y[:C], O.swiglu_expert(x[:C], w1[0], w3[0], w2[0]), rtol=1e-13)
+    assert (y[C:] == 0).all()
+
+
+def pin_expert_choice_capacity():
+    """Bucket size: the token-choice capacity ceil(cf*T*k/E), cf = 1 when unset, at most T."""
+    assert O.expert_choice_capacity(0.0, 4096, 2, 8) == 1024
+    assert O.expert_choice_capacity(1.25, 16384, 2, 64) == 640
+    assert O.expert_choice_capacity(0.0, 300, 3, 7) == 129          # ceil(900 / 7)
+    assert O.expert_choice_capacity(0.0, 10, 8, 2) == 10            # 40 capped at T
+    assert O.expert_choice_capacity(0.0, 0, 2, 8) == 0
+
+
 PINS = [pin_token_outputs_equal_grouped, pin_gates_worked_example, pin_gates_flowchart, pin_topk_brute_force, pin_zero_input,
         pin_gates_sum_to_one, pin_softmax_library, pin_selection_bias_only_selects,
         pin_logit_bias_enters_softmax, pin_dense_swiglu_E1, pin_k_equals_E,
         pin_naive_equals_grouped_handbook, pin_naive_equals_grouped_capacity,
         pin_align_brute_force, pin_align_invariants, pin_capacity_values, pin_silu,
         pin_balance_uniform, pin_balance_handbook, pin_sum_sq, pin_equivariance_and_scaling,
-        pin_bias_update_direction, pin_bias_update_balances]
+        pin_bias_update_direction, pin_bias_update_balances,
+        pin_expert_choice_all_tokens_is_softmax_mixture, pin_expert_choice_brute_force,
+        pin_expert_choice_single_expert, pin_expert_choice_capacity]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -471,9 +539,44 @@ def _mut_bias_sign_flipped(counts_pre, sel_bias, gamma, T, k):
     return _orig_bias_update(counts_pre, sel_bias, -gamma, T, k)
 
 
+def _mut_ec_smallest(x, w_gate, E, C, logit_bias=None):
+    tok, gates, probs = _orig_ec_route(x, w_gate, E, C, logit_bias)
+    for e in range(E):
+        t = np.sort(np.argsort(probs[:, e], kind="stable")[:C])
+        tok[e], gates[e] = t, probs[t, e]
+    return tok, gates, probs
+
+
+def _mut_ec_ties_high(x, w_gate, E, C, logit_bias=None):
+    tok, gates, probs = _orig_ec_route(x, w_gate, E, C, logit_bias)
+    T = probs.shape[0]
+    for e in range(E):
+        rev = np.argsort(-probs[::-1, e], kind="stable")[:C]
+        t = np.sort(T - 1 - rev)
+        tok[e], gates[e] = t, probs[t, e]
+    return tok, gates, probs
+
+
+def _mut_ec_renormalised(x, w_gate, experts, E, C, logit_bias=None, shared=(), tokens=None):
+    y, info = _orig_ec_forward(x, w_gate, experts, E, C, logit_bias, shared, tokens)
+    T = y.shape[0]
+    tot = np.zeros(T)
+    for e in range(E):
+        np.add.at(tot, info["tokens"][e], info["gates"][e])
+    y2 = np.zeros_like(y)
+    xx = np.asarray(x, dtype=np.float64)
+    for e in range(E):
+        tok = info["tokens"][e]
+        out = O.swiglu_expert(xx[tok], *experts(e))
+        np.add.at(y2, tok, (info["gates"][e] / tot[tok])[:, None] * out)
+    return y2, info
+
+
 _orig_align = O.align
 _orig_balance = O.balance
 _orig_bias_update = O.bias_update
+_orig_ec_route = O.expert_choice_route
+_orig_ec_forward = O.moe_forward_expert_choice
 
 MUTATIONS = {
     "gates_not_renormalised": ("renormalised_gates", _mut_no_renorm),
@@ -487,6 +590,9 @@ MUTATIONS = {
     "f_over_tokens_not_assignments": ("balance", _mut_f_over_T),
     "softmax_without_shift": ("softmax", _mut_softmax_no_shift),
     "bias_update_sign_flipped": ("bias_update", _mut_bias_sign_flipped),
+    "expert_choice_takes_smallest": ("expert_choice_route", _mut_ec_smallest),
+    "expert_choice_ties_to_higher_token": ("expert_choice_route", _mut_ec_ties_high),
+    "expert_choice_gates_renormalised": ("moe_forward_expert_choice", _mut_ec_renormalised),
 }
 
 

@@ -222,6 +222,48 @@ def cpu_baseline(w, inp, sample_tokens: int):
             "seconds": dt}
 
 
+# ----------------------------------------------------------------------------- expert choice
+def bench_expert_choice(args, w, p, g, kw, y, torch, moe):
+    """Times exactly K moe_forward_expert_choice calls; the algorithmic work counts the E*C
+    bucket rows. The per-kernel times come from rocprofv3 (profiles/), not from stage events."""
+    C = moe.expert_choice_capacity(p)
+    ws = torch.empty(max(moe.expert_choice_workspace_bytes(p), 1), dtype=torch.uint8,
+                     device=y.device)
+
+    def step():
+        moe.forward_expert_choice(p, g["x"], g["w_gate"], g["w1"], g["w3"], g["w2"],
+                                  logit_bias=kw["logit_bias"], ws1=kw["ws1"], ws3=kw["ws3"],
+                                  ws2=kw["ws2"], ws=ws, y=y)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    assert torch.isfinite(y).all().item()
+    ms_per_step = elapsed * 1e3 / args.steps
+    lw = algorithmic_work(w, [C] * w.E)
+    t_layer = ms_per_step * 1e-3
+    log(f"[bench] expert choice C={C}: {ms_per_step:.4f} ms/step, {w.T / (elapsed / args.steps):,.0f} tokens/s")
+    cfg = {"workload": w.name, "routing": "expert_choice", "C": C, "T": w.T, "d": w.d, "E": w.E,
+           "k": w.k, "d_ff": w.d_ff, "n_shared": w.n_shared, "capacity_factor": w.capacity_factor,
+           "seed": w.seed}
+    line = {"metric": METRIC, "value": w.T * args.steps / elapsed, "unit": "tokens/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "bf16" if w.dtype == "bf16" else "f32", "data": "synthetic", "config": cfg,
+            "roofline": None, "cpu_baseline": None,
+            "layer": {"flops": lw["flops"], "bytes": lw["bytes"], "bucket_rows": w.E * C,
+                      "mfma_frac": lw["flops"] / t_layer / (PEAK_BF16_TFLOPS * 1e12),
+                      "hbm_frac": lw["bytes"] / t_layer / (PEAK_HBM_GBS * 1e9)},
+            "launch": "eager"}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 # ----------------------------------------------------------------------------- main
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
@@ -232,6 +274,9 @@ def main(argv=None):
     ap.add_argument("--cpu-sample", type=int, default=2048,
                     help="tokens of the workload the CPU oracle baseline runs on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--routing", choices=("token_choice", "expert_choice"), default="token_choice",
+                    help="expert_choice: every expert takes its C highest-probability tokens "
+                         "(moe_forward_expert_choice); reported without a per-stage roofline")
     ap.add_argument("--graph", action="store_true",
                     help="replay the forward as one captured HIP graph per step (host launch "
                          "work out of the timed region)")
@@ -273,6 +318,9 @@ def main(argv=None):
     g = inp
     kw = dict(logit_bias=g["logit_bias"], sel_bias=g["sel_bias"], ws1=g["ws1"], ws3=g["ws3"],
               ws2=g["ws2"], ws=ws)
+
+    if args.routing == "expert_choice":
+        return bench_expert_choice(args, w, p, g, kw, y, torch, moe)
 
     # routing of this batch (for the algorithmic work); identical in every step
     _, r = moe.forward(p, g["x"], g["w_gate"], g["w1"], g["w3"], g["w2"], return_routing=True, y=y,

@@ -163,6 +163,34 @@ moe_status moe_balance(const moe_problem* p, const int32_t* counts_pre, const fl
 moe_status moe_bias_update(const moe_problem* p, const int32_t* counts_pre, float gamma,
                            float* sel_bias, hipStream_t stream);
 
+/* Expert-choice routing ("One Deep Concept #04", "Expert Choice -- Reverse Who Selects
+   Whom": the experts choose the tokens, with fixed bucket sizes, so a token may get any
+   number of experts). Scores are the router probabilities p = softmax over experts of
+   x * w_gate^T (+ logit_bias) ("MoE Architecture" §2 "Gating Function"). Expert e takes
+   the C tokens with the largest p[t,e], equal scores going to the lower token, and
+   y[t] = shared(x[t]) + sum over the experts e that took t, in expert order, of
+   p[t,e] * Expert_e(x[t]); nothing is renormalised.
+   Bucket size: C = ceil(cf * T*k / E) evaluated in double (cf = capacity_factor, or 1
+   when it is <= 0), at most T; k is the mean number of experts per token. */
+moe_status moe_expert_choice_capacity(const moe_problem* p, int32_t* c_out);
+
+/* Workspace bytes of moe_forward_expert_choice (host-only). */
+moe_status moe_expert_choice_workspace_bytes(const moe_problem* p, size_t* bytes_out);
+
+/* The expert-choice layer.
+     x, w_gate, logit_bias, w1/w3/w2, ws1/ws3/ws2: as for moe_forward (no selection bias);
+     y [T,d] fp32 out;
+     tokens_out [E*C] int32 out or NULL: expert e's bucket at e*C, ascending token ids;
+     gates_out [E*C] fp32 out or NULL: p[t,e] of each bucket slot;
+     prob_sum [E] fp32 out or NULL: sum over tokens of p[t,e];
+     ws: moe_expert_choice_workspace_bytes bytes. Errors as moe_forward. */
+moe_status moe_forward_expert_choice(const moe_problem* p, const void* x, const void* w_gate,
+                                     const float* logit_bias, const void* w1, const void* w3,
+                                     const void* w2, const void* ws1, const void* ws3,
+                                     const void* ws2, float* y, int32_t* tokens_out,
+                                     float* gates_out, float* prob_sum, void* ws,
+                                     size_t ws_bytes, hipStream_t stream);
+
 /* The whole layer in one call: route -> align -> expert FFNs -> combine.
    y [T,d] fp32 out (required). Every routing output pointer may be NULL, in
    which case it lives in ws; when given, it receives the same values the

@@ -22,7 +22,8 @@ __all__ = [
     "Problem", "MoEError", "lib", "make_problem", "validate", "capacity", "workspace_bytes",
     "route", "align", "expert_ffn", "combine", "balance", "forward", "LIB_PATH",
     "MOE_OK", "MOE_EINVAL", "MOE_EUNSUPPORTED", "MOE_EWORKSPACE", "MOE_EHIP", "forward_staged",
-    "STAGES", "problem_for", "PreparedForward", "bias_update",
+    "STAGES", "problem_for", "PreparedForward", "bias_update", "expert_choice_capacity",
+    "expert_choice_workspace_bytes", "forward_expert_choice",
 ]
 
 # stage names of moe_forward_staged, in event order (events 1..6 close these stages)
@@ -67,12 +68,17 @@ def _load() -> ctypes.CDLL:
     L.moe_combine.argtypes = [P, vp, vp, vp, vp, vp, vp]
     L.moe_balance.argtypes = [P, vp, vp, f32, vp, vp, vp, vp]
     L.moe_bias_update.argtypes = [P, vp, f32, vp, vp]
+    L.moe_expert_choice_capacity.argtypes = [P, ctypes.POINTER(i32)]
+    L.moe_expert_choice_workspace_bytes.argtypes = [P, ctypes.POINTER(sz)]
+    L.moe_forward_expert_choice.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                            vp, sz, vp]
     L.moe_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                               vp, vp, vp, vp, sz, vp]
     L.moe_forward_staged.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
     for fn in ("moe_validate", "moe_capacity", "moe_workspace_bytes", "moe_route", "moe_align",
                "moe_expert_ffn", "moe_combine", "moe_balance", "moe_forward", "moe_forward_staged",
-               "moe_bias_update"):
+               "moe_bias_update", "moe_expert_choice_capacity", "moe_expert_choice_workspace_bytes",
+               "moe_forward_expert_choice"):
         getattr(L, fn).restype = ctypes.c_int
     return L
 
@@ -302,6 +308,59 @@ def bias_update(p: Problem, counts_pre, sel_bias, gamma: float):
     _check("moe_bias_update", _lib.moe_bias_update(ctypes.byref(p), _ptr(counts_pre),
                                                    float(gamma), _ptr(sel_bias), _stream(dev)))
     return sel_bias
+
+
+def expert_choice_capacity(p: Problem) -> int:
+    """Bucket size C of expert-choice routing (host-only)."""
+    c = ctypes.c_int32(0)
+    _check("moe_expert_choice_capacity", _lib.moe_expert_choice_capacity(ctypes.byref(p),
+                                                                          ctypes.byref(c)))
+    return c.value
+
+
+def expert_choice_workspace_bytes(p: Problem) -> int:
+    n = ctypes.c_size_t(0)
+    _check("moe_expert_choice_workspace_bytes",
+           _lib.moe_expert_choice_workspace_bytes(ctypes.byref(p), ctypes.byref(n)))
+    return n.value
+
+
+def forward_expert_choice(p: Problem, x, w_gate, w1, w3, w2, logit_bias=None, ws1=None, ws3=None,
+                          ws2=None, return_routing: bool = False, ws=None, y=None):
+    """The expert-choice layer. -> y [T,d] fp32, or (y, dict(tokens [E,C], gates [E,C],
+    prob_sum [E])) with return_routing."""
+    dev, dt = x.device, _dt(p)
+    _need(x, "x", (p.T, p.d), dt, dev)
+    _need(w_gate, "w_gate", (p.E, p.d), dt, dev)
+    _need(w1, "w1", (p.E, p.d_ff, p.d), dt, dev)
+    _need(w3, "w3", (p.E, p.d_ff, p.d), dt, dev)
+    _need(w2, "w2", (p.E, p.d, p.d_ff), dt, dev)
+    _need(logit_bias, "logit_bias", (p.E,), torch.float32, dev, optional=True)
+    if p.n_shared:
+        _need(ws1, "ws1", (1, p.d_ff_shared, p.d), dt, dev)
+        _need(ws3, "ws3", (1, p.d_ff_shared, p.d), dt, dev)
+        _need(ws2, "ws2", (1, p.d, p.d_ff_shared), dt, dev)
+    if y is None:
+        y = torch.empty((p.T, p.d), dtype=torch.float32, device=dev)
+    else:
+        _need(y, "y", (p.T, p.d), torch.float32, dev)
+    C = expert_choice_capacity(p)
+    need = expert_choice_workspace_bytes(p)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    elif ws.device != dev or ws.dtype != torch.uint8 or ws.numel() < need:
+        raise ValueError(f"workspace must be a uint8 tensor of >= {need} bytes on {dev}")
+    r = {}
+    if return_routing:
+        r = dict(tokens=torch.empty((p.E, max(C, 0)), dtype=torch.int32, device=dev),
+                 gates=torch.empty((p.E, max(C, 0)), dtype=torch.float32, device=dev),
+                 prob_sum=torch.empty(p.E, dtype=torch.float32, device=dev))
+    g = r.get
+    _check("moe_forward_expert_choice", _lib.moe_forward_expert_choice(
+        ctypes.byref(p), _ptr(x), _ptr(w_gate), _ptr(logit_bias), _ptr(w1), _ptr(w3), _ptr(w2),
+        _ptr(ws1), _ptr(ws3), _ptr(ws2), _ptr(y), _ptr(g("tokens")), _ptr(g("gates")),
+        _ptr(g("prob_sum")), _ptr(ws), ws.numel(), _stream(dev)))
+    return (y, r) if return_routing else y
 
 
 class PreparedForward:

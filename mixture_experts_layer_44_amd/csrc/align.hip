@@ -135,11 +135,10 @@ __global__ __launch_bounds__(256) void align_scatter_kernel(
 // Offsets that did not come from align (decreasing, or past T*k) are clamped so that every
 // group stays inside [0, T*k) and the m-tile count inside the list's capacity.
 __global__ __launch_bounds__(256) void schedule_kernel(const int32_t* __restrict__ offsets, int E,
-                                                       int n_shared, int T, int k, int BM,
+                                                       int n_shared, int T, int n, int BM,
                                                        Schedule sc) {
   __shared__ int tmp[256];
-  const int G = E + n_shared;
-  const int n = T * k;
+  const int G = E + n_shared;   // n: rows that the routed segments can span
   // each thread owns groups 2*tid, 2*tid+1 (G <= 257 < 512)
   int rows[2], offs[2], mts[2];
   for (int i = 0; i < 2; ++i) {
@@ -175,9 +174,8 @@ __global__ __launch_bounds__(256) void schedule_kernel(const int32_t* __restrict
 
 }  // namespace
 
-int max_mtiles(int T, int k, int E, int n_shared, int BM) {
-  long long n = (long long)T * k;
-  long long m = (n + BM - 1) / BM + E + (n_shared ? (T + BM - 1) / BM + 1 : 0);
+int max_mtiles(long long n_rows, int T, int E, int n_shared, int BM) {
+  long long m = (n_rows + BM - 1) / BM + E + (n_shared ? (T + BM - 1) / BM + 1 : 0);
   return (int)m;
 }
 
@@ -201,8 +199,9 @@ hipError_t launch_align(const moe_problem& p, int cap, const int32_t* ids, int32
 }
 
 hipError_t launch_schedule(const moe_problem& p, const int32_t* offsets, const Schedule& sc,
-                           hipStream_t s) {
-  hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(256), 0, s, offsets, p.E, p.n_shared, p.T, p.k,
+                           hipStream_t s, long long n_rows) {
+  const int n = (int)(n_rows < 0 ? (long long)p.T * p.k : n_rows);
+  hipLaunchKernelGGL(schedule_kernel, dim3(1), dim3(256), 0, s, offsets, p.E, p.n_shared, p.T, n,
                      sc.BM, sc);
   return hipGetLastError();
 }

@@ -1,6 +1,7 @@
 // C ABI of libmoe_mi355x: argument validation, workspace layout and the stream-ordered
 // launch sequence route -> align -> schedule -> gate-up GEMM -> down GEMM -> combine.
 // Validation never touches the GPU, so invalid calls return before anything is enqueued.
+#include <algorithm>
 #include <climits>
 #include <cmath>
 
@@ -15,11 +16,21 @@ struct Layout {
   size_t logits_part, psum_part, blk_counts, blk_base, grp_rows, grp_off, mt_start, mt_group, h;
   size_t ids, gates, prob_sum, counts_pre, counts, offsets, sorted_assign, assign_pos;
   size_t out_rows, out_rows_b, shared_out;
+  size_t probsT, pos_table;   // expert choice only
   size_t total;
   int max_mt, BM;
 };
 
-Layout layout(const moe_problem& p) {
+// bucket size of expert-choice routing: ceil(cf * T*k / E) (cf = 1 when unset), at most T
+int ec_capacity(const moe_problem& p) {
+  const double cf = p.capacity_factor > 0 ? p.capacity_factor : 1.0;
+  const double c = std::ceil(cf * (double)((long long)p.T * p.k) / (double)p.E);
+  return c >= (double)p.T ? p.T : (int)c;
+}
+
+// Workspace of the token-choice path, or (ec) of the expert-choice path, whose routed rows are
+// the E*C bucket slots.
+Layout layout(const moe_problem& p, bool ec = false) {
   Layout L{};
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -27,12 +38,13 @@ Layout layout(const moe_problem& p) {
     off = align_up(off + (bytes ? bytes : 1), 256);
     return o;
   };
-  const size_t n = (size_t)p.T * p.k;
+  const size_t n = ec ? std::max((size_t)p.T * p.k, (size_t)p.E * ec_capacity(p))
+                      : (size_t)p.T * p.k;
   const int G = p.E + p.n_shared;
-  const int nblk_route = route_topk_blocks(p);
+  const int nblk_route = ec ? std::max(route_topk_blocks(p), ec_probs_blocks(p)) : route_topk_blocks(p);
   const int nblk_align = ceil_div((int)n, kAlignChunk);
   L.BM = gemm_bm(p);
-  L.max_mt = max_mtiles(p.T, p.k, p.E, p.n_shared, L.BM);
+  L.max_mt = max_mtiles((long long)n, p.T, p.E, p.n_shared, L.BM);
   const size_t esz = p.dtype == MOE_BF16 ? 2 : 4;
   L.logits_part = take(route_partial_bytes(p));
   L.psum_part = take((size_t)nblk_route * p.E * 4);
@@ -54,6 +66,8 @@ Layout layout(const moe_problem& p) {
   L.out_rows = take(n * p.d * 4);
   L.out_rows_b = take(down_ksplit(p) == 2 ? n * p.d * 4 : 0);
   L.shared_out = take((size_t)p.n_shared * p.T * p.d * 4);
+  L.probsT = ec ? take((size_t)p.E * p.T * 4) : 0;
+  L.pos_table = ec ? take((size_t)p.T * p.E * 4) : 0;
   L.total = off;
   return L;
 }
@@ -83,8 +97,8 @@ int kernel_cap(const moe_problem& p) {
   return c >= (double)n ? (int)n : (int)c;
 }
 
-moe_status check_ws(const moe_problem& p, const void* ws, size_t ws_bytes) {
-  const size_t need = layout(p).total;
+moe_status check_ws(const moe_problem& p, const void* ws, size_t ws_bytes, bool ec = false) {
+  const size_t need = layout(p, ec).total;
   if (ws_bytes < need) return MOE_EWORKSPACE;
   if (!ws) return MOE_EINVAL;
   return MOE_OK;
@@ -143,6 +157,62 @@ MOE_API moe_status moe_workspace_bytes(const moe_problem* p, size_t* bytes_out) 
   if (!bytes_out) return MOE_EINVAL;
   *bytes_out = layout(*p).total;
   return MOE_OK;
+}
+
+MOE_API moe_status moe_expert_choice_capacity(const moe_problem* p, int32_t* c_out) {
+  moe_status st = moe_validate(p);
+  if (st != MOE_OK) return st;
+  if (!c_out) return MOE_EINVAL;
+  *c_out = ec_capacity(*p);
+  return MOE_OK;
+}
+
+MOE_API moe_status moe_expert_choice_workspace_bytes(const moe_problem* p, size_t* bytes_out) {
+  moe_status st = moe_validate(p);
+  if (st != MOE_OK) return st;
+  if (!bytes_out) return MOE_EINVAL;
+  *bytes_out = layout(*p, true).total;
+  return MOE_OK;
+}
+
+MOE_API moe_status moe_forward_expert_choice(const moe_problem* p, const void* x,
+                                             const void* w_gate, const float* logit_bias,
+                                             const void* w1, const void* w3, const void* w2,
+                                             const void* ws1, const void* ws3, const void* ws2,
+                                             float* y, int32_t* tokens_out, float* gates_out,
+                                             float* prob_sum, void* ws, size_t ws_bytes,
+                                             hipStream_t stream) {
+  moe_status st = moe_validate(p);
+  if (st != MOE_OK) return st;
+  const bool hasT = p->T > 0;
+  if (!w_gate || !w1 || !w3 || !w2 || (hasT && (!x || !y))) return MOE_EINVAL;
+  if (p->n_shared && (!ws1 || !ws3 || !ws2)) return MOE_EINVAL;
+  if ((st = check_ws(*p, ws, ws_bytes, true)) != MOE_OK) return st;
+  const Layout L = layout(*p, true);
+  const int C = ec_capacity(*p);
+  int32_t* tokens = tokens_out ? tokens_out : at<int32_t>(ws, L.sorted_assign);
+  float* gates = gates_out ? gates_out : at<float>(ws, L.gates);
+  int32_t* offs = at<int32_t>(ws, L.offsets);
+  float* out_rows = at<float>(ws, L.out_rows);
+  float* out_b = down_ksplit(*p) == 2 ? at<float>(ws, L.out_rows_b) : nullptr;
+  float* shared_out = p->n_shared ? at<float>(ws, L.shared_out) : nullptr;
+  float* probsT = at<float>(ws, L.probsT);
+  int32_t* pos = at<int32_t>(ws, L.pos_table);
+  float* psum_part = at<float>(ws, L.psum_part);
+  const Schedule sc = schedule_in(*p, L, ws);
+  hipError_t e = launch_route_logits(*p, x, w_gate, at<float>(ws, L.logits_part), stream);
+  if (e == hipSuccess)
+    e = launch_ec_probs(*p, at<float>(ws, L.logits_part), logit_bias, probsT,
+                        prob_sum ? psum_part : nullptr, stream);
+  if (e == hipSuccess && prob_sum)
+    e = launch_psum_reduce(psum_part, hasT ? ec_probs_blocks(*p) : 0, p->E, prob_sum, stream);
+  if (e == hipSuccess) e = launch_ec_select(*p, C, probsT, tokens, gates, pos, offs, stream);
+  if (e == hipSuccess) e = launch_schedule(*p, offs, sc, stream, (long long)p->E * C);
+  if (e == hipSuccess)
+    e = launch_expert_ffn(*p, x, w1, w3, w2, ws1, ws3, ws2, tokens, sc, at<void>(ws, L.h), out_rows,
+                          out_b, shared_out, stream, nullptr, 1);
+  if (e == hipSuccess) e = launch_ec_combine(*p, pos, gates, out_rows, out_b, shared_out, y, stream);
+  return hip_status(e);
 }
 
 MOE_API moe_status moe_route(const moe_problem* p, const void* x, const void* w_gate,

@@ -653,7 +653,8 @@ hipError_t launch_expert_ffn(const moe_problem& p, const void* x, const void* w1
                              const void* w2, const void* ws1, const void* ws3, const void* ws2,
                              const int32_t* sorted_assign, const Schedule& sc, void* h,
                              float* out_rows, float* out_rows_b, float* shared_out, hipStream_t s,
-                             hipEvent_t between) {
+                             hipEvent_t between, int row_div) {
+  const int kdiv = row_div > 0 ? row_div : p.k;
   if (p.dtype == MOE_BF16) {
     GemmArgs a{};
     a.A = (const bf16_t*)x;
@@ -664,7 +665,7 @@ hipError_t launch_expert_ffn(const moe_problem& p, const void* x, const void* w1
     a.N = p.d_ff;
     a.K = p.d;
     a.E = p.E;
-    a.k = p.k;
+    a.k = kdiv;
     a.T = p.T;
     a.sorted_assign = sorted_assign;
     a.sc = sc;
@@ -676,7 +677,7 @@ hipError_t launch_expert_ffn(const moe_problem& p, const void* x, const void* w1
     b.N = p.d;
     b.K = p.d_ff;
     b.E = p.E;
-    b.k = p.k;
+    b.k = kdiv;
     b.T = p.T;
     b.sorted_assign = sorted_assign;
     b.sc = sc;
@@ -701,7 +702,7 @@ hipError_t launch_expert_ffn(const moe_problem& p, const void* x, const void* w1
   a.N = p.d_ff;
   a.K = p.d;
   a.E = p.E;
-  a.k = p.k;
+  a.k = kdiv;
   a.T = p.T;
   a.sorted_assign = sorted_assign;
   a.sc = sc;
@@ -718,7 +719,7 @@ hipError_t launch_expert_ffn(const moe_problem& p, const void* x, const void* w1
   b.N = p.d;
   b.K = p.d_ff;
   b.E = p.E;
-  b.k = p.k;
+  b.k = kdiv;
   b.T = p.T;
   b.sorted_assign = sorted_assign;
   b.sc = sc;

@@ -49,7 +49,8 @@ struct Schedule {
   int BM;
 };
 
-int max_mtiles(int T, int k, int E, int n_shared, int BM);
+// m-tiles that n_rows routed rows (in E segments) plus the shared expert's T rows can need
+int max_mtiles(long long n_rows, int T, int E, int n_shared, int BM);
 // grouped-GEMM tile shape class from the expected rows per expert: wide (256-row m-tiles),
 // narrow (128) or small (32)
 bool gemm_wide(const moe_problem& p);
@@ -92,18 +93,20 @@ hipError_t launch_align(const moe_problem& p, int cap, const int32_t* ids, int32
                         int32_t* counts, int32_t* offsets, int32_t* sorted_assign,
                         int32_t* assign_pos, int32_t* blk_counts, int32_t* blk_base, hipStream_t s);
 
+// n_rows: rows the routed segments can span (T*k when negative)
 hipError_t launch_schedule(const moe_problem& p, const int32_t* offsets, const Schedule& sc,
-                           hipStream_t s);
+                           hipStream_t s, long long n_rows = -1);
 
 // 2 when the down GEMM runs with its K range split in two (second half -> out_rows_b)
 int down_ksplit(const moe_problem& p);
 
-// out_rows_b: [T*k, d] second-half partial rows, required when down_ksplit(p) == 2
+// out_rows_b: [T*k, d] second-half partial rows, required when down_ksplit(p) == 2.
+// row_div: a routed row r gathers token sorted_assign[r] / row_div (0: k).
 hipError_t launch_expert_ffn(const moe_problem& p, const void* x, const void* w1, const void* w3,
                              const void* w2, const void* ws1, const void* ws3, const void* ws2,
                              const int32_t* sorted_assign, const Schedule& sc, void* h,
                              float* out_rows, float* out_rows_b, float* shared_out, hipStream_t s,
-                             hipEvent_t between = nullptr);
+                             hipEvent_t between = nullptr, int row_div = 0);
 
 // out_rows_b may be null; when given, each expert row is out_rows + out_rows_b
 hipError_t launch_combine(const moe_problem& p, const float* out_rows, const float* out_rows_b,
@@ -116,6 +119,23 @@ hipError_t launch_add_rows(const moe_problem& p, float* out_rows, const float* o
 
 hipError_t launch_balance(const moe_problem& p, const int32_t* counts_pre, const float* prob_sum,
                           float alpha, float* f, float* P, float* L, hipStream_t s);
+
+// prob_sum[e] = sum over the nblk per-workgroup partials, in workgroup order
+hipError_t launch_psum_reduce(const float* psum_part, int nblk, int E, float* prob_sum,
+                              hipStream_t s);
+
+// ---- expert-choice routing (expert_choice.hip)
+int ec_probs_blocks(const moe_problem& p);
+// router probabilities, expert-major probsT [E][T]; per-workgroup sums when psum_part != null
+hipError_t launch_ec_probs(const moe_problem& p, const float* logits_part, const float* logit_bias,
+                           float* probsT, float* psum_part, hipStream_t s);
+// buckets: tokens / gates [E*C] (expert e at e*C, ascending tokens), pos_table [T][E] (row of
+// (t,e) or -1), offsets [E+1] = e*C
+hipError_t launch_ec_select(const moe_problem& p, int C, const float* probsT, int32_t* tokens,
+                            float* gates, int32_t* pos_table, int32_t* offsets, hipStream_t s);
+hipError_t launch_ec_combine(const moe_problem& p, const int32_t* pos_table, const float* gates,
+                             const float* out_rows, const float* out_rows_b,
+                             const float* shared_out, float* y, hipStream_t s);
 
 hipError_t launch_bias_update(const moe_problem& p, const int32_t* counts_pre, float gamma,
                               float* sel_bias, hipStream_t s);

@@ -247,6 +247,12 @@ hipError_t launch_route_logits(const moe_problem& p, const void* x, const void* 
   return hipGetLastError();
 }
 
+hipError_t launch_psum_reduce(const float* psum_part, int nblk, int E, float* prob_sum,
+                              hipStream_t s) {
+  hipLaunchKernelGGL(psum_reduce_kernel, dim3(1), dim3(256), 0, s, psum_part, nblk, E, prob_sum);
+  return hipGetLastError();
+}
+
 hipError_t launch_route(const moe_problem& p, const void* x, const void* w_gate,
                         const float* logit_bias, const float* sel_bias, int32_t* ids,
                         float* gates, float* prob_sum, float* logits_part, float* psum_part,

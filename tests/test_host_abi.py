@@ -148,3 +148,12 @@ def test_package_has_no_cpu_fallback():
     src = open(os.path.join(ROOT, "mixture_experts_layer_44_amd", "__init__.py")).read()
     assert "oracle" not in src.replace("no CPU fallback", "")
     assert "import numpy" not in src
+
+
+def test_expert_choice_capacity_matches_oracle(moe):
+    import oracle
+    for (T, d, E, k, cf) in [(4096, 256, 8, 2, 0.0), (16384, 256, 64, 2, 1.25), (300, 256, 7, 3, 0.0),
+                             (10, 256, 2, 2, 0.0), (0, 256, 8, 2, 0.0), (1, 256, 128, 8, 0.0)]:
+        p = moe.make_problem(T, d, E, k, 256, capacity_factor=cf)
+        assert moe.expert_choice_capacity(p) == oracle.expert_choice_capacity(cf, T, k, E)
+    assert moe.expert_choice_workspace_bytes(moe.make_problem(4096, 256, 8, 2, 256)) > 0

@@ -37,8 +37,10 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)   # flop per byte
 KERNEL_SOURCES = {"gate_up": "gemm.hip", "down": "gemm.hip", "route": "route.hip",
                   "align": "align.hip", "schedule": "align.hip", "combine": "combine.hip"}
-KERNEL_NAMES = {"gate_up": "gemm_bf16_kernel<..., true> (gate-up + SwiGLU)",
-                "down": "gemm_bf16_kernel<..., false> (down projection)"}
+KERNEL_NAMES = {"gate_up": "grouped GEMM gate-up + SwiGLU (gemm_bf16_st_kernel / gemm_bf16_kernel "
+                           "with the gate-up flag set; template by row-tile class)",
+                "down": "grouped GEMM down projection (gemm_bf16_st_kernel / gemm_bf16_kernel "
+                        "with the gate-up flag clear)"}
 COPY_PATTERN = r"copyBuffer"   # the runtime's blit kernel (the calibration copy)
 
 
@@ -271,6 +273,8 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="mixtral_prefill")
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="override the workload's token count T (same shapes and seeds otherwise)")
     ap.add_argument("--cpu-sample", type=int, default=2048,
                     help="tokens of the workload the CPU oracle baseline runs on")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -303,6 +307,8 @@ def main(argv=None):
     import mixture_experts_layer_44_amd as moe
 
     w = workloads.get(args.workload)
+    if args.tokens:
+        w = w.with_tokens(args.tokens)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     log(f"[bench] workload {w}")

@@ -43,7 +43,7 @@ Layout layout(const moe_problem& p, bool ec = false) {
   const int G = p.E + p.n_shared;
   const int nblk_route = ec ? std::max(route_topk_blocks(p), ec_probs_blocks(p)) : route_topk_blocks(p);
   const int nblk_align = ceil_div((int)n, kAlignChunk);
-  L.BM = gemm_bm(p);
+  L.BM = ec ? gemm_bm_exact(p, ec_capacity(p)) : gemm_bm(p);
   L.max_mt = max_mtiles((long long)n, p.T, p.E, p.n_shared, L.BM);
   const size_t esz = p.dtype == MOE_BF16 ? 2 : 4;
   L.logits_part = take(route_partial_bytes(p));

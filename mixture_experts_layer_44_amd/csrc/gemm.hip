@@ -11,21 +11,24 @@
 // down:    out = H W2_g^T (n-tile = BNB features) -> fp32 rows in sorted order (routed) or
 //          token order (shared).
 //
-// One template, tile shapes chosen on the host per problem:
-//   wide   BM=256, BNB=256, BK=64, 2 stages: 8 waves (4x2), each a 64x128 block of 32x32
-//          MFMA tiles (8 accumulators, 128 fp32 per lane). For experts with ~1000 rows each.
-//   narrow BM=128, BNB=256 (gate-up) / 128 (down), BK=32, 6 stages: 8 waves (2x4), each 64
-//          rows. For segments of ~50-700 rows.
-//   small  BM=32, BNB=256 / 128, BK=64, 4 stages: 4 waves (1x4), one 32-row fragment each.
-//          For decode-sized segments: many workgroups stream the touched experts' weights.
+// Tile classes, chosen on the host per problem from the expected rows per expert r:
+//   small   (r <= 48)     gemm_bf16_kernel, BM=32, BNB=256 / 128, BK=64, 4-stage ring, 4 waves
+//                         (1x4): many workgroups stream the touched experts' weights (decode).
+//   ragged  (48 < r < 768) gemm_bf16_st_kernel, BM=128 / 192 (8 waves, 2x4) or 256 (4x2),
+//                         BNB=256, BK=64; B in the deep ring, A in the shallow one; the rows of
+//                         a tile past its segment's end are neither loaded nor multiplied.
+//   wide    (r >= 768)    gemm_bf16_st_kernel, BM=256, BNB=256, 8 waves (4x2), A in the deep
+//                         ring (the weight tiles are shared in L2 by several m-tiles).
+//   d % 256 != 0          gemm_bf16_kernel, BM=128, BNB=256 / 128, BK=64, 3-stage ring.
+// Each wave owns a block of 32x32 MFMA tiles (v_mfma_f32_32x32x16_bf16, fp32 accumulators).
 // Two waves per SIMD: while one waits for its LDS fragments the other issues MFMAs.
 // BNB counts B rows: the gate-up B tile holds the W1 rows and then the W3 rows of the same
 // BNB/2 features, and each wave reads the u and v fragments of the same features, so the
 // SwiGLU epilogue has u and v of an output in the same lane.
 //
-// Main loop: a ring of STAGES LDS buffers, each one K step of BK for all BM + BNB rows,
-// filled by direct global->LDS loads (global_load_lds_dwordx4, 16 bytes per lane, 1 KB per
-// instruction) with no register staging. STAGES-1 steps are in flight while the MFMAs
+// Main loop of gemm_bf16_kernel: a ring of STAGES LDS buffers, each one K step of BK for all
+// BM + BNB rows, filled by direct global->LDS loads (global_load_lds_dwordx4, 16 bytes per
+// lane, 1 KB per instruction) with no register staging. STAGES-1 steps are in flight while the MFMAs
 // consume one; each step is one wait for this wave's loads of the step, one barrier, the
 // loads of step kt+STAGES-1 into the buffer freed by step kt-1, and the MFMAs of step kt.
 // Past the last step the loads repeat the last step into a buffer nobody reads again, so
@@ -33,13 +36,16 @@
 // sits in a swizzled slot (see swz) so 16 consecutive rows at one logical chunk cover all 16
 // 16-byte bank groups of a 256-byte LDS cycle.
 //
-// Rows of an m-tile past the end of its segment are loaded from the segment's first row;
-// their results land only in padding rows of H (gate-up) or are not stored (down).
+// In gemm_bf16_kernel and the wide class, rows of an m-tile past the end of its segment are
+// loaded from the segment's first row; their results land only in padding rows of H (gate-up)
+// or are not stored (down).
 //
 // Work order: tiles are numbered group-major, then n-tile, then m-tile, so neighbouring
 // tiles share a weight tile (B) or a row block (A). Workgroups are dealt round-robin to
 // the 8 XCDs, so workgroup b runs tile (b % 8) * per + b / 8: each XCD walks its own
 // contiguous range and its L2 sees the reuse.
+#include <type_traits>
+
 #include "moe_internal.h"
 
 namespace moe {
@@ -373,12 +379,19 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_st_kernel(GemmArgs arg
     boff[i] = (uint32_t)(tc.n0 + (second ? br - BNB / 2 : br)) * (uint32_t)K + lchunk * 8;
   }
 
+  // Rows of this tile that hold data (the last tile of a segment is ragged). With A as the
+  // shallow operand, A row groups past them are not loaded at all: the step's wait leaves only
+  // the deep B loads of later steps in flight, whatever number of A loads was issued before
+  // them. Their LDS rows keep stale bits, which reach only padding rows of the results.
+  const int rows_here = __builtin_amdgcn_readfirstlane(min(BM, tc.rows - tc.m_local * BM));
   auto issue_a = [&](int kt, int slot) {
     bf16_t* dst = As + slot * ASLOT;
 #pragma unroll
-    for (int i = 0; i < DMA_A; ++i)
+    for (int i = 0; i < DMA_A; ++i) {
+      if (DEEPB && (wave * DMA_A + i) * RPI >= rows_here) continue;   // wave-uniform
       __builtin_amdgcn_global_load_lds((const void*)(args.A + aoff[i] + k0 + kt * BK),
                                        (lds_ptr_t)(dst + (wave * DMA_A + i) * RPI * BK), 16, 0, 0);
+    }
   };
   auto issue_b = [&](int kt, int slot) {
     bf16_t* dst = Bs + slot * BSLOT;
@@ -397,6 +410,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_st_kernel(GemmArgs arg
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
+  // Row fragments are dealt to the waves interleaved: fragment i of wave row wm covers tile
+  // rows (i*WM + wm)*32 .. +32, so the fragments of a ragged tile that hold data are spread
+  // over all wave rows (and SIMDs) rather than piled on the first ones.
   // Fragment reads. Lane l reads row (block base + l%32) at 16-byte chunk 2*ks + l/32. Every
   // fragment block starts at a multiple of 16 rows, so a lane's swizzle key ((row/2) % 8) is the
   // same for all its rows: the address is one per-lane offset per sub-step plus a
@@ -410,7 +426,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_st_kernel(GemmArgs arg
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks) {
     const int ch = ((2 * ks + fkc) ^ sw) << 3;
-    aoffs[ks] = (wm * TM + fr) * BK + ch;
+    aoffs[ks] = (wm * 32 + fr) * BK + ch;
     boffs[ks] = (wn * fw + fr) * BK + ch;
   }
   auto bconst = [](int j) {   // compile-time B row of fragment j relative to the wave's rows
@@ -427,42 +443,58 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_st_kernel(GemmArgs arg
     else issue_a(kt, kt % DS);
   };
   constexpr int DEEP_OPS = DEEPB ? DMA_B : DMA_A;
-  issue_shallow(0);
+  // The K loop for a wave whose first NF row fragments hold data: the others are all padding
+  // rows, so their LDS reads and MFMAs are skipped (NF = 0: the wave only loads and waits).
+  auto k_loop = [&](auto nf_tag) {
+    constexpr int NF = decltype(nf_tag)::value;
+    issue_shallow(0);
 #pragma unroll
-  for (int s = 0; s < DS - 1; ++s) issue_deep(s < KT ? s : KT - 1);
-  for (int kt = 0; kt < KT; ++kt) {
-    __builtin_amdgcn_s_waitcnt(wait_vm(DEEP_OPS));
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    issue_shallow(kt + 1 < KT ? kt + 1 : KT - 1);
-    issue_deep(kt + DS - 1 < KT ? kt + DS - 1 : KT - 1);
-    const bf16_t* a = As + (kt % NA) * ASLOT;
-    const bf16_t* b = Bs + (kt % NB) * BSLOT;
-    __builtin_amdgcn_iglp_opt(1);
-    bf16x8 af[2][FM], bfr[2][FN];
+    for (int s = 0; s < DS - 1; ++s) issue_deep(s < KT ? s : KT - 1);
+    for (int kt = 0; kt < KT; ++kt) {
+      __builtin_amdgcn_s_waitcnt(wait_vm(DEEP_OPS));
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      issue_shallow(kt + 1 < KT ? kt + 1 : KT - 1);
+      issue_deep(kt + DS - 1 < KT ? kt + DS - 1 : KT - 1);
+      if (NF == 0) continue;
+      const bf16_t* a = As + (kt % NA) * ASLOT;
+      const bf16_t* b = Bs + (kt % NB) * BSLOT;
+      __builtin_amdgcn_iglp_opt(1);
+      bf16x8 af[2][FM], bfr[2][FN];
 #pragma unroll
-    for (int i = 0; i < FM; ++i) af[0][i] = *(const bf16x8*)&a[aoffs[0] + i * 32 * BK];
+      for (int i = 0; i < NF; ++i) af[0][i] = *(const bf16x8*)&a[aoffs[0] + i * WM * 32 * BK];
 #pragma unroll
-    for (int j = 0; j < FN; ++j) bfr[0][j] = *(const bf16x8*)&b[boffs[0] + bconst(j) * BK];
+      for (int j = 0; j < FN; ++j) bfr[0][j] = *(const bf16x8*)&b[boffs[0] + bconst(j) * BK];
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      const int cur = ks & 1, nxt = cur ^ 1;
-      if (ks + 1 < NKS) {
+      for (int ks = 0; ks < NKS; ++ks) {
+        const int cur = ks & 1, nxt = cur ^ 1;
+        if (ks + 1 < NKS) {
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
-          af[nxt][i] = *(const bf16x8*)&a[aoffs[ks + 1] + i * 32 * BK];
+          for (int i = 0; i < NF; ++i)
+            af[nxt][i] = *(const bf16x8*)&a[aoffs[ks + 1] + i * WM * 32 * BK];
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-          bfr[nxt][j] = *(const bf16x8*)&b[boffs[ks + 1] + bconst(j) * BK];
+          for (int j = 0; j < FN; ++j)
+            bfr[nxt][j] = *(const bf16x8*)&b[boffs[ks + 1] + bconst(j) * BK];
+        }
+#pragma unroll
+        for (int i = 0; i < NF; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bfr[cur][j],
+                                                                acc[i][j], 0, 0, 0);
       }
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bfr[cur][j], acc[i][j],
-                                                              0, 0, 0);
     }
-  }
+  };
+  // Padding work is skipped only with A as the shallow operand (the ragged classes). The wide
+  // class keeps every tile the same length: a segment's last tile finishing early let the
+  // following tiles start out of step, and the m-tiles that share a weight tile then stopped
+  // meeting in L2 (FETCH_SIZE doubled at unchanged time).
+  static_assert(FM <= 3, "the K-loop dispatch covers up to three row fragments per wave");
+  const int nf = DEEPB ? min(FM, max(0, (rows_here - wm * 32 + WM * 32 - 1) / (WM * 32))) : FM;
+  if (nf >= FM) k_loop(std::integral_constant<int, FM>{});
+  else if (nf == 2) k_loop(std::integral_constant<int, (FM > 2 ? 2 : 0)>{});
+  else if (nf == 1) k_loop(std::integral_constant<int, (FM > 1 ? 1 : 0)>{});
+  else k_loop(std::integral_constant<int, 0>{});
   __builtin_amdgcn_s_waitcnt(wait_vm(0));
 
   // ---- epilogue (same accumulator layout and stores as gemm_bf16_kernel)
@@ -474,11 +506,13 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_st_kernel(GemmArgs arg
       const int col = tc.n0 + wn * (FEAT / WN) + j * 32 + fr;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int lr = wm * TM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        const int lr = (i * WM + wm) * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         if (GATEUP) {
-          const float u = acc[i][j][r];
-          const float v = acc[i][j + FN / 2][r];
-          args.H[(size_t)(tc.mt_global * BM + lr) * N + col] = f32_to_bf16(silu_f(u) * v);
+          if (lr < rows_here) {          // padding rows of H feed only padding rows of the down
+            const float u = acc[i][j][r];
+            const float v = acc[i][j + FN / 2][r];
+            args.H[(size_t)(tc.mt_global * BM + lr) * N + col] = f32_to_bf16(silu_f(u) * v);
+          }
         } else {
           const int rg = tc.m_local * BM + lr;
           if (rg < tc.rows) {
@@ -587,16 +621,46 @@ int grid_for(int mtiles, int nt) {
   return (int)((g + 7) / 8 * 8);
 }
 
-int gemm_bm(const moe_problem& p) {
-  if (p.dtype != MOE_BF16) return kGemmBM32;
-  return gemm_wide(p) ? 256 : gemm_small(p) ? 32 : 128;
-}
-
 // expected kept rows per expert: T*k/E, or the capacity if that is smaller
 static double expected_rows(const moe_problem& p) {
   double rows = (double)p.T * p.k / p.E;
   if (p.capacity_factor > 0) rows = std::min(rows, std::ceil(p.capacity_factor * rows));
   return rows;
+}
+
+// Row-tile classes between the small and the wide one (bf16, d % 256 == 0). All use ragged
+// tiles (the staggered kernel skips the A loads, LDS reads and MFMAs of padding rows), so a
+// taller tile costs little extra MFMA work and streams each weight tile once for more rows.
+// The height, by the expected rows per expert r, is the one measured fastest on MI355X for
+// DeepSeek-V3-like routing (segment sizes spread about +-13% around r):
+//   r <= 100: 128;  (100, 176]: 192;  (176, 288]: 256;  (288, 448]: 192;  (448, 768): 256.
+// With a capacity limit the routing is usually skewed (a few segments at the cap, many tiny
+// ones) and 128 was fastest throughout.
+int gemm_bm(const moe_problem& p) {
+  if (p.dtype != MOE_BF16) return kGemmBM32;
+  if (gemm_wide(p)) return 256;
+  if (gemm_small(p)) return 32;
+  if (p.d % 256 || p.capacity_factor > 0) return 128;
+  const double r = expected_rows(p);
+  if (r <= 100.0) return 128;
+  if (r <= 176.0 || (r > 288.0 && r <= 448.0)) return 192;
+  return 256;
+}
+
+// Expert-choice routing: every segment holds exactly C rows, so take the height with the
+// fewest tiles per segment, the shortest of those on a tie.
+int gemm_bm_exact(const moe_problem& p, int C) {
+  if (p.dtype != MOE_BF16) return kGemmBM32;
+  if (gemm_wide(p)) return 256;
+  if (gemm_small(p)) return 32;
+  if (p.d % 256) return 128;
+  int best = 128, tiles = ceil_div(C, 128);
+  for (int bm : {192, 256})
+    if (ceil_div(C, bm) < tiles) {
+      best = bm;
+      tiles = ceil_div(C, bm);
+    }
+  return best;
 }
 
 bool gemm_wide(const moe_problem& p) {
@@ -687,10 +751,13 @@ hipError_t launch_expert_ffn(const moe_problem& p, const void* x, const void* w1
     b.ksplit = down_ksplit(p);
     b.out_rows_b = out_rows_b;
     if (b.ksplit == 2 && !out_rows_b) return hipErrorInvalidValue;
-    if (sc.BM == 256) return launch_bf16_st<256, 256, 4, 2, 256, 4, 2, false>(p, a, b, s, between);
+    if (sc.BM == 256 && gemm_wide(p))
+      return launch_bf16_st<256, 256, 4, 2, 256, 4, 2, false>(p, a, b, s, between);
+    if (sc.BM == 256) return launch_bf16_st<256, 256, 4, 2, 256, 4, 2, true>(p, a, b, s, between);
+    if (sc.BM == 192) return launch_bf16_st<192, 256, 2, 4, 256, 2, 4, true>(p, a, b, s, between);
     if (sc.BM == 32) return launch_bf16<32, 256, 1, 4, 128, 1, 4, 64, 4>(p, a, b, s, between);
     // down tiles of 256 output features need d % 256 == 0 (the entry points accept d % 128)
-    if (p.d % 256 == 0) return launch_bf16<128, 256, 2, 4, 256, 2, 4, 64, 3>(p, a, b, s, between);
+    if (p.d % 256 == 0) return launch_bf16_st<128, 256, 2, 4, 256, 2, 4, true>(p, a, b, s, between);
     return launch_bf16<128, 256, 2, 4, 128, 2, 4, 64, 3>(p, a, b, s, between);
   }
   GemmArgs32 a{};

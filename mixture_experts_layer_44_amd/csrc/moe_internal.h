@@ -56,6 +56,7 @@ int max_mtiles(long long n_rows, int T, int E, int n_shared, int BM);
 bool gemm_wide(const moe_problem& p);
 bool gemm_small(const moe_problem& p);
 int gemm_bm(const moe_problem& p);
+int gemm_bm_exact(const moe_problem& p, int C);   // all segments of exactly C rows
 int grid_for(int mtiles, int nt);
 
 // ---------------------------------------------------------------- launchers

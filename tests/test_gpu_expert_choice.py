@@ -30,6 +30,9 @@ CASES = [
     W("ec_E256", T=512, d=256, E=256, k=8, d_ff=128, seed=407),
     W("ec_T4096", T=4096, d=512, E=8, k=2, d_ff=512, seed=408, capacity_factor=1.25),
     W("ec_wide_ksplit", T=2048, d=1024, E=4, k=2, d_ff=1024, seed=409),
+    # buckets of C = 150 rows (one ragged 192-row tile) and C = 250 (one ragged 256-row tile)
+    W("ec_mid192", T=1200, d=256, E=8, k=1, d_ff=256, seed=410),
+    W("ec_mid256", T=1000, d=512, E=4, k=1, d_ff=256, seed=411, n_shared=1, d_ff_shared=256),
 ]
 
 

@@ -50,6 +50,12 @@ SMALL = [
     W("bf16_wide", T=1600, d=512, E=4, k=2, d_ff=384, seed=113, n_shared=1, d_ff_shared=384),
     # wide tiles with the down GEMM's K range split in two (few down tiles, no shared expert)
     W("bf16_wide_ksplit", T=2048, d=1024, E=4, k=2, d_ff=1024, seed=114),
+    # ragged 192-row tiles: ~150 rows per expert (one tile), the shared group 600 rows (four)
+    W("bf16_mid192", T=600, d=512, E=8, k=2, d_ff=384, seed=115, n_shared=1, d_ff_shared=384),
+    # ragged 192-row tiles, ~350 rows per expert (two tiles each)
+    W("bf16_mid192_two", T=1400, d=256, E=8, k=2, d_ff=256, seed=116),
+    # ragged 256-row tiles (~230 rows per expert) with a selection bias
+    W("bf16_mid256", T=920, d=256, E=8, k=2, d_ff=256, seed=117, sel_bias=True),
 ]
 
 

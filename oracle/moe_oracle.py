@@ -1,4 +1,4 @@
-"""Plain fp64 CPU oracle for the sparse top-k MoE layer forward.
+"""Plain fp64 CPU oracle for the sparse top-k MoE layer: forward and backward.
 
 TEST INFRASTRUCTURE ONLY. Nothing on the product path imports this module:
 only the tests, the smoke check and the benchmark's CPU-baseline leg may call
@@ -30,6 +30,10 @@ f_i counted before dropping over T*k assignments; alpha inside L_balance.
 bias_update follows the pages' direction rule; its threshold (the mean load)
 and step (a caller parameter) are readings.
 
+moe_backward is the chain rule through the same forward, with the selection
+held fixed (top-k and capacity drops have no gradient) and f_i a constant in
+the balance loss, as the [Deep Dive] derivation prescribes.
+
 Pin status: every function below is pinned by a `-m "not gpu"` test against
 values the pages print, closed forms, library special cases or brute force,
 except the readings themselves (drop order, the Zipf offset, what the
@@ -47,6 +51,8 @@ __all__ = [
     "route", "capacity", "align", "silu", "swiglu_expert", "moe_forward",
     "moe_forward_naive", "token_output", "token_outputs", "balance", "expert_table",
     "bias_update", "expert_choice_capacity", "expert_choice_route", "moe_forward_expert_choice",
+    "sigmoid", "silu_grad", "swiglu_expert_backward", "gate_logit_grad", "balance_logit_grad",
+    "moe_backward",
 ]
 
 ExpertFn = Callable[[int], Tuple[np.ndarray, np.ndarray, np.ndarray]]
@@ -394,3 +400,143 @@ def moe_forward_expert_choice(x, w_gate, experts: ExpertFn, E: int, C: int, logi
     y += _shared_sum(x, shared)
     return y, dict(tokens=r_tok, gates=gates, probs=probs)
 
+
+
+# ----------------------------------------------------------------------------- backward
+# The layer's gradient, written step by step from the chain rule. The objective is
+#   J = sum_t <dy_t, y_t> + dL * L_balance,
+# where dy is the upstream gradient of the output and dL that of the balance loss. The
+# selection (top-k ids, capacity drops) is a discrete decision with no gradient; f_i is the
+# count of that decision and is held constant, so the balance loss reaches the router only
+# through P_i ([Deep Dive] "Load Balancing Loss Derivation": F is a post-hoc statistic with
+# no gradient, P is the differentiable proxy that carries it; [Arch] §2 "Load Balancing").
+def sigmoid(z: np.ndarray) -> np.ndarray:
+    """1 / (1 + exp(-z)), written as exp(z) / (1 + exp(z)) for z < 0 (no overflow)."""
+    z = np.asarray(z, dtype=np.float64)
+    out = np.empty_like(z)
+    pos = z >= 0
+    out[pos] = 1.0 / (1.0 + np.exp(-z[pos]))
+    ez = np.exp(z[~pos])
+    out[~pos] = ez / (1.0 + ez)
+    return out
+
+
+def silu_grad(z: np.ndarray) -> np.ndarray:
+    """d/dz [z * sigmoid(z)] = sigmoid(z) * (1 + z * (1 - sigmoid(z)))."""
+    s = sigmoid(z)
+    return s * (1.0 + np.asarray(z, dtype=np.float64) * (1.0 - s))
+
+
+def swiglu_expert_backward(rows, w1, w3, w2, d_out):
+    """Backward of one SwiGLU expert o = W2 (SiLU(W1 x) * (W3 x)) over a batch of rows.
+
+    d_out [n, d] is the gradient of the n output rows. Returns (d_rows [n, d], dw1 [d_ff, d],
+    dw3 [d_ff, d], dw2 [d, d_ff], o [n, d]) -- o, the forward output, is what a gate's
+    gradient is taken against."""
+    rows = np.asarray(rows, dtype=np.float64)
+    w1 = np.asarray(w1, dtype=np.float64)
+    w3 = np.asarray(w3, dtype=np.float64)
+    w2 = np.asarray(w2, dtype=np.float64)
+    u = rows @ w1.T
+    v = rows @ w3.T
+    s = silu(u)
+    h = s * v
+    o = h @ w2.T
+    dw2 = d_out.T @ h                     # o = h W2^T
+    dh = d_out @ w2
+    du = dh * v * silu_grad(u)            # h = SiLU(u) * v
+    dv = dh * s
+    dw1 = du.T @ rows                     # u = x W1^T
+    dw3 = dv.T @ rows                     # v = x W3^T
+    d_rows = du @ w1 + dv @ w3
+    return d_rows, dw1, dw3, dw2, o
+
+
+def gate_logit_grad(gates: np.ndarray, dgate: np.ndarray) -> np.ndarray:
+    """Gradient of the k renormalised gates of each token w.r.t. the logits of its selected
+    experts. The gates are the selected probabilities over their sum, which is a softmax over
+    the k selected logits ([Deep Dive] "Weighted Sum Output"; [Arch] §2 "Gating Function"), so
+    d g_j / d l_m = g_j (delta_jm - g_m) for selected m and 0 for the rest. Returns [T, k]:
+    the gradient of each selected logit."""
+    inner = (gates * dgate).sum(axis=1, keepdims=True)
+    return gates * (dgate - inner)
+
+
+def balance_logit_grad(probs: np.ndarray, counts_pre: np.ndarray, T: int, k: int,
+                       alpha: float, dL: float) -> np.ndarray:
+    """Gradient of dL * L_balance w.r.t. the router logits, with f held constant.
+
+    L = alpha * E * sum_i f_i P_i and P_i = mean over tokens of p[t, i], so
+    dJ/dp[t, i] = dL * alpha * E * f_i / T; the softmax then gives
+    dJ/dl[t, e] = p[t, e] * (dJ/dp[t, e] - sum_i p[t, i] dJ/dp[t, i]). Returns [T, E]."""
+    probs = np.asarray(probs, dtype=np.float64)
+    E = probs.shape[1]
+    f = np.asarray(counts_pre, dtype=np.float64) / float(T * k)
+    w = float(dL) * float(alpha) * E * f / float(T)
+    return probs * (w[None, :] - (probs * w[None, :]).sum(axis=1, keepdims=True))
+
+
+def moe_backward(x, w_gate, experts: ExpertFn, E: int, k: int, dy, logit_bias=None,
+                 sel_bias=None, shared: Sequence = (), capacity_factor: float = 0.0, ids=None,
+                 alpha: float = 0.01, dL: float = 0.0):
+    """Gradients of J = sum_t <dy_t, y_t> + dL * L_balance w.r.t. every input of the layer.
+
+    The forward is moe_forward's (with `ids` given, routing uses those ids, as there). Each
+    kept assignment (t, j) to expert e adds g_tj * o_tj to y_t with o_tj = Expert_e(x_t):
+      d g_tj = <dy_t, o_tj>; the expert's rows get d o = g_tj * dy_t;
+      a dropped assignment adds nothing, so its d g is 0 (it still sits in the renormalising
+      sum of the gates);
+      the shared experts take dy_t with gate 1.
+    The router: d l = gate part (selected logits) + balance part; dx gets d l W_gate,
+    dW_gate = d l^T x, d logit_bias = column sums of d l. sel_bias has no gradient.
+    Returns a dict: dx [T,d], dw_gate [E,d], dlogit_bias [E], dw1/dw3 [E,d_ff,d],
+    dw2 [E,d,d_ff], dshared (list of (ds1, ds3, ds2)), dgate [T,k], dlogits [T,E], and the
+    routing (ids, gates, probs, align outputs)."""
+    x = np.asarray(x, dtype=np.float64)
+    dy = np.asarray(dy, dtype=np.float64)
+    T, d = x.shape
+    r_ids, gates, probs, keys = route(x, w_gate, k, logit_bias, sel_bias)
+    if ids is not None:
+        r_ids = np.asarray(ids, dtype=np.int64)
+        gates = renormalised_gates(probs, r_ids)
+    cap = capacity(capacity_factor, T, k, E)
+    al = align(r_ids, E, cap)
+    flat_gates = gates.reshape(-1)
+    dx = np.zeros((T, d), dtype=np.float64)
+    dgate = np.zeros(T * k, dtype=np.float64)
+    dw1, dw3, dw2 = [], [], []
+    for e in range(E):
+        w1_e, w3_e, w2_e = experts(e)
+        seg = al["sorted_assign"][al["offsets"][e]:al["offsets"][e + 1]]
+        if seg.size == 0:                         # an expert with no kept rows: zero gradient
+            dw1.append(np.zeros_like(w1_e))
+            dw3.append(np.zeros_like(w3_e))
+            dw2.append(np.zeros_like(w2_e))
+            continue
+        tok = seg // k
+        g = flat_gates[seg]
+        d_rows, g1, g3, g2, o = swiglu_expert_backward(x[tok], w1_e, w3_e, w2_e,
+                                                       g[:, None] * dy[tok])
+        dgate[seg] = (dy[tok] * o).sum(axis=1)
+        np.add.at(dx, tok, d_rows)
+        dw1.append(g1)
+        dw3.append(g3)
+        dw2.append(g2)
+    dshared = []
+    for (s1, s3, s2) in shared:
+        d_rows, g1, g3, g2, _ = swiglu_expert_backward(x, s1, s3, s2, dy)
+        dx += d_rows
+        dshared.append((g1, g3, g2))
+    dgate = dgate.reshape(T, k)
+    dlogits = np.zeros((T, E), dtype=np.float64)
+    if T:
+        sel_grad = gate_logit_grad(gates, dgate)
+        np.add.at(dlogits, (np.repeat(np.arange(T), k), r_ids.reshape(-1)), sel_grad.reshape(-1))
+        if dL:
+            dlogits += balance_logit_grad(probs, al["counts_pre"], T, k, alpha, dL)
+    w_gate64 = np.asarray(w_gate, dtype=np.float64)
+    dx += dlogits @ w_gate64
+    return dict(dx=dx, dw_gate=dlogits.T @ x, dlogit_bias=dlogits.sum(axis=0),
+                dw1=np.stack(dw1) if E else np.zeros((0,)), dw3=np.stack(dw3) if E else np.zeros((0,)),
+                dw2=np.stack(dw2) if E else np.zeros((0,)), dshared=dshared, dgate=dgate,
+                dlogits=dlogits, ids=r_ids, gates=gates, probs=probs, cap=cap, **al)

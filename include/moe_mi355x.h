@@ -222,6 +222,43 @@ moe_status moe_forward_staged(const moe_problem* p, const void* x, const void* w
                               void* ws, size_t ws_bytes, hipStream_t stream,
                               hipEvent_t* stage_events);
 
+/* Workspace bytes of moe_backward (host-only). MOE_EUNSUPPORTED unless dtype is
+   MOE_BF16 and k <= 16. */
+moe_status moe_backward_workspace_bytes(const moe_problem* p, size_t* bytes_out);
+
+/* Layer backward: the gradient of J = sum_t <dy_t, y_t> + dL * L_balance with respect to
+   every input of the layer, for the routing a moe_forward call produced.
+   The selection (top-k ids, capacity drops) is held fixed -- it has no gradient -- and f_i
+   is its count, a constant in L_balance = alpha * E * sum_i f_i P_i, so the balance term
+   reaches the router only through P ("MoE (Mixture of Experts) Deep Dive", "Load
+   Balancing Loss Derivation"; "MoE Architecture" §2 "Load Balancing"). The gates are a
+   softmax over the k selected logits ("Weighted Sum Output"; §2 "Gating Function"), so a
+   gate's gradient reaches only the selected logits; a dropped slot has a zero gate
+   gradient but stays in its token's renormalising sum. SwiGLU experts as in §3.
+     x, w_gate, logit_bias, w1/w3/w2, ws1/ws3/ws2: the forward's inputs (bf16 storage);
+     topk_ids, topk_w, counts_pre, offsets, sorted_assign, assign_pos: the forward's
+       routing outputs, unchanged (device);
+     dy [T,d] fp32: gradient of y; alpha: the balance loss's alpha; dL: gradient of
+       L_balance (0 leaves the balance term out); both finite;
+     dx [T,d] fp32 out; dw_gate [E,d] fp32 out; dlogit_bias [E] fp32 out or NULL;
+     dw1, dw3 [E,d_ff,d] and dw2 [E,d,d_ff] out, bf16 (the weights' storage type; an
+       expert with no kept rows gets zeros); dws1/dws3/dws2 likewise for the shared
+       expert (required when n_shared = 1);
+     ws: moe_backward_workspace_bytes bytes, caller-owned scratch.
+   Rounding: dy, g*dy, du, dv and the router's logit gradient enter the MFMA products as
+   bf16 (fp32 accumulation); u and v are recomputed with the forward's own gate-up GEMM.
+   Errors: MOE_EINVAL for a NULL required pointer or a non-finite alpha / dL,
+   MOE_EUNSUPPORTED for fp32 storage or k > 16, MOE_EWORKSPACE, MOE_EHIP. */
+moe_status moe_backward(const moe_problem* p, const void* x, const void* w_gate,
+                        const float* logit_bias, const void* w1, const void* w3, const void* w2,
+                        const void* ws1, const void* ws3, const void* ws2,
+                        const int32_t* topk_ids, const float* topk_w, const int32_t* counts_pre,
+                        const int32_t* offsets, const int32_t* sorted_assign,
+                        const int32_t* assign_pos, const float* dy, float alpha, float dL,
+                        float* dx, float* dw_gate, float* dlogit_bias, void* dw1, void* dw3,
+                        void* dw2, void* dws1, void* dws3, void* dws2, void* ws,
+                        size_t ws_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -75,10 +75,12 @@ def _load() -> ctypes.CDLL:
     L.moe_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                               vp, vp, vp, vp, sz, vp]
     L.moe_forward_staged.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
+    L.moe_backward_workspace_bytes.argtypes = [P, ctypes.POINTER(sz)]
+    L.moe_backward.argtypes = [P] + [vp] * 16 + [f32, f32] + [vp] * 10 + [sz, vp]
     for fn in ("moe_validate", "moe_capacity", "moe_workspace_bytes", "moe_route", "moe_align",
                "moe_expert_ffn", "moe_combine", "moe_balance", "moe_forward", "moe_forward_staged",
                "moe_bias_update", "moe_expert_choice_capacity", "moe_expert_choice_workspace_bytes",
-               "moe_forward_expert_choice"):
+               "moe_forward_expert_choice", "moe_backward_workspace_bytes", "moe_backward"):
         getattr(L, fn).restype = ctypes.c_int
     return L
 
@@ -361,6 +363,74 @@ def forward_expert_choice(p: Problem, x, w_gate, w1, w3, w2, logit_bias=None, ws
         _ptr(ws1), _ptr(ws3), _ptr(ws2), _ptr(y), _ptr(g("tokens")), _ptr(g("gates")),
         _ptr(g("prob_sum")), _ptr(ws), ws.numel(), _stream(dev)))
     return (y, r) if return_routing else y
+
+
+def backward_workspace_bytes(p: Problem) -> int:
+    n = ctypes.c_size_t(0)
+    _check("moe_backward_workspace_bytes",
+           _lib.moe_backward_workspace_bytes(ctypes.byref(p), ctypes.byref(n)))
+    return n.value
+
+
+def backward(p: Problem, x, w_gate, w1, w3, w2, routing, dy, logit_bias=None, ws1=None, ws3=None,
+             ws2=None, alpha: float = 0.01, dL: float = 0.0, want_dlogit_bias: bool = False,
+             ws=None, out=None):
+    """Layer backward (bf16 storage) for the routing a forward(..., return_routing=True) call
+    returned. dy: [T,d] fp32 gradient of y; dL: gradient of the balance loss (alpha as in the
+    forward's balance statistics). Returns a dict: dx [T,d] fp32, dw_gate [E,d] fp32,
+    dw1/dw3 [E,d_ff,d] and dw2 [E,d,d_ff] in the weights' dtype, the shared expert's
+    dws1/dws3/dws2 when it has one, and dlogit_bias [E] fp32 with want_dlogit_bias.
+    `out` may hold preallocated tensors under those names."""
+    dev, dt = x.device, _dt(p)
+    _need(x, "x", (p.T, p.d), dt, dev)
+    _need(w_gate, "w_gate", (p.E, p.d), dt, dev)
+    _need(w1, "w1", (p.E, p.d_ff, p.d), dt, dev)
+    _need(w3, "w3", (p.E, p.d_ff, p.d), dt, dev)
+    _need(w2, "w2", (p.E, p.d, p.d_ff), dt, dev)
+    _need(dy, "dy", (p.T, p.d), torch.float32, dev)
+    _need(logit_bias, "logit_bias", (p.E,), torch.float32, dev, optional=True)
+    if p.n_shared:
+        _need(ws1, "ws1", (1, p.d_ff_shared, p.d), dt, dev)
+        _need(ws3, "ws3", (1, p.d_ff_shared, p.d), dt, dev)
+        _need(ws2, "ws2", (1, p.d, p.d_ff_shared), dt, dev)
+    r = routing
+    _need(r["topk_ids"], "topk_ids", (p.T, p.k), torch.int32, dev)
+    _need(r["topk_w"], "topk_w", (p.T, p.k), torch.float32, dev)
+    _need(r["counts_pre"], "counts_pre", (p.E,), torch.int32, dev)
+    _need(r["offsets"], "offsets", (p.E + 1,), torch.int32, dev)
+    for key in ("sorted_assign", "assign_pos"):
+        t = r[key]
+        if t.device != dev or t.dtype != torch.int32 or not t.is_contiguous() or t.numel() < p.T * p.k:
+            raise ValueError(f"{key} must be a contiguous int32 tensor of >= T*k entries on {dev}")
+    o = dict(out or {})
+    want = dict(dx=((p.T, p.d), torch.float32), dw_gate=((p.E, p.d), torch.float32),
+                dw1=((p.E, p.d_ff, p.d), dt), dw3=((p.E, p.d_ff, p.d), dt),
+                dw2=((p.E, p.d, p.d_ff), dt))
+    if p.n_shared:
+        want.update(dws1=((1, p.d_ff_shared, p.d), dt), dws3=((1, p.d_ff_shared, p.d), dt),
+                    dws2=((1, p.d, p.d_ff_shared), dt))
+    if want_dlogit_bias:
+        want["dlogit_bias"] = ((p.E,), torch.float32)
+    for name, (shape, dtype) in want.items():
+        if name in o:
+            _need(o[name], name, shape, dtype, dev)
+        else:
+            o[name] = torch.empty(shape, dtype=dtype, device=dev)
+    need = backward_workspace_bytes(p)
+    if ws is None:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    elif ws.device != dev or ws.dtype != torch.uint8 or ws.numel() < need:
+        raise ValueError(f"workspace must be a uint8 tensor of >= {need} bytes on {dev}")
+    g = o.get
+    _check("moe_backward", _lib.moe_backward(
+        ctypes.byref(p), _ptr(x), _ptr(w_gate), _ptr(logit_bias), _ptr(w1), _ptr(w3), _ptr(w2),
+        _ptr(ws1), _ptr(ws3), _ptr(ws2), _ptr(r["topk_ids"]), _ptr(r["topk_w"]),
+        _ptr(r["counts_pre"]), _ptr(r["offsets"]), _ptr(r["sorted_assign"]),
+        _ptr(r["assign_pos"]), _ptr(dy), float(alpha), float(dL), _ptr(g("dx")),
+        _ptr(g("dw_gate")), _ptr(g("dlogit_bias")), _ptr(g("dw1")), _ptr(g("dw3")),
+        _ptr(g("dw2")), _ptr(g("dws1")), _ptr(g("dws3")), _ptr(g("dws2")), _ptr(ws), ws.numel(),
+        _stream(dev)))
+    return o
 
 
 class PreparedForward:

@@ -296,6 +296,44 @@ MOE_API moe_status moe_bias_update(const moe_problem* p, const int32_t* counts_p
   return hip_status(launch_bias_update(*p, counts_pre, gamma, sel_bias, stream));
 }
 
+MOE_API moe_status moe_backward_workspace_bytes(const moe_problem* p, size_t* bytes_out) {
+  moe_status st = moe_validate(p);
+  if (st != MOE_OK) return st;
+  if (!bytes_out) return MOE_EINVAL;
+  if (p->dtype != MOE_BF16 || p->k > 16) return MOE_EUNSUPPORTED;
+  *bytes_out = backward_layout(*p).total;
+  return MOE_OK;
+}
+
+MOE_API moe_status moe_backward(const moe_problem* p, const void* x, const void* w_gate,
+                                const float* logit_bias, const void* w1, const void* w3,
+                                const void* w2, const void* ws1, const void* ws3, const void* ws2,
+                                const int32_t* topk_ids, const float* topk_w,
+                                const int32_t* counts_pre, const int32_t* offsets,
+                                const int32_t* sorted_assign, const int32_t* assign_pos,
+                                const float* dy, float alpha, float dL, float* dx, float* dw_gate,
+                                float* dlogit_bias, void* dw1, void* dw3, void* dw2, void* dws1,
+                                void* dws3, void* dws2, void* ws, size_t ws_bytes,
+                                hipStream_t stream) {
+  moe_status st = moe_validate(p);
+  if (st != MOE_OK) return st;
+  if (p->dtype != MOE_BF16 || p->k > 16) return MOE_EUNSUPPORTED;
+  const bool hasT = p->T > 0;
+  if (!w_gate || !w1 || !w3 || !w2 || !counts_pre || !offsets || !dw_gate || !dw1 || !dw3 || !dw2)
+    return MOE_EINVAL;
+  if (hasT && (!x || !topk_ids || !topk_w || !sorted_assign || !assign_pos || !dy || !dx))
+    return MOE_EINVAL;
+  if (p->n_shared && (!ws1 || !ws3 || !ws2 || !dws1 || !dws3 || !dws2)) return MOE_EINVAL;
+  if (!std::isfinite(alpha) || !std::isfinite(dL)) return MOE_EINVAL;
+  const BwdLayout L = backward_layout(*p);
+  if (ws_bytes < L.total) return MOE_EWORKSPACE;
+  if (!ws) return MOE_EINVAL;
+  return hip_status(launch_backward(*p, L, ws, x, w_gate, logit_bias, w1, w3, w2, ws1, ws3, ws2,
+                                    topk_ids, topk_w, counts_pre, offsets, sorted_assign,
+                                    assign_pos, dy, alpha, dL, dx, dw_gate, dlogit_bias, dw1, dw3,
+                                    dw2, dws1, dws3, dws2, stream));
+}
+
 namespace {
 
 moe_status forward_impl(const moe_problem* p, const void* x, const void* w_gate,

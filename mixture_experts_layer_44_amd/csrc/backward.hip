@@ -1,0 +1,843 @@
+// Layer backward: the gradient of <dy, y> + dL * L_balance with respect to x, the router
+// weight (and logit offset) and every expert weight, for bf16 storage.
+//
+// Pages: "MoE (Mixture of Experts) Deep Dive", "Load Balancing Loss Derivation" (F is a
+// post-hoc count with no gradient, P carries it); "MoE Architecture" §2 "Gating Function"
+// (softmax, top-k, renormalised gates) and "Load Balancing" (L = alpha * E * sum f_i p_i);
+// §3 "Standard MoE" (SwiGLU experts); "Mixture of experts (MoE)" handbook, "Implementation:
+// token by token vs. grouped by expert" (grouped expert GEMMs). The selection is held fixed:
+// top-k and capacity drops have no gradient.
+//
+// Per kept row r of expert e (token t, gate g): d o = g dy_t, d g = <dy_t, o>,
+//   dh = W2^T d o, du = dh * v * SiLU'(u), dv = dh * SiLU(u), d x_t += W1^T du + W3^T dv,
+//   dW2 += d o h^T, dW1 += du x^T, dW3 += dv x^T.
+// Router: d l = (softmax over the selected logits)' d g + the balance term through p;
+//   dx += d l W_gate, dW_gate = d l^T x, d logit_bias = column sums of d l.
+//
+// Storage. Every per-row activation lives in "storage rows": group g's rows r = 0..rows_g-1
+// at row mt_start[g] * 128 + r of a [m-tiles * 128, width] buffer (the 128-row schedule of the
+// grouped GEMMs; the shared expert is group E). The recompute of the gate-up GEMM writes
+// h (bf16) and u, v (fp32) there; a prep kernel writes g * dy (bf16) and the gathered x rows
+// (bf16) there, and dy once in bf16 in token order.
+//
+// GEMMs (one template, bf16 MFMA 32x32x16, fp32 accumulation, 128 x BN tiles, 8 waves, BK 64,
+// a 3-stage ring of direct global->LDS loads):
+//   dgrad-down  [rows x d_ff] = dy_tok [rows x d] . W2_e [d x d_ff]   + SwiGLU backward epilogue
+//   dgrad-x     [rows x d]    = (du|dv) [rows x 2 d_ff] . (W1_e;W3_e) [2 d_ff x d]
+//   wgrad-down  dW2_e [d x d_ff]     = (g dy)^T [d x rows] . h [rows x d_ff]
+//   wgrad-up    (dW1_e;dW3_e) [2 d_ff x d] = (du|dv)^T . x_gathered [rows x d]
+//   router      dx_r [T x d] = d l [T x E] . W_gate [E x d];  dW_gate = d l^T x  (K = T)
+// Every weight and activation stays in its forward layout in HBM. An operand whose contraction
+// index is its row index ("transposed": the weights in dgrad, everything in wgrad) is staged
+// into LDS as [k][m] rows, as it lies in memory, and read with ds_read_b64_tr_b16: within each
+// 16-lane group, lane i points at row k0 + i/4, columns m0 + 4 (i%4) .. +3, and lane j receives
+// column m0 + j at rows k0 .. k0+3 -- half of an MFMA operand; two such reads make the 8 k
+// values a 32x32x16 fragment takes. Such [k][m] rows are XOR-swizzled in 16-byte chunks by
+// 4 * (k % 4), so the 4 rows x 2 chunks of a 16-lane group (and the 4 x 4 of 32 lanes) hit
+// distinct bank groups. Contraction rows past a segment's end read a zero row.
+#include "moe_internal.h"
+#include "mfma_tiles.h"
+#include "topk.h"
+
+namespace moe {
+
+namespace {
+
+typedef short v4s __attribute__((ext_vector_type(4)));
+typedef short v8s __attribute__((ext_vector_type(8)));
+typedef __attribute__((address_space(3))) v4s* lds_v4s_ptr;
+
+constexpr int BBM = 128;   // rows of every backward m-tile (the schedule's BM)
+constexpr int ZERO_ELEMS = 256;
+
+enum AKind : int { A_TOKEN, A_STORE, A_IDENT, AT_STORE, AT_IDENT };
+enum BKind : int { B_W2, B_W13, B_WGATE, BT_STORE, BT_IDENT };
+enum EpiKind : int { EPI_DDOWN, EPI_ROWS, EPI_WBF16, EPI_WF32 };
+enum ModeKind : int { M_ROWS, M_WEIGHTS };
+
+struct BwdArgs {
+  const bf16_t* A;          // A_TOKEN: dy (bf16, token rows); A_STORE / AT_STORE: storage rows;
+  int lda;                  // A_IDENT / AT_IDENT: d l rows [T, lda]
+  const bf16_t* B0;         // routed weights (B_W2: w2; B_W13: w1; B_WGATE: w_gate) or row source
+  const bf16_t* B1;         // B_W13: w3
+  const bf16_t* S0;         // shared expert's weights (B_W2: ws2; B_W13: ws1)
+  const bf16_t* S1;         // B_W13: ws3
+  int ldb;
+  const bf16_t* zero;       // ZERO_ELEMS zero bf16: contraction rows past a segment's end
+  int M, N, K;              // K: rows mode only (weights mode: each group's rows)
+  int E, k, T;
+  int ident;                // 1: one group of ident_rows rows in identity order (router)
+  int ident_rows;
+  int Kvalid;               // B_WGATE: rows of B that exist (E)
+  const int32_t* sorted_assign;
+  Schedule sc;              // BM = 128
+  float* out;               // EPI_ROWS: routed rows (sorted order) or identity rows
+  float* out_shared;        // EPI_ROWS: the shared expert's rows (token order)
+  bf16_t* W0;               // EPI_WBF16: routed dW, output rows < Msplit
+  bf16_t* W1;               //            routed dW, output rows >= Msplit
+  bf16_t* SW0;              //            shared expert, rows < Msplit
+  bf16_t* SW1;              //            shared expert, rows >= Msplit
+  int Msplit;
+  float* Wf;                // EPI_WF32: [Mvalid, N]
+  int Mvalid;
+  const float* U;           // EPI_DDOWN: u, v (fp32 storage rows, width N)
+  const float* V;
+  const float* topk_w;
+  bf16_t* DUV;              //            du | dv (bf16 storage rows, width 2N)
+  float* dgate_part;        //            [rows, NT] per-n-tile partial sums of d g (routed)
+  int NT;
+};
+
+// Physical offset of logical element (row, col) of a swizzled [k][W] tile (transposed stage).
+template <int W>
+__device__ __forceinline__ int tr_off(int row, int col) {
+  return row * W + ((((col >> 3) ^ ((row & 3) << 2))) << 3) + (col & 7);
+}
+
+// One 8 x bf16 MFMA operand from a transposed [k][W] stage: rows (ks*16 + 8*(lane/32)) .. +7,
+// column mb + lane%32. `base` is this lane's precomputed offset for block mb (see below).
+template <int W>
+__device__ __forceinline__ bf16x8 tr_frag(const bf16_t* st, int base, int ks) {
+  auto p0 = (lds_v4s_ptr)(__attribute__((address_space(3))) char*)(st + base + ks * 16 * W);
+  auto p1 = (lds_v4s_ptr)(__attribute__((address_space(3))) char*)(st + base + ks * 16 * W + 4 * W);
+  const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p0);
+  const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p1);
+  const v8s c = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  return __builtin_bit_cast(bf16x8, c);
+}
+
+// This lane's element offset, in a transposed [k][W] stage, of the first of the 4 rows it
+// points at for the operand block whose first column is mb (sub-step 0, first read):
+// lane i of each 16-lane group points at row 8*(group/2) + i/4, column mb + 16*(group%2) + 4*(i%4).
+template <int W>
+__device__ __forceinline__ int tr_base(int lane, int mb) {
+  const int g16 = lane >> 4, i = lane & 15;
+  const int row = 8 * (g16 >> 1) + (i >> 2);
+  const int col = mb + 16 * (g16 & 1) + 4 * (i & 3);
+  return tr_off<W>(row, col);
+}
+
+template <int BN, int MODE, int AK, int BKIND, int EPI>
+__global__ __launch_bounds__(512) void bwd_gemm_kernel(BwdArgs a) {
+  constexpr int BM = BBM, BK = 64, WM = 2, WN = 4, NW = WM * WN, NKS = BK / 16;
+  constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
+  constexpr bool ATR = AK == AT_STORE || AK == AT_IDENT;
+  constexpr int ASZ = BM * BK, BSZ = BN * BK, STAGE = ASZ + BSZ;
+  constexpr int DMA_A = ASZ * 2 / 1024 / NW, DMA_B = BSZ * 2 / 1024 / NW;
+  static_assert(DMA_A * 1024 * NW == ASZ * 2 && DMA_B * 1024 * NW == BSZ * 2, "even split");
+  static_assert(FM >= 1 && FN >= 1, "wave tile covers whole fragments");
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[3 * STAGE];
+  __shared__ float red[EPI == EPI_DDOWN ? WN : 1][EPI == EPI_DDOWN ? BM : 1];
+  __shared__ float gate_s[EPI == EPI_DDOWN ? BM : 1];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+
+  // ---- tile
+  int g = 0, rows = 0, off = 0, m_local = 0, mt_global = 0, n0 = 0, m0 = 0, sbase = 0;
+  if (MODE == M_ROWS) {
+    if (a.ident) {
+      const int MT = (a.ident_rows + BM - 1) / BM, NTt = a.N / BN, total = MT * NTt;
+      const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, per = (total + 7) >> 3;
+      if (slot >= per) return;
+      const int L = xcd * per + slot;
+      if (L >= total) return;
+      const int nt = L / MT;
+      m_local = L - nt * MT;
+      mt_global = m_local;
+      n0 = nt * BN;
+      rows = a.ident_rows;
+    } else {
+      TileCoord tc;
+      if (!tile_coord(a.sc, a.N / BN, BN, tc)) return;
+      g = tc.g;
+      m_local = tc.m_local;
+      mt_global = tc.mt_global;
+      n0 = tc.n0;
+      rows = tc.rows;
+      off = tc.off;
+    }
+  } else {
+    const int G = a.ident ? 1 : a.sc.G;
+    const int MT = a.M / BM, NTt = a.N / BN, total = G * MT * NTt;
+    const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, per = (total + 7) >> 3;
+    if (slot >= per) return;
+    const int L = xcd * per + slot;
+    if (L >= total) return;
+    g = L / (MT * NTt);
+    const int rem = L - g * MT * NTt;
+    const int mt = rem / NTt;
+    m0 = mt * BM;
+    n0 = (rem - mt * NTt) * BN;
+    rows = a.ident ? a.ident_rows : a.sc.grp_rows[g];
+    sbase = a.ident ? 0 : a.sc.mt_start[g] * BM;
+  }
+  const bool shared_grp = !a.ident && g >= a.E;
+  const int KT = MODE == M_ROWS ? a.K / BK : (rows + BK - 1) / BK;
+
+  // ---- A loads
+  // non-transposed [BM][BK] stage (rows mode): load i of this wave fills rows q*8 .. q*8+7
+  // (q = wave*DMA_A + i); lane l fetches the logical chunk that the swizzle puts at physical
+  // chunk l%8 of row q*8 + l/8. Row sources are fixed for the whole tile.
+  // transposed [BK][BM] stage (weights mode): load i fills k-rows q*4 .. q*4+3; lane l writes
+  // physical chunk l%16 of k-row q*4 + l/16.
+  uint32_t aoff[DMA_A];
+  int akrow[DMA_A], alch[DMA_A];
+#pragma unroll
+  for (int i = 0; i < DMA_A; ++i) {
+    const int q = wave * DMA_A + i;
+    if (!ATR) {
+      const int row = q * 8 + lane / 8;
+      const int lchunk = (swz<BK>(row, lane % 8) - row * BK) >> 3;
+      const int rg = m_local * BM + row;
+      const bool valid = rg < rows;
+      int src;
+      if (AK == A_TOKEN) {
+        if (shared_grp) src = valid ? rg : 0;
+        else src = a.sorted_assign[off + (valid ? rg : 0)] / a.k;
+        src = (unsigned)src < (unsigned)a.T ? src : 0;
+      } else if (AK == A_STORE) {
+        src = mt_global * BM + row;
+      } else {
+        src = valid ? rg : 0;
+      }
+      aoff[i] = (uint32_t)src * (uint32_t)a.lda + lchunk * 8;
+    } else {
+      akrow[i] = q * 4 + lane / 16;
+      alch[i] = (lane % 16) ^ ((akrow[i] & 3) << 2);
+    }
+  }
+  auto issue_a = [&](int kt, bf16_t* dst) {
+#pragma unroll
+    for (int i = 0; i < DMA_A; ++i) {
+      const bf16_t* src;
+      if (!ATR) {
+        src = a.A + aoff[i] + kt * BK;
+      } else {
+        const int r = kt * BK + akrow[i];
+        src = r < rows ? a.A + (uint32_t)(sbase + r) * (uint32_t)a.lda + m0 + alch[i] * 8
+                       : a.zero + alch[i] * 8;
+      }
+      __builtin_amdgcn_global_load_lds((const void*)src,
+                                       (lds_ptr_t)(dst + (wave * DMA_A + i) * 512), 16, 0, 0);
+    }
+  };
+
+  // ---- B loads: transposed [BK][BN] stage; load i fills k-rows q*RB .. (q = wave*DMA_B + i)
+  constexpr int CPR = BN / 8, RB = 64 / CPR;   // 16-byte chunks per k-row, k-rows per load
+  int bkrow[DMA_B], blch[DMA_B];
+#pragma unroll
+  for (int i = 0; i < DMA_B; ++i) {
+    const int q = wave * DMA_B + i;
+    bkrow[i] = q * RB + lane / CPR;
+    blch[i] = (lane % CPR) ^ ((bkrow[i] & 3) << 2);
+  }
+  const bf16_t* bmat0 = nullptr;   // B_W2 / B_W13: this group's matrices
+  const bf16_t* bmat1 = nullptr;
+  if (BKIND == B_W2) {
+    bmat0 = shared_grp ? a.S0 : a.B0 + (size_t)g * a.K * a.N;
+  } else if (BKIND == B_W13) {
+    const size_t msz = (size_t)(a.K / 2) * a.N;
+    bmat0 = shared_grp ? a.S0 : a.B0 + (size_t)g * msz;
+    bmat1 = shared_grp ? a.S1 : a.B1 + (size_t)g * msz;
+  }
+  auto issue_b = [&](int kt, bf16_t* dst) {
+#pragma unroll
+    for (int i = 0; i < DMA_B; ++i) {
+      const int r = kt * BK + bkrow[i];
+      const bf16_t* src;
+      if (BKIND == B_W2) {
+        src = bmat0 + (uint32_t)r * (uint32_t)a.ldb + n0 + blch[i] * 8;
+      } else if (BKIND == B_W13) {
+        const int half = a.K / 2;
+        src = r < half ? bmat0 + (uint32_t)r * (uint32_t)a.ldb + n0 + blch[i] * 8
+                       : bmat1 + (uint32_t)(r - half) * (uint32_t)a.ldb + n0 + blch[i] * 8;
+      } else if (BKIND == B_WGATE) {
+        src = r < a.Kvalid ? a.B0 + (uint32_t)r * (uint32_t)a.ldb + n0 + blch[i] * 8
+                           : a.zero + blch[i] * 8;
+      } else {
+        src = r < rows ? a.B0 + (uint32_t)(sbase + r) * (uint32_t)a.ldb + n0 + blch[i] * 8
+                       : a.zero + blch[i] * 8;
+      }
+      __builtin_amdgcn_global_load_lds((const void*)src,
+                                       (lds_ptr_t)(dst + (wave * DMA_B + i) * 512), 16, 0, 0);
+    }
+  };
+
+  // ---- fragment offsets
+  const int fr = lane & 31, fkc = lane >> 5;
+  int aoffs[NKS], abase[FM], bbase[FN];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks)
+    aoffs[ks] = (wm * TM + fr) * BK + ((((2 * ks + fkc) ^ ((fr >> 1) & 7))) << 3);
+#pragma unroll
+  for (int i = 0; i < FM; ++i) abase[i] = tr_base<BM>(lane, wm * TM + i * 32);
+#pragma unroll
+  for (int j = 0; j < FN; ++j) bbase[j] = tr_base<BN>(lane, wn * TN + j * 32);
+
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  auto compute = [&](const bf16_t* As, const bf16_t* Bs) {
+    __builtin_amdgcn_iglp_opt(1);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      bf16x8 af[FM], bfv[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+        af[i] = ATR ? tr_frag<BM>(As, abase[i], ks)
+                    : *(const bf16x8*)&As[aoffs[ks] + i * 32 * BK];
+#pragma unroll
+      for (int j = 0; j < FN; ++j) bfv[j] = tr_frag<BN>(Bs, bbase[j], ks);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfv[j], acc[i][j], 0, 0, 0);
+    }
+  };
+
+  // ---- main loop: 3-stage ring, two steps in flight (as in the forward's ring kernel)
+  if (KT > 0) {
+    issue_a(0, smem);
+    issue_b(0, smem + ASZ);
+    issue_a(KT > 1 ? 1 : 0, smem + STAGE);
+    issue_b(KT > 1 ? 1 : 0, smem + STAGE + ASZ);
+    for (int kt = 0; kt < KT; ++kt) {
+      __builtin_amdgcn_s_waitcnt(wait_vm(DMA_A + DMA_B));
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      const int nxt = kt + 2, ld = nxt < KT ? nxt : KT - 1;
+      bf16_t* st = smem + (nxt % 3) * STAGE;
+      issue_a(ld, st);
+      issue_b(ld, st + ASZ);
+      const bf16_t* cs = smem + (kt % 3) * STAGE;
+      compute(cs, cs + ASZ);
+    }
+    __builtin_amdgcn_s_waitcnt(wait_vm(0));
+  }
+
+  // ---- epilogues. 32x32 accumulator layout: lane holds column lane%32 and rows
+  // 8*(r/4) + 4*(lane/32) + r%4 for r = 0..15 of each fragment.
+  if (EPI == EPI_DDOWN) {
+    if (tid < BM) {
+      const int rg = m_local * BM + tid;
+      float gv = 1.f;
+      if (!shared_grp && rg < rows) gv = a.topk_w[a.sorted_assign[off + rg]];
+      gate_s[tid] = gv;
+    }
+    __syncthreads();
+    const int N = a.N;
+    float part[FM][16];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) part[i][r] = 0.f;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        const int col = n0 + wn * TN + j * 32 + fr;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int lr = wm * TM + i * 32 + 8 * (r >> 2) + 4 * fkc + (r & 3);
+          if (m_local * BM + lr < rows) {
+            const size_t s = (size_t)(mt_global * BM + lr);
+            const float u = a.U[s * N + col], v = a.V[s * N + col];
+            const float dh = acc[i][j][r];
+            const float sig = __builtin_amdgcn_rcpf(1.0f + __expf(-u));
+            const float sl = u * sig;                           // SiLU(u), as the forward
+            const float h = bf16_to_f32(f32_to_bf16(sl * v));   // the forward's stored h
+            part[i][r] += dh * h;
+            const float gdh = gate_s[lr] * dh;
+            a.DUV[s * 2 * N + col] = f32_to_bf16(gdh * v * sig * (1.0f + u * (1.0f - sig)));
+            a.DUV[s * 2 * N + N + col] = f32_to_bf16(gdh * sl);
+          }
+        }
+      }
+    // row sums over this wave's columns: the 32 lanes of each half share their rows
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float v = part[i][r];
+        v += __shfl_xor(v, 16, 32);
+        v += __shfl_xor(v, 8, 32);
+        v += __shfl_xor(v, 4, 32);
+        v += __shfl_xor(v, 2, 32);
+        v += __shfl_xor(v, 1, 32);
+        if (fr == 0) red[wn][wm * TM + i * 32 + 8 * (r >> 2) + 4 * fkc + (r & 3)] = v;
+      }
+    __syncthreads();
+    if (tid < BM && !shared_grp) {
+      const int rg = m_local * BM + tid;
+      if (rg < rows) {
+        float s = 0.f;
+#pragma unroll
+        for (int w = 0; w < WN; ++w) s += red[w][tid];
+        a.dgate_part[(size_t)(off + rg) * a.NT + n0 / BN] = s;
+      }
+    }
+    return;
+  }
+
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int col = n0 + wn * TN + j * 32 + fr;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int lr = wm * TM + i * 32 + 8 * (r >> 2) + 4 * fkc + (r & 3);
+        const float val = acc[i][j][r];
+        if (EPI == EPI_ROWS) {
+          const int rg = m_local * BM + lr;
+          if (rg < rows) {
+            float* dst = a.ident ? a.out + (size_t)rg * a.N
+                         : shared_grp     ? a.out_shared + (size_t)rg * a.N
+                                          : a.out + (size_t)(off + rg) * a.N;
+            dst[col] = val;
+          }
+        } else if (EPI == EPI_WBF16) {
+          const int m = m0 + lr;
+          const bool second = m >= a.Msplit;
+          const int mm = second ? m - a.Msplit : m;
+          bf16_t* base = shared_grp ? (second ? a.SW1 : a.SW0)
+                                    : (second ? a.W1 : a.W0) + (size_t)g * a.Msplit * a.N;
+          base[(size_t)mm * a.N + col] = f32_to_bf16(val);
+        } else {
+          const int m = m0 + lr;
+          if (m < a.Mvalid) a.Wf[(size_t)m * a.N + col] = val;
+        }
+      }
+    }
+}
+
+// ------------------------------------------------------------------ small kernels
+// Items 0..T-1: dy row t -> bf16. Items T..: storage rows s of the grouped layout: routed row
+// (group g, row r) -> assignment a = sorted_assign[off + r], token t = a / k, gate g_a:
+// DO[s] = bf16(g_a dy_t), XS[s] = x_t; shared rows: DO[s] = bf16(dy_r), XS[s] = x_r. Padding
+// rows are skipped. The first workgroup also clears the zero row.
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const float* __restrict__ dy,
+                                                       const bf16_t* __restrict__ x,
+                                                       const int32_t* __restrict__ sorted_assign,
+                                                       const float* __restrict__ topk_w,
+                                                       Schedule sc, int T, int d, int k, int E,
+                                                       bf16_t* __restrict__ dyb,
+                                                       bf16_t* __restrict__ DO,
+                                                       bf16_t* __restrict__ XS,
+                                                       bf16_t* __restrict__ zero) {
+  if (blockIdx.x == 0 && threadIdx.x < ZERO_ELEMS) zero[threadIdx.x] = 0;
+  const int total = T + sc.mt_start[sc.G] * BBM;
+  const int d4 = d >> 2;
+  for (int item = blockIdx.x; item < total; item += gridDim.x) {
+    if (item < T) {
+      const f32x4* src = (const f32x4*)(dy + (size_t)item * d);
+      for (int c = threadIdx.x; c < d4; c += 256) {
+        const f32x4 v = src[c];
+        bf16_t* o = dyb + (size_t)item * d + 4 * c;
+        o[0] = f32_to_bf16(v[0]);
+        o[1] = f32_to_bf16(v[1]);
+        o[2] = f32_to_bf16(v[2]);
+        o[3] = f32_to_bf16(v[3]);
+      }
+      continue;
+    }
+    const int s = item - T;
+    const int mt = s / BBM, g = sc.mt_group[mt];
+    const int r = (mt - sc.mt_start[g]) * BBM + s % BBM;
+    if (r >= sc.grp_rows[g]) continue;
+    int t = r;
+    float gate = 1.f;
+    if (g < E) {
+      const int asg = sorted_assign[sc.grp_off[g] + r];
+      t = asg / k;
+      gate = topk_w[asg];
+    }
+    const f32x4* src = (const f32x4*)(dy + (size_t)t * d);
+    const uint2* xs = (const uint2*)(x + (size_t)t * d);
+    for (int c = threadIdx.x; c < d4; c += 256) {
+      const f32x4 v = src[c];
+      bf16_t* o = DO + (size_t)s * d + 4 * c;
+      o[0] = f32_to_bf16(gate * v[0]);
+      o[1] = f32_to_bf16(gate * v[1]);
+      o[2] = f32_to_bf16(gate * v[2]);
+      o[3] = f32_to_bf16(gate * v[3]);
+      ((uint2*)(XS + (size_t)s * d))[c] = xs[c];
+    }
+  }
+}
+
+// Router backward, one wave per token (4 per workgroup). Lane e (+64 i) recomputes the logit
+// and the softmax probability of expert e exactly as the forward's router does; lanes j < k
+// hold slot j's gate gradient (the sum of its per-n-tile partials, 0 if the slot was dropped).
+// d l[e] = sum over slots j choosing e of g_j (dg_j - sum_j' g_j' dg_j')          (gates)
+//        + p_e (w_e - sum_e' p_e' w_e'),  w_e = dL alpha E counts_pre[e] / (T k T)  (balance)
+// Writes d l in bf16 ([T, E_pad], zero past E) and per-workgroup column sums (fp32, for the
+// logit offset's gradient).
+__global__ __launch_bounds__(256) void bwd_router_kernel(
+    const float* __restrict__ part, int KS, int T, int E, int E16, int k,
+    const float* __restrict__ logit_bias, const int32_t* __restrict__ ids,
+    const float* __restrict__ topk_w, const int32_t* __restrict__ assign_pos,
+    const float* __restrict__ dgate_part, int NT, const int32_t* __restrict__ counts_pre,
+    float bal_coef, int E_pad, bf16_t* __restrict__ dlog, float* __restrict__ dlb_part) {
+  __shared__ float colsum[4][256];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wave;
+  float dl[4] = {0.f, 0.f, 0.f, 0.f};
+  if (t < T) {                          // uniform across the wave
+    float lg[4];
+    bool live[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = lane + 64 * i;
+      live[i] = e < E;
+      lg[i] = live[i] ? sum_partials(part, KS, T, E16, t, e) + (logit_bias ? logit_bias[e] : 0.f)
+                      : -INFINITY;
+    }
+    const float m = wave_max_f(fmaxf(fmaxf(lg[0], lg[1]), fmaxf(lg[2], lg[3])));
+    float ex[4], loc = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      ex[i] = live[i] ? expf(lg[i] - m) : 0.f;
+      loc += ex[i];
+    }
+    const float inv = 1.0f / wave_sum_f(loc);
+    // slots
+    float dg = 0.f, gj = 0.f;
+    int ej = -1;
+    if (lane < k) {
+      const int asg = t * k + lane;
+      const int pos = assign_pos[asg];
+      if (pos >= 0)
+        for (int n = 0; n < NT; ++n) dg += dgate_part[(size_t)pos * NT + n];
+      gj = topk_w[asg];
+      ej = ids[asg];
+    }
+    const float inner = wave_sum_f(lane < k ? gj * dg : 0.f);
+    const float cj = gj * (dg - inner);
+    for (int j = 0; j < k; ++j) {
+      const int e = __builtin_amdgcn_readlane(ej, j);
+      const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cj), j));
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (lane + 64 * i == e) dl[i] += c;
+    }
+    if (bal_coef != 0.f) {
+      float w[4], pw = 0.f;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        w[i] = live[i] ? bal_coef * (float)counts_pre[lane + 64 * i] : 0.f;
+        pw += ex[i] * inv * w[i];
+      }
+      pw = wave_sum_f(pw);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dl[i] += ex[i] * inv * (w[i] - pw);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = lane + 64 * i;
+      if (e < E_pad) dlog[(size_t)t * E_pad + e] = f32_to_bf16(live[i] ? dl[i] : 0.f);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) colsum[wave][lane + 64 * i] = dl[i];
+  __syncthreads();
+  if (dlb_part)
+    for (int e = threadIdx.x; e < E; e += 256)
+      dlb_part[(size_t)blockIdx.x * E + e] =
+          ((colsum[0][e] + colsum[1][e]) + colsum[2][e]) + colsum[3][e];
+}
+
+// dx[t] = router share + shared expert's rows + the kept slots' rows in slot order.
+__global__ __launch_bounds__(256) void bwd_dx_kernel(const float* __restrict__ dx_router,
+                                                     const float* __restrict__ dx_shared,
+                                                     const float* __restrict__ dx_rows,
+                                                     const int32_t* __restrict__ assign_pos,
+                                                     int k, int d, float* __restrict__ dx) {
+  __shared__ int pos[16];
+  const int t = blockIdx.x;
+  if (threadIdx.x < k) pos[threadIdx.x] = assign_pos[(size_t)t * k + threadIdx.x];
+  __syncthreads();
+  const int d4 = d >> 2;
+  for (int c = threadIdx.x; c < d4; c += 256) {
+    f32x4 acc = *(const f32x4*)(dx_router + (size_t)t * d + 4 * c);
+    if (dx_shared) {
+      const f32x4 v = *(const f32x4*)(dx_shared + (size_t)t * d + 4 * c);
+      acc[0] += v[0];
+      acc[1] += v[1];
+      acc[2] += v[2];
+      acc[3] += v[3];
+    }
+    for (int j = 0; j < k; ++j) {
+      if (pos[j] < 0) continue;
+      const f32x4 v = *(const f32x4*)(dx_rows + (size_t)pos[j] * d + 4 * c);
+      acc[0] += v[0];
+      acc[1] += v[1];
+      acc[2] += v[2];
+      acc[3] += v[3];
+    }
+    *(f32x4*)(dx + (size_t)t * d + 4 * c) = acc;
+  }
+}
+
+template <int BN, int MODE, int AK, int BKIND, int EPI>
+hipError_t launch_gemm(const BwdArgs& a, int tiles, hipStream_t s) {
+  if (tiles <= 0) return hipSuccess;
+  hipLaunchKernelGGL((bwd_gemm_kernel<BN, MODE, AK, BKIND, EPI>), dim3((tiles + 7) / 8 * 8),
+                     dim3(512), 0, s, a);
+  return hipGetLastError();
+}
+
+// BN for an output width: 256 when it divides, else 128
+inline int bn_for(int n) { return n % 256 == 0 ? 256 : 128; }
+
+}  // namespace
+
+// ------------------------------------------------------------------ workspace
+BwdLayout backward_layout(const moe_problem& p) {
+  BwdLayout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t o = off;
+    off = align_up(off + (bytes ? bytes : 1), 256);
+    return o;
+  };
+  const size_t n = (size_t)p.T * p.k;
+  const int G = p.E + p.n_shared;
+  L.E_pad = ceil_div(p.E, 128) * 128;
+  L.max_mt = max_mtiles((long long)n, p.T, p.E, p.n_shared, BBM);
+  const size_t srows = (size_t)L.max_mt * BBM;
+  L.NT_down = p.d_ff / bn_for(p.d_ff);
+  L.nblk_router = ceil_div(p.T, 4);
+  L.grp_rows = take((size_t)G * 4);
+  L.grp_off = take((size_t)G * 4);
+  L.mt_start = take((size_t)(G + 1) * 4);
+  L.mt_group = take((size_t)L.max_mt * 4);
+  L.logits_part = take(route_partial_bytes(p));
+  L.dlb_part = take((size_t)L.nblk_router * p.E * 4);
+  L.zero = take(ZERO_ELEMS * 2);
+  L.H = take(srows * p.d_ff * 2);
+  L.U = take(srows * p.d_ff * 4);
+  L.V = take(srows * p.d_ff * 4);
+  L.DUV = take(srows * 2 * p.d_ff * 2);
+  L.DO = take(srows * p.d * 2);
+  L.XS = take(srows * p.d * 2);
+  L.dyb = take((size_t)p.T * p.d * 2);
+  L.dgate_part = take(n * L.NT_down * 4);
+  L.dx_rows = take(n * p.d * 4);
+  L.dx_shared = take((size_t)p.n_shared * p.T * p.d * 4);
+  L.dlog = take((size_t)p.T * L.E_pad * 2);
+  L.dx_router = take((size_t)p.T * p.d * 4);
+  L.total = off;
+  return L;
+}
+
+// ------------------------------------------------------------------ the pass
+hipError_t launch_backward(const moe_problem& p, const BwdLayout& L, void* ws, const void* x,
+                           const void* w_gate, const float* logit_bias, const void* w1,
+                           const void* w3, const void* w2, const void* ws1, const void* ws3,
+                           const void* ws2, const int32_t* topk_ids, const float* topk_w,
+                           const int32_t* counts_pre, const int32_t* offsets,
+                           const int32_t* sorted_assign, const int32_t* assign_pos,
+                           const float* dy, float alpha, float dL, float* dx, float* dw_gate,
+                           float* dlogit_bias, void* dw1, void* dw3, void* dw2, void* dws1,
+                           void* dws3, void* dws2, hipStream_t s) {
+  char* base = (char*)ws;
+  auto at = [&](size_t o) { return (void*)(base + o); };
+  const int G = p.E + p.n_shared;
+  Schedule sc;
+  sc.grp_rows = (int32_t*)at(L.grp_rows);
+  sc.grp_off = (int32_t*)at(L.grp_off);
+  sc.mt_start = (int32_t*)at(L.mt_start);
+  sc.mt_group = (int32_t*)at(L.mt_group);
+  sc.max_mtiles = L.max_mt;
+  sc.G = G;
+  sc.BM = BBM;
+  bf16_t* H = (bf16_t*)at(L.H);
+  float* U = (float*)at(L.U);
+  float* V = (float*)at(L.V);
+  bf16_t* DUV = (bf16_t*)at(L.DUV);
+  bf16_t* DO = (bf16_t*)at(L.DO);
+  bf16_t* XS = (bf16_t*)at(L.XS);
+  bf16_t* dyb = (bf16_t*)at(L.dyb);
+  bf16_t* zero = (bf16_t*)at(L.zero);
+  float* dgate_part = (float*)at(L.dgate_part);
+  float* dx_rows = (float*)at(L.dx_rows);
+  float* dx_shared = p.n_shared ? (float*)at(L.dx_shared) : nullptr;
+  bf16_t* dlog = (bf16_t*)at(L.dlog);
+  float* dx_router = (float*)at(L.dx_router);
+  float* logits_part = (float*)at(L.logits_part);
+  float* dlb_part = (float*)at(L.dlb_part);
+
+  hipError_t err;
+#define MOE_TRY(call)                  \
+  do {                                 \
+    if ((err = (call)) != hipSuccess) \
+      return err;                      \
+  } while (0)
+  // 1. schedule (128-row m-tiles) and the gate-up recompute (h, u, v in storage rows)
+  MOE_TRY(launch_schedule(p, offsets, sc, s));
+  MOE_TRY(launch_expert_ffn(p, x, w1, w3, w2, ws1, ws3, ws2, sorted_assign, sc, H, nullptr,
+                            nullptr, nullptr, s, nullptr, 0, U, V));
+  // 2. dy in bf16, g dy and the gathered x rows in storage rows
+  hipLaunchKernelGGL(bwd_prep_kernel, dim3(std::min(p.T + L.max_mt * BBM, 16384)), dim3(256), 0,
+                     s, dy, (const bf16_t*)x, sorted_assign, topk_w, sc, p.T, p.d, p.k, p.E, dyb,
+                     DO, XS, zero);
+  MOE_TRY(hipGetLastError());
+
+  BwdArgs c{};
+  c.E = p.E;
+  c.k = p.k;
+  c.T = p.T;
+  c.sorted_assign = sorted_assign;
+  c.sc = sc;
+  c.zero = zero;
+  const int mt_max = L.max_mt;
+  // 3. dgrad-down + SwiGLU backward: d h' = dy_t W2, then du, dv, d g partials
+  {
+    BwdArgs a = c;
+    a.A = dyb;
+    a.lda = p.d;
+    a.B0 = (const bf16_t*)w2;
+    a.S0 = (const bf16_t*)ws2;
+    a.ldb = p.d_ff;
+    a.M = 0;
+    a.N = p.d_ff;
+    a.K = p.d;
+    a.U = U;
+    a.V = V;
+    a.topk_w = topk_w;
+    a.DUV = DUV;
+    a.dgate_part = dgate_part;
+    a.NT = L.NT_down;
+    const int tiles = mt_max * L.NT_down;
+    err = (L.NT_down * 256 == p.d_ff) ? launch_gemm<256, M_ROWS, A_TOKEN, B_W2, EPI_DDOWN>(a, tiles, s)
+                             : launch_gemm<128, M_ROWS, A_TOKEN, B_W2, EPI_DDOWN>(a, tiles, s);
+    MOE_TRY(err);
+  }
+  // 4. dgrad-x: (du | dv) (W1; W3) -> per-row dx (sorted order) and the shared rows
+  {
+    BwdArgs a = c;
+    a.A = DUV;
+    a.lda = 2 * p.d_ff;
+    a.B0 = (const bf16_t*)w1;
+    a.B1 = (const bf16_t*)w3;
+    a.S0 = (const bf16_t*)ws1;
+    a.S1 = (const bf16_t*)ws3;
+    a.ldb = p.d;
+    a.N = p.d;
+    a.K = 2 * p.d_ff;
+    a.out = dx_rows;
+    a.out_shared = dx_shared;
+    const int bn = bn_for(p.d);
+    const int tiles = mt_max * (p.d / bn);
+    err = (bn == 256) ? launch_gemm<256, M_ROWS, A_STORE, B_W13, EPI_ROWS>(a, tiles, s)
+                             : launch_gemm<128, M_ROWS, A_STORE, B_W13, EPI_ROWS>(a, tiles, s);
+    MOE_TRY(err);
+  }
+  // 5. wgrad-down: dW2_g = (g dy)^T h over the group's rows
+  {
+    BwdArgs a = c;
+    a.A = DO;
+    a.lda = p.d;
+    a.B0 = H;
+    a.ldb = p.d_ff;
+    a.M = p.d;
+    a.N = p.d_ff;
+    a.W0 = (bf16_t*)dw2;
+    a.SW0 = (bf16_t*)dws2;
+    a.Msplit = p.d;
+    const int bn = bn_for(p.d_ff);
+    const int tiles = G * (p.d / BBM) * (p.d_ff / bn);
+    err = (bn == 256) ? launch_gemm<256, M_WEIGHTS, AT_STORE, BT_STORE, EPI_WBF16>(a, tiles, s)
+                             : launch_gemm<128, M_WEIGHTS, AT_STORE, BT_STORE, EPI_WBF16>(a, tiles, s);
+    MOE_TRY(err);
+  }
+  // 6. wgrad-up: (dW1_g; dW3_g) = (du | dv)^T x_rows
+  {
+    BwdArgs a = c;
+    a.A = DUV;
+    a.lda = 2 * p.d_ff;
+    a.B0 = XS;
+    a.ldb = p.d;
+    a.M = 2 * p.d_ff;
+    a.N = p.d;
+    a.W0 = (bf16_t*)dw1;
+    a.W1 = (bf16_t*)dw3;
+    a.SW0 = (bf16_t*)dws1;
+    a.SW1 = (bf16_t*)dws3;
+    a.Msplit = p.d_ff;
+    const int bn = bn_for(p.d);
+    const int tiles = G * (2 * p.d_ff / BBM) * (p.d / bn);
+    err = (bn == 256) ? launch_gemm<256, M_WEIGHTS, AT_STORE, BT_STORE, EPI_WBF16>(a, tiles, s)
+                             : launch_gemm<128, M_WEIGHTS, AT_STORE, BT_STORE, EPI_WBF16>(a, tiles, s);
+    MOE_TRY(err);
+  }
+  // 7. router: logits again, then d l per token (gates + balance), then its column sums
+  if (p.T > 0) {
+    MOE_TRY(launch_route_logits(p, x, w_gate, logits_part, s));
+    const float coef = dL * alpha * (float)p.E / ((float)p.T * (float)p.k * (float)p.T);
+    hipLaunchKernelGGL(bwd_router_kernel, dim3(L.nblk_router), dim3(256), 0, s, logits_part,
+                       route_ksplit(p), p.T, p.E, ceil_div(p.E, 16) * 16, p.k, logit_bias,
+                       topk_ids, topk_w, assign_pos, dgate_part, L.NT_down, counts_pre, coef,
+                       L.E_pad, dlog, dlogit_bias ? dlb_part : nullptr);
+    MOE_TRY(hipGetLastError());
+  }
+  if (dlogit_bias) MOE_TRY(launch_psum_reduce(dlb_part, p.T > 0 ? L.nblk_router : 0, p.E, dlogit_bias, s));
+  // 8. router dgrad: dx_router = d l W_gate (K = E_pad; rows of W_gate past E read zeros)
+  {
+    BwdArgs a = c;
+    a.A = dlog;
+    a.lda = L.E_pad;
+    a.B0 = (const bf16_t*)w_gate;
+    a.ldb = p.d;
+    a.N = p.d;
+    a.K = L.E_pad;
+    a.Kvalid = p.E;
+    a.ident = 1;
+    a.ident_rows = p.T;
+    a.out = dx_router;
+    const int bn = bn_for(p.d);
+    const int tiles = ceil_div(p.T, BBM) * (p.d / bn);
+    err = (bn == 256) ? launch_gemm<256, M_ROWS, A_IDENT, B_WGATE, EPI_ROWS>(a, tiles, s)
+                             : launch_gemm<128, M_ROWS, A_IDENT, B_WGATE, EPI_ROWS>(a, tiles, s);
+    MOE_TRY(err);
+  }
+  // 9. router wgrad: dW_gate = d l^T x (K = T)
+  {
+    BwdArgs a = c;
+    a.A = dlog;
+    a.lda = L.E_pad;
+    a.B0 = (const bf16_t*)x;
+    a.ldb = p.d;
+    a.M = L.E_pad;
+    a.N = p.d;
+    a.ident = 1;
+    a.ident_rows = p.T;
+    a.Wf = dw_gate;
+    a.Mvalid = p.E;
+    const int bn = bn_for(p.d);
+    const int tiles = (L.E_pad / BBM) * (p.d / bn);
+    // (T = 0: the K loop is empty and every tile writes zeros)
+    err = (bn == 256) ? launch_gemm<256, M_WEIGHTS, AT_IDENT, BT_IDENT, EPI_WF32>(a, tiles, s)
+                             : launch_gemm<128, M_WEIGHTS, AT_IDENT, BT_IDENT, EPI_WF32>(a, tiles, s);
+    MOE_TRY(err);
+  }
+  // 10. dx
+  if (p.T > 0) {
+    hipLaunchKernelGGL(bwd_dx_kernel, dim3(p.T), dim3(256), 0, s, dx_router, dx_shared, dx_rows,
+                       assign_pos, p.k, p.d, dx);
+    MOE_TRY(hipGetLastError());
+  }
+#undef MOE_TRY
+  return hipSuccess;
+}
+
+}  // namespace moe

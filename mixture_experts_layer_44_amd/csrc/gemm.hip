@@ -47,16 +47,11 @@
 #include <type_traits>
 
 #include "moe_internal.h"
+#include "mfma_tiles.h"
 
 namespace moe {
 
 namespace {
-
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-// s_waitcnt immediate that waits until at most n vector-memory ops are outstanding
-// (expcnt and lgkmcnt left unconstrained)
-constexpr int wait_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 
 struct GemmArgs {
   const bf16_t* A;      // gate-up: x [T,K]; down: H [mtiles*BM, K]
@@ -72,52 +67,9 @@ struct GemmArgs {
   float* shared_out;    // down output, shared rows (token order)
   float* out_rows_b;    // down with K split in two: the second half's routed rows
   int ksplit;           // 1, or 2 for the down GEMM (routed groups only, no shared expert)
+  float* U;             // gate-up, or null: also store u and v (fp32, in H's row layout)
+  float* V;
 };
-
-struct TileCoord {
-  int g, m_local, n0, mt_global, rows, off;
-};
-
-// Tile for this workgroup, or false if it has none. Uniform across the workgroup.
-__device__ __forceinline__ bool tile_coord(const Schedule& sc, int NT, int bn, TileCoord& tc,
-                                           int S = 1, int* half = nullptr) {
-  const int total = sc.mt_start[sc.G] * NT;
-  const int bid = blockIdx.x;
-  const int xcd = bid & 7, slot = bid >> 3;
-  const int per = (total * S + 7) >> 3;
-  if (slot >= per) return false;
-  int L = xcd * per + slot;
-  if (L >= total * S) return false;
-  if (half) *half = L / total;   // work unit L = half * total + tile
-  L %= total;
-  const int g = sc.mt_group[L / NT];
-  const int ms = sc.mt_start[g];
-  const int mtg = sc.mt_start[g + 1] - ms;
-  const int lp = L - ms * NT;
-  const int n_tile = lp / mtg;
-  tc.g = g;
-  tc.m_local = lp - n_tile * mtg;
-  tc.n0 = n_tile * bn;
-  tc.mt_global = ms + tc.m_local;
-  tc.rows = sc.grp_rows[g];
-  tc.off = sc.grp_off[g];
-  return true;
-}
-
-// SiLU(u) = u * sigmoid(u) with the hardware exp and reciprocal (a few ulp; the result is
-// rounded to bf16 right after). exp(-u) overflows to inf for u < -88: u * rcp(inf) = -0.
-__device__ __forceinline__ float silu_f(float u) {
-  return u * __builtin_amdgcn_rcpf(1.0f + __expf(-u));
-}
-
-// Element offset of (row, 16-byte chunk) in a swizzled [rows][BK] bf16 stage. A 256-byte
-// LDS cycle spans W = 128/BK rows; chunk c of row r goes to slot c ^ ((r / W) % (BK/8)), so
-// 16 consecutive rows read at one logical chunk hit 16 distinct 16-byte bank groups.
-template <int BK>
-__device__ __forceinline__ int swz(int r, int c) {
-  constexpr int CH = BK / 8, W = 128 / BK;
-  return r * BK + ((c ^ ((r / W) & (CH - 1))) << 3);
-}
 
 template <int BM, int BNB, int WM, int WN, int BK, int STAGES, bool GATEUP>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs args) {
@@ -274,7 +226,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs args) 
         if (GATEUP) {
           const float u = acc[i][j][r];
           const float v = acc[i][j + FN / 2][r];
-          args.H[(size_t)(tc.mt_global * BM + lr) * N + col] = f32_to_bf16(silu_f(u) * v);
+          const size_t o = (size_t)(tc.mt_global * BM + lr) * N + col;
+          args.H[o] = f32_to_bf16(silu_f(u) * v);
+          if (args.U) {
+            args.U[o] = u;
+            args.V[o] = v;
+          }
         } else {
           const int rg = tc.m_local * BM + lr;
           if (rg < tc.rows) {
@@ -511,7 +468,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_st_kernel(GemmArgs arg
           if (lr < rows_here) {          // padding rows of H feed only padding rows of the down
             const float u = acc[i][j][r];
             const float v = acc[i][j + FN / 2][r];
-            args.H[(size_t)(tc.mt_global * BM + lr) * N + col] = f32_to_bf16(silu_f(u) * v);
+            const size_t o = (size_t)(tc.mt_global * BM + lr) * N + col;
+            args.H[o] = f32_to_bf16(silu_f(u) * v);
+            if (args.U) {
+              args.U[o] = u;
+              args.V[o] = v;
+            }
           }
         } else {
           const int rg = tc.m_local * BM + lr;
@@ -683,13 +645,13 @@ bool gemm_small(const moe_problem& p) { return p.dtype == MOE_BF16 && expected_r
 
 template <int BM, int BNB_UP, int WM_UP, int WN_UP, int BNB_DN, int WM_DN, int WN_DN, int BK, int ST>
 hipError_t launch_bf16(const moe_problem& p, const GemmArgs& a, const GemmArgs& b, hipStream_t s,
-                       hipEvent_t between) {
+                       hipEvent_t between, bool up_only) {
   if (p.d_ff % (BNB_UP / 2) || p.d % BNB_DN) return hipErrorInvalidValue;   // n-tiles cover N
   hipLaunchKernelGGL((gemm_bf16_kernel<BM, BNB_UP, WM_UP, WN_UP, BK, ST, true>),
                      dim3(grid_for(a.sc.max_mtiles, p.d_ff / (BNB_UP / 2))), dim3(WM_UP * WN_UP * 64),
                      0, s, a);
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  if (err != hipSuccess || up_only) return err;
   if (between && (err = hipEventRecord(between, s)) != hipSuccess) return err;
   hipLaunchKernelGGL((gemm_bf16_kernel<BM, BNB_DN, WM_DN, WN_DN, BK, ST, false>),
                      dim3(grid_for(b.sc.max_mtiles, p.d / BNB_DN)), dim3(WM_DN * WN_DN * 64), 0, s,
@@ -699,13 +661,13 @@ hipError_t launch_bf16(const moe_problem& p, const GemmArgs& a, const GemmArgs& 
 
 template <int BM, int BNB_UP, int WM_UP, int WN_UP, int BNB_DN, int WM_DN, int WN_DN, bool DEEPB>
 hipError_t launch_bf16_st(const moe_problem& p, const GemmArgs& a, const GemmArgs& b,
-                          hipStream_t s, hipEvent_t between) {
+                          hipStream_t s, hipEvent_t between, bool up_only) {
   if (p.d_ff % (BNB_UP / 2) || p.d % BNB_DN) return hipErrorInvalidValue;   // n-tiles cover N
   hipLaunchKernelGGL((gemm_bf16_st_kernel<BM, BNB_UP, WM_UP, WN_UP, true, DEEPB>),
                      dim3(grid_for(a.sc.max_mtiles, p.d_ff / (BNB_UP / 2))), dim3(WM_UP * WN_UP * 64),
                      0, s, a);
   hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  if (err != hipSuccess || up_only) return err;
   if (between && (err = hipEventRecord(between, s)) != hipSuccess) return err;
   hipLaunchKernelGGL((gemm_bf16_st_kernel<BM, BNB_DN, WM_DN, WN_DN, false, DEEPB>),
                      dim3(grid_for(b.sc.max_mtiles * b.ksplit, p.d / BNB_DN)),
@@ -717,7 +679,8 @@ hipError_t launch_expert_ffn(const moe_problem& p, const void* x, const void* w1
                              const void* w2, const void* ws1, const void* ws3, const void* ws2,
                              const int32_t* sorted_assign, const Schedule& sc, void* h,
                              float* out_rows, float* out_rows_b, float* shared_out, hipStream_t s,
-                             hipEvent_t between, int row_div) {
+                             hipEvent_t between, int row_div, float* U, float* V) {
+  const bool up_only = U != nullptr;   // the backward's recompute: gate-up with u and v kept
   const int kdiv = row_div > 0 ? row_div : p.k;
   if (p.dtype == MOE_BF16) {
     GemmArgs a{};
@@ -734,6 +697,8 @@ hipError_t launch_expert_ffn(const moe_problem& p, const void* x, const void* w1
     a.sorted_assign = sorted_assign;
     a.sc = sc;
     a.H = (bf16_t*)h;
+    a.U = U;
+    a.V = V;
     GemmArgs b{};
     b.A = (const bf16_t*)h;
     b.B0 = (const bf16_t*)w2;
@@ -750,16 +715,17 @@ hipError_t launch_expert_ffn(const moe_problem& p, const void* x, const void* w1
     a.ksplit = 1;
     b.ksplit = down_ksplit(p);
     b.out_rows_b = out_rows_b;
-    if (b.ksplit == 2 && !out_rows_b) return hipErrorInvalidValue;
+    if (!up_only && b.ksplit == 2 && !out_rows_b) return hipErrorInvalidValue;
     if (sc.BM == 256 && gemm_wide(p))
-      return launch_bf16_st<256, 256, 4, 2, 256, 4, 2, false>(p, a, b, s, between);
-    if (sc.BM == 256) return launch_bf16_st<256, 256, 4, 2, 256, 4, 2, true>(p, a, b, s, between);
-    if (sc.BM == 192) return launch_bf16_st<192, 256, 2, 4, 256, 2, 4, true>(p, a, b, s, between);
-    if (sc.BM == 32) return launch_bf16<32, 256, 1, 4, 128, 1, 4, 64, 4>(p, a, b, s, between);
+      return launch_bf16_st<256, 256, 4, 2, 256, 4, 2, false>(p, a, b, s, between, up_only);
+    if (sc.BM == 256) return launch_bf16_st<256, 256, 4, 2, 256, 4, 2, true>(p, a, b, s, between, up_only);
+    if (sc.BM == 192) return launch_bf16_st<192, 256, 2, 4, 256, 2, 4, true>(p, a, b, s, between, up_only);
+    if (sc.BM == 32) return launch_bf16<32, 256, 1, 4, 128, 1, 4, 64, 4>(p, a, b, s, between, up_only);
     // down tiles of 256 output features need d % 256 == 0 (the entry points accept d % 128)
-    if (p.d % 256 == 0) return launch_bf16_st<128, 256, 2, 4, 256, 2, 4, true>(p, a, b, s, between);
-    return launch_bf16<128, 256, 2, 4, 128, 2, 4, 64, 3>(p, a, b, s, between);
+    if (p.d % 256 == 0) return launch_bf16_st<128, 256, 2, 4, 256, 2, 4, true>(p, a, b, s, between, up_only);
+    return launch_bf16<128, 256, 2, 4, 128, 2, 4, 64, 3>(p, a, b, s, between, up_only);
   }
+  if (up_only) return hipErrorInvalidValue;   // the backward runs on bf16 storage only
   GemmArgs32 a{};
   a.A = (const float*)x;
   a.B0 = (const float*)w1;

@@ -103,11 +103,14 @@ int down_ksplit(const moe_problem& p);
 
 // out_rows_b: [T*k, d] second-half partial rows, required when down_ksplit(p) == 2.
 // row_div: a routed row r gathers token sorted_assign[r] / row_div (0: k).
+// U, V (bf16 storage only): when given, only the gate-up GEMM runs, and it also stores u and v
+// in fp32 in H's row layout (the backward's recompute).
 hipError_t launch_expert_ffn(const moe_problem& p, const void* x, const void* w1, const void* w3,
                              const void* w2, const void* ws1, const void* ws3, const void* ws2,
                              const int32_t* sorted_assign, const Schedule& sc, void* h,
                              float* out_rows, float* out_rows_b, float* shared_out, hipStream_t s,
-                             hipEvent_t between = nullptr, int row_div = 0);
+                             hipEvent_t between = nullptr, int row_div = 0, float* U = nullptr,
+                             float* V = nullptr);
 
 // out_rows_b may be null; when given, each expert row is out_rows + out_rows_b
 hipError_t launch_combine(const moe_problem& p, const float* out_rows, const float* out_rows_b,
@@ -140,5 +143,24 @@ hipError_t launch_ec_combine(const moe_problem& p, const int32_t* pos_table, con
 
 hipError_t launch_bias_update(const moe_problem& p, const int32_t* counts_pre, float gamma,
                               float* sel_bias, hipStream_t s);
+
+// ---------------------------------------------------------------- backward
+// Workspace of the layer backward (byte offsets; bf16 storage only).
+struct BwdLayout {
+  size_t grp_rows, grp_off, mt_start, mt_group, logits_part, dlb_part, zero;
+  size_t H, U, V, DUV, DO, XS, dyb, dgate_part, dx_rows, dx_shared, dlog, dx_router;
+  size_t total;
+  int max_mt, E_pad, NT_down, nblk_router;
+};
+BwdLayout backward_layout(const moe_problem& p);
+hipError_t launch_backward(const moe_problem& p, const BwdLayout& L, void* ws, const void* x,
+                           const void* w_gate, const float* logit_bias, const void* w1,
+                           const void* w3, const void* w2, const void* ws1, const void* ws3,
+                           const void* ws2, const int32_t* topk_ids, const float* topk_w,
+                           const int32_t* counts_pre, const int32_t* offsets,
+                           const int32_t* sorted_assign, const int32_t* assign_pos,
+                           const float* dy, float alpha, float dL, float* dx, float* dw_gate,
+                           float* dlogit_bias, void* dw1, void* dw3, void* dw2, void* dws1,
+                           void* dws3, void* dws2, hipStream_t s);
 
 }  // namespace moe

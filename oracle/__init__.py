@@ -1,4 +1,4 @@
-"""fp64 CPU oracle for the sparse MoE layer forward -- test infrastructure only.
+"""fp64 CPU oracle for the sparse MoE layer (forward and backward) -- test infrastructure only.
 
 Only the tests, the smoke check and the benchmark's CPU-baseline leg import
 this package; the product path never does.

@@ -1,0 +1,158 @@
+"""Layer backward on the GPU (moe_backward, through the C ABI) against the fp64 oracle.
+
+Both sides differentiate the same selection: the GPU forward's top-k ids are handed to the
+oracle (the selection has no gradient, and near-ties are the forward tests' business).
+
+Tolerance. The HIP path rounds dy, g*dy, du, dv and the router's logit gradient to bf16
+before its MFMA products (fp32 accumulation), and writes the expert weight gradients in
+bf16; each rounding is a relative error of at most 2^-9 per element, and the products over
+K terms of random sign keep a normwise error of the same order. Every gradient tensor must
+be within 1e-2 relative Frobenius error of the oracle's, and no element may be off by more
+than 3e-2 of the tensor's largest magnitude."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads
+from util import f64
+
+pytestmark = pytest.mark.gpu
+
+W = workloads.Workload
+REL_F = 1e-2
+REL_MAX = 3e-2
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _dy(w, scale=1.0):
+    g = torch.Generator()
+    g.manual_seed(workloads.tensor_seed(w.seed, "x", 7))
+    return (torch.randn((w.T, w.d), generator=g, dtype=torch.float32) * scale)
+
+
+def _compare(name, got, ref):
+    got = f64(got)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (name, got.shape, ref.shape)
+    if ref.size == 0:
+        return 0.0, 0.0
+    scale = np.abs(ref).max()
+    err = np.abs(got - ref)
+    den = np.linalg.norm(ref)
+    relf = float(np.linalg.norm(got - ref) / den) if den > 0 else float(np.linalg.norm(got))
+    relmax = float(err.max() / scale) if scale > 0 else float(err.max())
+    assert np.isfinite(got).all(), f"{name}: non-finite values"
+    if den > 0:
+        assert relf <= REL_F, f"{name}: relative Frobenius error {relf:.3e} > {REL_F}"
+        assert relmax <= REL_MAX, f"{name}: max error {relmax:.3e} of max|ref| > {REL_MAX}"
+    else:
+        assert err.max() == 0.0, f"{name}: expected exact zeros"
+    return relf, relmax
+
+
+def run_backward(w, alpha=0.01, dL=1.0, dy_scale=1.0):
+    import mixture_experts_layer_44_amd as moe
+    inp = workloads.generate(w)
+    g = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
+    p = moe.problem_for(w)
+    y, r = moe.forward(p, g["x"], g["w_gate"], g["w1"], g["w3"], g["w2"],
+                       logit_bias=g["logit_bias"], sel_bias=g["sel_bias"], ws1=g["ws1"],
+                       ws3=g["ws3"], ws2=g["ws2"], return_routing=True)
+    dy = _dy(w, dy_scale)
+    grads = moe.backward(p, g["x"], g["w_gate"], g["w1"], g["w3"], g["w2"], r, dy.cuda(),
+                         logit_bias=g["logit_bias"], ws1=g["ws1"], ws3=g["ws3"], ws2=g["ws2"],
+                         alpha=alpha, dL=dL, want_dlogit_bias=True)
+    torch.cuda.synchronize()
+    ids = r["topk_ids"].cpu().numpy().astype(np.int64)
+    shared = [] if not w.n_shared else [(f64(inp["ws1"][0]), f64(inp["ws3"][0]), f64(inp["ws2"][0]))]
+    ref = O.moe_backward(f64(inp["x"]), f64(inp["w_gate"]),
+                         O.expert_table(f64(inp["w1"]), f64(inp["w3"]), f64(inp["w2"])), w.E, w.k,
+                         f64(dy), f64(inp["logit_bias"]), None, shared, w.capacity_factor, ids=ids,
+                         alpha=alpha, dL=dL)
+    return grads, ref, r
+
+
+CASES = [
+    W("bwd_basic", T=300, d=256, E=16, k=4, d_ff=384, seed=501),
+    W("bwd_shared_sel_cap", T=257, d=384, E=32, k=8, d_ff=256, seed=502, n_shared=1,
+      d_ff_shared=256, sel_bias=True, capacity_factor=1.0),
+    W("bwd_zipf_cap", T=500, d=256, E=16, k=2, d_ff=256, seed=503, capacity_factor=1.0, zipf_s=1.1),
+    W("bwd_E1", T=200, d=256, E=1, k=1, d_ff=512, seed=504),
+    W("bwd_many_small", T=600, d=256, E=128, k=8, d_ff=256, seed=505, n_shared=1,
+      d_ff_shared=256, sel_bias=True),
+    W("bwd_E256", T=64, d=256, E=256, k=8, d_ff=128, seed=506),
+    W("bwd_long_segments", T=1600, d=512, E=4, k=2, d_ff=384, seed=507, n_shared=1,
+      d_ff_shared=384),
+    W("bwd_k_eq_E", T=100, d=128, E=8, k=8, d_ff=128, seed=508),
+]
+
+
+@pytest.mark.parametrize("w", CASES, ids=[w.name for w in CASES])
+def test_backward_parity(w):
+    _say(f"[backward] {w}")
+    grads, ref, r = run_backward(w)
+    report = {}
+    for name in ("dx", "dw_gate", "dlogit_bias", "dw1", "dw3", "dw2"):
+        report[name] = _compare(name, grads[name], ref[name])
+    if w.n_shared:
+        for m, name in enumerate(("dws1", "dws3", "dws2")):
+            report[name] = _compare(name, grads[name][0], ref["dshared"][0][m])
+    _say(f"{w.name}: " + ", ".join(f"{k}=({a:.1e},{b:.1e})" for k, (a, b) in report.items()))
+    if w.capacity_factor:
+        assert (r["assign_pos"][: w.T * w.k] < 0).any()
+
+
+def test_backward_balance_term_only():
+    """dy = 0: only the balance loss drives the router; the expert weights get exactly zero."""
+    w = W("bwd_balance_only", T=400, d=256, E=16, k=2, d_ff=256, seed=509, zipf_s=1.1,
+          capacity_factor=1.25)
+    grads, ref, _ = run_backward(w, alpha=0.01, dL=50.0, dy_scale=0.0)
+    for name in ("dx", "dw_gate", "dlogit_bias"):
+        _compare(name, grads[name], ref[name])
+    for name in ("dw1", "dw3", "dw2"):
+        assert torch.count_nonzero(grads[name]).item() == 0, name
+    assert np.abs(ref["dw_gate"]).max() > 0
+
+
+def test_backward_empty_batch():
+    """T = 0: every weight gradient is exactly zero."""
+    import mixture_experts_layer_44_amd as moe
+    w = W("bwd_empty", T=0, d=256, E=8, k=2, d_ff=256, seed=510, n_shared=1, d_ff_shared=256)
+    inp = {k: (None if v is None else v.cuda()) for k, v in workloads.generate(w).items()}
+    p = moe.problem_for(w)
+    y, r = moe.forward(p, inp["x"], inp["w_gate"], inp["w1"], inp["w3"], inp["w2"], ws1=inp["ws1"],
+                       ws3=inp["ws3"], ws2=inp["ws2"], return_routing=True)
+    grads = moe.backward(p, inp["x"], inp["w_gate"], inp["w1"], inp["w3"], inp["w2"], r,
+                         torch.zeros((0, w.d), device="cuda"), ws1=inp["ws1"], ws3=inp["ws3"],
+                         ws2=inp["ws2"], want_dlogit_bias=True,
+                         out={n: torch.full(s, 7.0, device="cuda", dtype=dt) for n, s, dt in (
+                             ("dw_gate", (w.E, w.d), torch.float32),
+                             ("dw1", (w.E, w.d_ff, w.d), torch.bfloat16),
+                             ("dws2", (1, w.d, w.d_ff), torch.bfloat16))})
+    torch.cuda.synchronize()
+    for name in ("dw_gate", "dlogit_bias", "dw1", "dw3", "dw2", "dws1", "dws3", "dws2"):
+        assert torch.count_nonzero(grads[name]).item() == 0, name
+
+
+def test_backward_deterministic():
+    """Two runs give the same bits (no atomics anywhere in the backward)."""
+    import mixture_experts_layer_44_amd as moe
+    w = CASES[1]
+    inp = {k: (None if v is None else v.cuda()) for k, v in workloads.generate(w).items()}
+    p = moe.problem_for(w)
+    _, r = moe.forward(p, inp["x"], inp["w_gate"], inp["w1"], inp["w3"], inp["w2"],
+                       sel_bias=inp["sel_bias"], ws1=inp["ws1"], ws3=inp["ws3"], ws2=inp["ws2"],
+                       return_routing=True)
+    dy = _dy(w).cuda()
+    outs = [moe.backward(p, inp["x"], inp["w_gate"], inp["w1"], inp["w3"], inp["w2"], r, dy,
+                         ws1=inp["ws1"], ws3=inp["ws3"], ws2=inp["ws2"], dL=1.0) for _ in range(2)]
+    torch.cuda.synchronize()
+    for name in outs[0]:
+        assert torch.equal(outs[0][name], outs[1][name]), name

@@ -267,6 +267,131 @@ def bench_expert_choice(args, w, p, g, kw, y, torch, moe):
 
 
 # ----------------------------------------------------------------------------- main
+def backward_stage_work(w, counts, stage, T=None):
+    """Algorithmic flops and bytes of one stage of the layer backward (bf16 storage).
+
+    rows = kept routed rows + the shared expert's T rows; groups = touched experts (+ shared);
+    every expert's weight gradient is written (zeros for an untouched one). Each distinct
+    input is counted once, each output once; padding, staging copies and re-reads are not.
+      recompute  4 d d_ff / row;  x, W1 and W3 of each group;  h (bf16) and u, v (fp32) rows
+      dgrad_down 2 d d_ff / row;  dy (bf16, per token), W2 per group, u, v;  du|dv (bf16)
+      dgrad_x    4 d d_ff / row;  du|dv, W1 and W3 per group;  fp32 output rows
+      wgrad_down 2 d d_ff / row;  g dy and h rows;  dW2 of every expert (bf16)
+      wgrad_up   4 d d_ff / row;  du|dv and x rows;  dW1 and dW3 of every expert (bf16)
+      router_dgrad / router_wgrad  2 T E d each;  d l (bf16) + W_gate or x;  fp32 output"""
+    T = w.T if T is None else T
+    kept = int(sum(counts))
+    touched = int(sum(1 for c in counts if c > 0))
+    rows = kept + T * w.n_shared
+    groups = touched + w.n_shared
+    G = w.E + w.n_shared
+    d, f = w.d, w.d_ff
+    wmat = d * f * 2
+    if stage == "recompute":
+        return dict(flops=4 * d * f * rows, bytes=T * d * 2 + 2 * wmat * groups + rows * f * 10)
+    if stage == "dgrad_down":
+        return dict(flops=2 * d * f * rows,
+                    bytes=T * d * 2 + wmat * groups + rows * f * 8 + rows * 2 * f * 2)
+    if stage == "dgrad_x":
+        return dict(flops=4 * d * f * rows,
+                    bytes=rows * 2 * f * 2 + 2 * wmat * groups + rows * d * 4)
+    if stage == "wgrad_down":
+        return dict(flops=2 * d * f * rows, bytes=rows * (d + f) * 2 + wmat * G)
+    if stage == "wgrad_up":
+        return dict(flops=4 * d * f * rows, bytes=rows * (2 * f + d) * 2 + 2 * wmat * G)
+    if stage in ("router_dgrad", "router_wgrad"):
+        return dict(flops=2 * T * w.E * d, bytes=T * w.E * 2 + T * d * 2 + w.E * d * 2 + T * d * 4)
+    raise ValueError(stage)
+
+
+def bench_backward(args, w, p, g, kw, y, torch, moe):
+    """Time moe_backward over the resident batch: K calls between two synchronisations, then
+    a second pass of K staged calls for the per-stage times and the dominant kernel."""
+    dev = y.device
+    _, r = moe.forward(p, g["x"], g["w_gate"], g["w1"], g["w3"], g["w2"], return_routing=True, y=y,
+                       **kw)
+    counts = r["counts"].cpu().tolist()
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4401)
+    dy = torch.randn((w.T, w.d), generator=gen, device=dev, dtype=torch.float32)
+    bw = dict(logit_bias=kw["logit_bias"], ws1=kw["ws1"], ws3=kw["ws3"], ws2=kw["ws2"],
+              alpha=0.01, dL=1.0, want_dlogit_bias=True)
+    bws = torch.empty(moe.backward_workspace_bytes(p), dtype=torch.uint8, device=dev)
+    out = moe.backward(p, g["x"], g["w_gate"], g["w1"], g["w3"], g["w2"], r, dy, ws=bws, **bw)
+    torch.cuda.synchronize()
+    for _ in range(args.warmup):
+        moe.backward(p, g["x"], g["w_gate"], g["w1"], g["w3"], g["w2"], r, dy, ws=bws, out=out, **bw)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        moe.backward(p, g["x"], g["w_gate"], g["w1"], g["w3"], g["w2"], r, dy, ws=bws, out=out, **bw)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms = elapsed * 1e3 / args.steps
+    for name, t in out.items():
+        assert torch.isfinite(t.float()).all().item(), name
+
+    n_ev = len(moe.BWD_STAGES) + 1
+    stream = torch.cuda.current_stream(dev)
+    events = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
+    for evs in events:
+        for e in evs:
+            e.record(stream)
+    torch.cuda.synchronize()
+    for s_ in range(args.steps):
+        moe.backward(p, g["x"], g["w_gate"], g["w1"], g["w3"], g["w2"], r, dy, ws=bws, out=out,
+                     events=[e.cuda_event for e in events[s_]], **bw)
+    torch.cuda.synchronize()
+    stage_ms = {}
+    for i, name in enumerate(moe.BWD_STAGES):
+        vals = [events[s][i].elapsed_time(events[s][i + 1]) for s in range(args.steps)]
+        stage_ms[name] = sum(vals) / len(vals)
+    log("[bench] backward stage ms: " + ", ".join(f"{k}={v:.4f}" for k, v in stage_ms.items()))
+    log(f"[bench] backward {ms:.4f} ms/step, {w.T / (ms * 1e-3):,.0f} tokens/s "
+        f"(stage-event pass: {sum(stage_ms.values()):.4f} ms/step)")
+
+    gemms = ("recompute", "dgrad_down", "dgrad_x", "wgrad_down", "wgrad_up")
+    dom = max(gemms, key=lambda s: stage_ms[s])
+    kwk = backward_stage_work(w, counts, dom)
+    t_dom = stage_ms[dom] * 1e-3
+    if kwk["flops"] / kwk["bytes"] >= RIDGE:
+        roof = {"bound": "mfma", "achieved": kwk["flops"] / t_dom / 1e12, "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s"}
+    else:
+        roof = {"bound": "hbm", "achieved": kwk["bytes"] / t_dom / 1e9, "peak": PEAK_HBM_GBS,
+                "unit": "GB/s"}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = f"bwd_gemm_kernel ({dom})" if dom != "recompute" else "gate-up recompute"
+    roof["launch_stream"] = "torch current stream (HIP events recorded around the launch)"
+    roof["avg_launch_ms"] = stage_ms[dom]
+    roof["algorithmic_per_launch"] = {"flops": kwk["flops"], "bytes": kwk["bytes"]}
+    per_stage = {}
+    for st in gemms + ("router_dgrad", "router_wgrad"):
+        k_ = backward_stage_work(w, counts, st)
+        t_ = stage_ms[st] * 1e-3
+        per_stage[st] = {"ms": round(stage_ms[st], 5),
+                         "tflops": round(k_["flops"] / t_ / 1e12, 1) if t_ > 0 else None,
+                         "gbs": round(k_["bytes"] / t_ / 1e9, 1) if t_ > 0 else None}
+    total_flops = sum(backward_stage_work(w, counts, st)["flops"]
+                      for st in gemms + ("router_dgrad", "router_wgrad"))
+    cfg = {"workload": w.name, "pass": "backward", "T": w.T, "d": w.d, "E": w.E, "k": w.k,
+           "d_ff": w.d_ff, "n_shared": w.n_shared, "capacity_factor": w.capacity_factor,
+           "seed": w.seed}
+    line = {"metric": "MoE-layer backward tokens/sec at 1 GPU (gate-up recompute included)",
+            "value": w.T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+            "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": cfg, "roofline": roof, "cpu_baseline": None,
+            "layer": {"flops": total_flops,
+                      "mfma_frac": total_flops / (ms * 1e-3) / (PEAK_BF16_TFLOPS * 1e12),
+                      "stages": per_stage,
+                      "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()}},
+            "launch": "eager"}
+    print(json.dumps(line), flush=True)
+    return 0
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -281,6 +406,9 @@ def main(argv=None):
     ap.add_argument("--routing", choices=("token_choice", "expert_choice"), default="token_choice",
                     help="expert_choice: every expert takes its C highest-probability tokens "
                          "(moe_forward_expert_choice); reported without a per-stage roofline")
+    ap.add_argument("--pass", dest="pass_", choices=("forward", "backward"), default="forward",
+                    help="backward: time moe_backward (the layer's gradient, gate-up recompute "
+                         "included) for the forward's routing")
     ap.add_argument("--graph", action="store_true",
                     help="replay the forward as one captured HIP graph per step (host launch "
                          "work out of the timed region)")
@@ -327,6 +455,11 @@ def main(argv=None):
 
     if args.routing == "expert_choice":
         return bench_expert_choice(args, w, p, g, kw, y, torch, moe)
+    if args.pass_ == "backward":
+        if w.dtype != "bf16":
+            log("bench.py --pass backward: the backward runs on bf16 storage only")
+            return 2
+        return bench_backward(args, w, p, g, kw, y, torch, moe)
 
     # routing of this batch (for the algorithmic work); identical in every step
     _, r = moe.forward(p, g["x"], g["w_gate"], g["w1"], g["w3"], g["w2"], return_routing=True, y=y,

@@ -259,6 +259,24 @@ moe_status moe_backward(const moe_problem* p, const void* x, const void* w_gate,
                         void* dw2, void* dws1, void* dws3, void* dws2, void* ws,
                         size_t ws_bytes, hipStream_t stream);
 
+/* Per-stage timing of moe_backward, for measurement tools: the same computation, and
+   additionally records caller-created HIP events on `stream`: stage_events[0] before the
+   first kernel, then one after each stage -- [1] gate-up recompute, [2] row preparation
+   (bf16 dy, g*dy, gathered x), [3] dgrad-down + SwiGLU backward, [4] dgrad-x, [5] wgrad-down,
+   [6] wgrad-up, [7] router logit gradient, [8] router dgrad, [9] router wgrad, [10] dx
+   gather. MOE_EINVAL if stage_events or any of its entries is NULL. */
+#define MOE_BWD_STAGE_EVENTS 11
+moe_status moe_backward_staged(const moe_problem* p, const void* x, const void* w_gate,
+                               const float* logit_bias, const void* w1, const void* w3,
+                               const void* w2, const void* ws1, const void* ws3, const void* ws2,
+                               const int32_t* topk_ids, const float* topk_w,
+                               const int32_t* counts_pre, const int32_t* offsets,
+                               const int32_t* sorted_assign, const int32_t* assign_pos,
+                               const float* dy, float alpha, float dL, float* dx,
+                               float* dw_gate, float* dlogit_bias, void* dw1, void* dw3,
+                               void* dw2, void* dws1, void* dws3, void* dws2, void* ws,
+                               size_t ws_bytes, hipStream_t stream, hipEvent_t* stage_events);
+
 #ifdef __cplusplus
 }
 #endif

@@ -23,8 +23,13 @@ __all__ = [
     "route", "align", "expert_ffn", "combine", "balance", "forward", "LIB_PATH",
     "MOE_OK", "MOE_EINVAL", "MOE_EUNSUPPORTED", "MOE_EWORKSPACE", "MOE_EHIP", "forward_staged",
     "STAGES", "problem_for", "PreparedForward", "bias_update", "expert_choice_capacity",
-    "expert_choice_workspace_bytes", "forward_expert_choice",
+    "expert_choice_workspace_bytes", "forward_expert_choice", "backward",
+    "backward_workspace_bytes", "BWD_STAGES",
 ]
+
+# stage names of moe_backward_staged, in event order (events 1..10 close these stages)
+BWD_STAGES = ("recompute", "prep", "dgrad_down", "dgrad_x", "wgrad_down", "wgrad_up", "router",
+              "router_dgrad", "router_wgrad", "dx")
 
 # stage names of moe_forward_staged, in event order (events 1..6 close these stages)
 STAGES = ("route", "align", "schedule", "gate_up", "down", "combine")
@@ -77,10 +82,12 @@ def _load() -> ctypes.CDLL:
     L.moe_forward_staged.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
     L.moe_backward_workspace_bytes.argtypes = [P, ctypes.POINTER(sz)]
     L.moe_backward.argtypes = [P] + [vp] * 16 + [f32, f32] + [vp] * 10 + [sz, vp]
+    L.moe_backward_staged.argtypes = [P] + [vp] * 16 + [f32, f32] + [vp] * 10 + [sz, vp, vp]
     for fn in ("moe_validate", "moe_capacity", "moe_workspace_bytes", "moe_route", "moe_align",
                "moe_expert_ffn", "moe_combine", "moe_balance", "moe_forward", "moe_forward_staged",
                "moe_bias_update", "moe_expert_choice_capacity", "moe_expert_choice_workspace_bytes",
-               "moe_forward_expert_choice", "moe_backward_workspace_bytes", "moe_backward"):
+               "moe_forward_expert_choice", "moe_backward_workspace_bytes", "moe_backward",
+               "moe_backward_staged"):
         getattr(L, fn).restype = ctypes.c_int
     return L
 
@@ -374,13 +381,14 @@ def backward_workspace_bytes(p: Problem) -> int:
 
 def backward(p: Problem, x, w_gate, w1, w3, w2, routing, dy, logit_bias=None, ws1=None, ws3=None,
              ws2=None, alpha: float = 0.01, dL: float = 0.0, want_dlogit_bias: bool = False,
-             ws=None, out=None):
+             ws=None, out=None, events=None):
     """Layer backward (bf16 storage) for the routing a forward(..., return_routing=True) call
     returned. dy: [T,d] fp32 gradient of y; dL: gradient of the balance loss (alpha as in the
     forward's balance statistics). Returns a dict: dx [T,d] fp32, dw_gate [E,d] fp32,
     dw1/dw3 [E,d_ff,d] and dw2 [E,d,d_ff] in the weights' dtype, the shared expert's
     dws1/dws3/dws2 when it has one, and dlogit_bias [E] fp32 with want_dlogit_bias.
-    `out` may hold preallocated tensors under those names."""
+    `out` may hold preallocated tensors under those names. `events`: 11 raw hipEvent_t
+    handles for moe_backward_staged (BWD_STAGES names the stages they close)."""
     dev, dt = x.device, _dt(p)
     _need(x, "x", (p.T, p.d), dt, dev)
     _need(w_gate, "w_gate", (p.E, p.d), dt, dev)
@@ -422,14 +430,22 @@ def backward(p: Problem, x, w_gate, w1, w3, w2, routing, dy, logit_bias=None, ws
     elif ws.device != dev or ws.dtype != torch.uint8 or ws.numel() < need:
         raise ValueError(f"workspace must be a uint8 tensor of >= {need} bytes on {dev}")
     g = o.get
-    _check("moe_backward", _lib.moe_backward(
-        ctypes.byref(p), _ptr(x), _ptr(w_gate), _ptr(logit_bias), _ptr(w1), _ptr(w3), _ptr(w2),
-        _ptr(ws1), _ptr(ws3), _ptr(ws2), _ptr(r["topk_ids"]), _ptr(r["topk_w"]),
-        _ptr(r["counts_pre"]), _ptr(r["offsets"]), _ptr(r["sorted_assign"]),
-        _ptr(r["assign_pos"]), _ptr(dy), float(alpha), float(dL), _ptr(g("dx")),
-        _ptr(g("dw_gate")), _ptr(g("dlogit_bias")), _ptr(g("dw1")), _ptr(g("dw3")),
-        _ptr(g("dw2")), _ptr(g("dws1")), _ptr(g("dws3")), _ptr(g("dws2")), _ptr(ws), ws.numel(),
-        _stream(dev)))
+    args = (ctypes.byref(p), _ptr(x), _ptr(w_gate), _ptr(logit_bias), _ptr(w1), _ptr(w3), _ptr(w2),
+            _ptr(ws1), _ptr(ws3), _ptr(ws2), _ptr(r["topk_ids"]), _ptr(r["topk_w"]),
+            _ptr(r["counts_pre"]), _ptr(r["offsets"]), _ptr(r["sorted_assign"]),
+            _ptr(r["assign_pos"]), _ptr(dy), float(alpha), float(dL), _ptr(g("dx")),
+            _ptr(g("dw_gate")), _ptr(g("dlogit_bias")), _ptr(g("dw1")), _ptr(g("dw3")),
+            _ptr(g("dw2")), _ptr(g("dws1")), _ptr(g("dws3")), _ptr(g("dws2")), _ptr(ws),
+            ws.numel(), _stream(dev))
+    if events is None:
+        _check("moe_backward", _lib.moe_backward(*args))
+    else:
+        if len(events) != len(BWD_STAGES) + 1:
+            raise ValueError(f"events: need {len(BWD_STAGES) + 1} handles")
+        ev = (ctypes.c_void_p * len(events))(
+            *[ctypes.c_void_p(int(e)) if not isinstance(e, ctypes.c_void_p) else e
+              for e in events])
+        _check("moe_backward_staged", _lib.moe_backward_staged(*args, ev))
     return o
 
 

@@ -305,7 +305,7 @@ MOE_API moe_status moe_backward_workspace_bytes(const moe_problem* p, size_t* by
   return MOE_OK;
 }
 
-MOE_API moe_status moe_backward(const moe_problem* p, const void* x, const void* w_gate,
+static moe_status backward_impl(const moe_problem* p, const void* x, const void* w_gate,
                                 const float* logit_bias, const void* w1, const void* w3,
                                 const void* w2, const void* ws1, const void* ws3, const void* ws2,
                                 const int32_t* topk_ids, const float* topk_w,
@@ -314,7 +314,7 @@ MOE_API moe_status moe_backward(const moe_problem* p, const void* x, const void*
                                 const float* dy, float alpha, float dL, float* dx, float* dw_gate,
                                 float* dlogit_bias, void* dw1, void* dw3, void* dw2, void* dws1,
                                 void* dws3, void* dws2, void* ws, size_t ws_bytes,
-                                hipStream_t stream) {
+                                hipStream_t stream, hipEvent_t* ev) {
   moe_status st = moe_validate(p);
   if (st != MOE_OK) return st;
   if (p->dtype != MOE_BF16 || p->k > 16) return MOE_EUNSUPPORTED;
@@ -331,7 +331,39 @@ MOE_API moe_status moe_backward(const moe_problem* p, const void* x, const void*
   return hip_status(launch_backward(*p, L, ws, x, w_gate, logit_bias, w1, w3, w2, ws1, ws3, ws2,
                                     topk_ids, topk_w, counts_pre, offsets, sorted_assign,
                                     assign_pos, dy, alpha, dL, dx, dw_gate, dlogit_bias, dw1, dw3,
-                                    dw2, dws1, dws3, dws2, stream));
+                                    dw2, dws1, dws3, dws2, stream, ev));
+}
+
+MOE_API moe_status moe_backward(const moe_problem* p, const void* x, const void* w_gate,
+                                const float* logit_bias, const void* w1, const void* w3,
+                                const void* w2, const void* ws1, const void* ws3, const void* ws2,
+                                const int32_t* topk_ids, const float* topk_w,
+                                const int32_t* counts_pre, const int32_t* offsets,
+                                const int32_t* sorted_assign, const int32_t* assign_pos,
+                                const float* dy, float alpha, float dL, float* dx, float* dw_gate,
+                                float* dlogit_bias, void* dw1, void* dw3, void* dw2, void* dws1,
+                                void* dws3, void* dws2, void* ws, size_t ws_bytes,
+                                hipStream_t stream) {
+  return backward_impl(p, x, w_gate, logit_bias, w1, w3, w2, ws1, ws3, ws2, topk_ids, topk_w,
+                       counts_pre, offsets, sorted_assign, assign_pos, dy, alpha, dL, dx, dw_gate,
+                       dlogit_bias, dw1, dw3, dw2, dws1, dws3, dws2, ws, ws_bytes, stream, nullptr);
+}
+
+MOE_API moe_status moe_backward_staged(
+    const moe_problem* p, const void* x, const void* w_gate, const float* logit_bias,
+    const void* w1, const void* w3, const void* w2, const void* ws1, const void* ws3,
+    const void* ws2, const int32_t* topk_ids, const float* topk_w, const int32_t* counts_pre,
+    const int32_t* offsets, const int32_t* sorted_assign, const int32_t* assign_pos,
+    const float* dy, float alpha, float dL, float* dx, float* dw_gate, float* dlogit_bias,
+    void* dw1, void* dw3, void* dw2, void* dws1, void* dws3, void* dws2, void* ws,
+    size_t ws_bytes, hipStream_t stream, hipEvent_t* stage_events) {
+  if (!stage_events) return MOE_EINVAL;
+  for (int i = 0; i < MOE_BWD_STAGE_EVENTS; ++i)
+    if (!stage_events[i]) return MOE_EINVAL;
+  return backward_impl(p, x, w_gate, logit_bias, w1, w3, w2, ws1, ws3, ws2, topk_ids, topk_w,
+                       counts_pre, offsets, sorted_assign, assign_pos, dy, alpha, dL, dx, dw_gate,
+                       dlogit_bias, dw1, dw3, dw2, dws1, dws3, dws2, ws, ws_bytes, stream,
+                       stage_events);
 }
 
 namespace {

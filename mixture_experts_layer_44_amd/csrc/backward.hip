@@ -648,7 +648,7 @@ hipError_t launch_backward(const moe_problem& p, const BwdLayout& L, void* ws, c
                            const int32_t* sorted_assign, const int32_t* assign_pos,
                            const float* dy, float alpha, float dL, float* dx, float* dw_gate,
                            float* dlogit_bias, void* dw1, void* dw3, void* dw2, void* dws1,
-                           void* dws3, void* dws2, hipStream_t s) {
+                           void* dws3, void* dws2, hipStream_t s, hipEvent_t* ev) {
   char* base = (char*)ws;
   auto at = [&](size_t o) { return (void*)(base + o); };
   const int G = p.E + p.n_shared;
@@ -677,20 +677,25 @@ hipError_t launch_backward(const moe_problem& p, const BwdLayout& L, void* ws, c
   float* dlb_part = (float*)at(L.dlb_part);
 
   hipError_t err;
+  int stage = 0;
+  auto mark = [&]() { return ev ? hipEventRecord(ev[stage++], s) : hipSuccess; };
 #define MOE_TRY(call)                  \
   do {                                 \
     if ((err = (call)) != hipSuccess) \
       return err;                      \
   } while (0)
   // 1. schedule (128-row m-tiles) and the gate-up recompute (h, u, v in storage rows)
+  MOE_TRY(mark());
   MOE_TRY(launch_schedule(p, offsets, sc, s));
   MOE_TRY(launch_expert_ffn(p, x, w1, w3, w2, ws1, ws3, ws2, sorted_assign, sc, H, nullptr,
                             nullptr, nullptr, s, nullptr, 0, U, V));
+  MOE_TRY(mark());
   // 2. dy in bf16, g dy and the gathered x rows in storage rows
   hipLaunchKernelGGL(bwd_prep_kernel, dim3(std::min(p.T + L.max_mt * BBM, 16384)), dim3(256), 0,
                      s, dy, (const bf16_t*)x, sorted_assign, topk_w, sc, p.T, p.d, p.k, p.E, dyb,
                      DO, XS, zero);
   MOE_TRY(hipGetLastError());
+  MOE_TRY(mark());
 
   BwdArgs c{};
   c.E = p.E;
@@ -722,6 +727,7 @@ hipError_t launch_backward(const moe_problem& p, const BwdLayout& L, void* ws, c
                              : launch_gemm<128, M_ROWS, A_TOKEN, B_W2, EPI_DDOWN>(a, tiles, s);
     MOE_TRY(err);
   }
+  MOE_TRY(mark());
   // 4. dgrad-x: (du | dv) (W1; W3) -> per-row dx (sorted order) and the shared rows
   {
     BwdArgs a = c;
@@ -742,6 +748,7 @@ hipError_t launch_backward(const moe_problem& p, const BwdLayout& L, void* ws, c
                              : launch_gemm<128, M_ROWS, A_STORE, B_W13, EPI_ROWS>(a, tiles, s);
     MOE_TRY(err);
   }
+  MOE_TRY(mark());
   // 5. wgrad-down: dW2_g = (g dy)^T h over the group's rows
   {
     BwdArgs a = c;
@@ -760,6 +767,7 @@ hipError_t launch_backward(const moe_problem& p, const BwdLayout& L, void* ws, c
                              : launch_gemm<128, M_WEIGHTS, AT_STORE, BT_STORE, EPI_WBF16>(a, tiles, s);
     MOE_TRY(err);
   }
+  MOE_TRY(mark());
   // 6. wgrad-up: (dW1_g; dW3_g) = (du | dv)^T x_rows
   {
     BwdArgs a = c;
@@ -780,6 +788,7 @@ hipError_t launch_backward(const moe_problem& p, const BwdLayout& L, void* ws, c
                              : launch_gemm<128, M_WEIGHTS, AT_STORE, BT_STORE, EPI_WBF16>(a, tiles, s);
     MOE_TRY(err);
   }
+  MOE_TRY(mark());
   // 7. router: logits again, then d l per token (gates + balance), then its column sums
   if (p.T > 0) {
     MOE_TRY(launch_route_logits(p, x, w_gate, logits_part, s));
@@ -791,6 +800,7 @@ hipError_t launch_backward(const moe_problem& p, const BwdLayout& L, void* ws, c
     MOE_TRY(hipGetLastError());
   }
   if (dlogit_bias) MOE_TRY(launch_psum_reduce(dlb_part, p.T > 0 ? L.nblk_router : 0, p.E, dlogit_bias, s));
+  MOE_TRY(mark());
   // 8. router dgrad: dx_router = d l W_gate (K = E_pad; rows of W_gate past E read zeros)
   {
     BwdArgs a = c;
@@ -810,6 +820,7 @@ hipError_t launch_backward(const moe_problem& p, const BwdLayout& L, void* ws, c
                              : launch_gemm<128, M_ROWS, A_IDENT, B_WGATE, EPI_ROWS>(a, tiles, s);
     MOE_TRY(err);
   }
+  MOE_TRY(mark());
   // 9. router wgrad: dW_gate = d l^T x (K = T)
   {
     BwdArgs a = c;
@@ -830,12 +841,14 @@ hipError_t launch_backward(const moe_problem& p, const BwdLayout& L, void* ws, c
                              : launch_gemm<128, M_WEIGHTS, AT_IDENT, BT_IDENT, EPI_WF32>(a, tiles, s);
     MOE_TRY(err);
   }
+  MOE_TRY(mark());
   // 10. dx
   if (p.T > 0) {
     hipLaunchKernelGGL(bwd_dx_kernel, dim3(p.T), dim3(256), 0, s, dx_router, dx_shared, dx_rows,
                        assign_pos, p.k, p.d, dx);
     MOE_TRY(hipGetLastError());
   }
+  MOE_TRY(mark());
 #undef MOE_TRY
   return hipSuccess;
 }

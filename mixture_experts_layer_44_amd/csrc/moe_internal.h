@@ -161,6 +161,6 @@ hipError_t launch_backward(const moe_problem& p, const BwdLayout& L, void* ws, c
                            const int32_t* sorted_assign, const int32_t* assign_pos,
                            const float* dy, float alpha, float dL, float* dx, float* dw_gate,
                            float* dlogit_bias, void* dw1, void* dw3, void* dw2, void* dws1,
-                           void* dws3, void* dws2, hipStream_t s);
+                           void* dws3, void* dws2, hipStream_t s, hipEvent_t* ev = nullptr);
 
 }  // namespace moe

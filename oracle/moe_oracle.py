@@ -52,7 +52,7 @@ __all__ = [
     "moe_forward_naive", "token_output", "token_outputs", "balance", "expert_table",
     "bias_update", "expert_choice_capacity", "expert_choice_route", "moe_forward_expert_choice",
     "sigmoid", "silu_grad", "swiglu_expert_backward", "gate_logit_grad", "balance_logit_grad",
-    "moe_backward",
+    "moe_backward", "moe_backward_sampled",
 ]
 
 ExpertFn = Callable[[int], Tuple[np.ndarray, np.ndarray, np.ndarray]]
@@ -540,3 +540,53 @@ def moe_backward(x, w_gate, experts: ExpertFn, E: int, k: int, dy, logit_bias=No
                 dw1=np.stack(dw1) if E else np.zeros((0,)), dw3=np.stack(dw3) if E else np.zeros((0,)),
                 dw2=np.stack(dw2) if E else np.zeros((0,)), dshared=dshared, dgate=dgate,
                 dlogits=dlogits, ids=r_ids, gates=gates, probs=probs, cap=cap, **al)
+
+
+def moe_backward_sampled(x, w_gate, experts: ExpertFn, E: int, k: int, dy, ids, tokens,
+                         sample_experts, logit_bias=None, shared: Sequence = (),
+                         capacity_factor: float = 0.0, alpha: float = 0.01, dL: float = 0.0):
+    """The parts of moe_backward that can be computed one by one on a full-size layer: dx of
+    the given tokens and the weight gradients of the given experts, for the batch's routing
+    `ids` [T, k] (the whole batch's ids fix the capacity drops and f_i). The same steps as
+    moe_backward, restricted: each sampled token's gate gradients come from its own expert
+    outputs; an expert's weight gradient sums over all of its kept rows.
+    Returns dict(dx [S, d], dlogits [S, E], dgate [S, k], wgrads {e: (dw1, dw3, dw2)})."""
+    x = np.asarray(x, dtype=np.float64)
+    dy = np.asarray(dy, dtype=np.float64)
+    ids = np.asarray(ids, dtype=np.int64)
+    T, d = x.shape
+    cap = capacity(capacity_factor, T, k, E)
+    al = align(ids, E, cap)
+    kept = (al["assign_pos"] >= 0).reshape(T, k)
+    tokens = np.asarray(tokens, dtype=np.int64)
+    xs, dys, ids_s, kept_s = x[tokens], dy[tokens], ids[tokens], kept[tokens]
+    probs = softmax(router_logits(xs, w_gate, logit_bias))
+    gates = renormalised_gates(probs, ids_s)
+    S = tokens.size
+    dx = np.zeros((S, d), dtype=np.float64)
+    dgate = np.zeros((S, k), dtype=np.float64)
+    for e in np.unique(ids_s[kept_s]):
+        rows, slots = np.nonzero((ids_s == e) & kept_s)   # a token chooses e at most once
+        d_rows, _, _, _, o = swiglu_expert_backward(xs[rows], *experts(int(e)),
+                                                    gates[rows, slots][:, None] * dys[rows])
+        dgate[rows, slots] = (dys[rows] * o).sum(axis=1)
+        np.add.at(dx, rows, d_rows)
+    for (s1, s3, s2) in shared:
+        d_rows, *_ = swiglu_expert_backward(xs, s1, s3, s2, dys)
+        dx += d_rows
+    dlogits = np.zeros((S, E), dtype=np.float64)
+    if S:
+        sel_grad = gate_logit_grad(gates, dgate)
+        np.add.at(dlogits, (np.repeat(np.arange(S), k), ids_s.reshape(-1)), sel_grad.reshape(-1))
+        if dL:
+            dlogits += balance_logit_grad(probs, al["counts_pre"], T, k, alpha, dL)
+    dx += dlogits @ np.asarray(w_gate, dtype=np.float64)
+    wgrads = {}
+    for e in sample_experts:
+        seg = al["sorted_assign"][al["offsets"][e]:al["offsets"][e + 1]]
+        tok, slot = seg // k, seg % k
+        g = renormalised_gates(softmax(router_logits(x[tok], w_gate, logit_bias)), ids[tok])
+        _, g1, g3, g2, _ = swiglu_expert_backward(x[tok], *experts(int(e)),
+                                                  g[np.arange(tok.size), slot][:, None] * dy[tok])
+        wgrads[int(e)] = (g1, g3, g2)
+    return dict(dx=dx, dlogits=dlogits, dgate=dgate, wgrads=wgrads)

@@ -156,3 +156,52 @@ def test_backward_deterministic():
     torch.cuda.synchronize()
     for name in outs[0]:
         assert torch.equal(outs[0][name], outs[1][name]), name
+
+
+FULL = [("mixtral_prefill", 16, 2), ("dsv3_fine", 8, 3), ("skew_cap", 16, 3)]
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name,n_tok,n_exp", FULL, ids=[f[0] for f in FULL])
+def test_full_size_backward_sampled(name, n_tok, n_exp):
+    """Full-size layer, in the launch configuration the benchmark times: dx of sampled tokens
+    and the weight gradients of sampled experts (the most and least loaded touched ones and a
+    random one) against the oracle computed one by one."""
+    import mixture_experts_layer_44_amd as moe
+    w = workloads.get(name)
+    _say(f"[backward] full {w} tokens={n_tok} experts={n_exp}")
+    g = workloads.generate(w, device="cuda")
+    p = moe.problem_for(w)
+    _, r = moe.forward(p, g["x"], g["w_gate"], g["w1"], g["w3"], g["w2"], logit_bias=g["logit_bias"],
+                       sel_bias=g["sel_bias"], ws1=g["ws1"], ws3=g["ws3"], ws2=g["ws2"],
+                       return_routing=True)
+    dy = _dy(w).cuda()
+    grads = moe.backward(p, g["x"], g["w_gate"], g["w1"], g["w3"], g["w2"], r, dy,
+                         logit_bias=g["logit_bias"], ws1=g["ws1"], ws3=g["ws3"], ws2=g["ws2"],
+                         alpha=0.01, dL=1.0)
+    torch.cuda.synchronize()
+    ids = r["topk_ids"].cpu().numpy().astype(np.int64)
+    counts = r["counts"].cpu().numpy()
+    rng = np.random.default_rng(w.seed)
+    tokens = np.sort(rng.choice(w.T, size=n_tok, replace=False))
+    touched = np.nonzero(counts > 0)[0]
+    picks = [int(touched[np.argmax(counts[touched])]), int(touched[np.argmin(counts[touched])])]
+    rest = [e for e in touched if e not in picks]
+    picks += [int(e) for e in rng.choice(rest, size=max(0, n_exp - 2), replace=False)]
+
+    def experts(e):
+        return f64(g["w1"][e]), f64(g["w3"][e]), f64(g["w2"][e])
+
+    shared = [] if not w.n_shared else [(f64(g["ws1"][0]), f64(g["ws3"][0]), f64(g["ws2"][0]))]
+    ref = O.moe_backward_sampled(f64(g["x"]), f64(g["w_gate"]), experts, w.E, w.k, f64(dy), ids,
+                                 tokens, picks, f64(g["logit_bias"]), shared, w.capacity_factor,
+                                 alpha=0.01, dL=1.0)
+    rep = {"dx": _compare("dx", grads["dx"][torch.from_numpy(tokens).cuda()], ref["dx"])}
+    for e in picks:
+        for m, key in enumerate(("dw1", "dw3", "dw2")):
+            rep[f"{key}[{e}]"] = _compare(f"{key}[{e}]", grads[key][e], ref["wgrads"][e][m])
+    _say(f"{name}: experts {picks} rows {[int(counts[e]) for e in picks]}: " +
+         ", ".join(f"{k}=({a:.1e},{b:.1e})" for k, (a, b) in rep.items()))
+    del grads, g
+    torch.cuda.empty_cache()

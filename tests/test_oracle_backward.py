@@ -196,7 +196,24 @@ def pin_bwd_unused_and_dropped():
     np.testing.assert_allclose(g["dx"][t], want, rtol=1e-12, atol=1e-13)
 
 
-PINS = [pin_bwd_finite_differences, pin_bwd_autograd, pin_bwd_logit_rows_sum_to_zero,
+def pin_bwd_sampled_equals_full():
+    """moe_backward_sampled (dx of chosen tokens, weight gradients of chosen experts) equals
+    the corresponding parts of moe_backward, with drops, a shared expert and dL != 0."""
+    P = _problem(17, T=40, d=8, E=6, k=2, d_ff=6, n_shared=1, cf=0.8)
+    g = _backward(P, 0.02, 1.3)
+    tokens = [0, 3, 17, 39, 22]
+    sample = [1, 4]
+    s = O.moe_backward_sampled(P["x"], P["w_gate"], O.expert_table(P["w1"], P["w3"], P["w2"]),
+                               P["E"], P["k"], P["dy"], g["ids"], tokens, sample, P["logit_bias"],
+                               P["shared"], P["cf"], alpha=0.02, dL=1.3)
+    np.testing.assert_allclose(s["dx"], g["dx"][tokens], rtol=1e-12, atol=1e-13)
+    np.testing.assert_allclose(s["dlogits"], g["dlogits"][tokens], rtol=1e-12, atol=1e-14)
+    for e in sample:
+        for m, key in enumerate(("dw1", "dw3", "dw2")):
+            np.testing.assert_allclose(s["wgrads"][e][m], g[key][e], rtol=1e-12, atol=1e-13)
+
+
+PINS = [pin_bwd_sampled_equals_full, pin_bwd_finite_differences, pin_bwd_autograd, pin_bwd_logit_rows_sum_to_zero,
         pin_bwd_linear_in_upstream, pin_bwd_single_expert_is_dense_swiglu,
         pin_bwd_unused_and_dropped]
 

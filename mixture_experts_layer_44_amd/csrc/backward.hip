@@ -48,6 +48,12 @@ typedef short v8s __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) v4s* lds_v4s_ptr;
 
 constexpr int BBM = 128;   // rows of every backward m-tile (the schedule's BM)
+// The weight-gradient GEMMs contract over a segment's rows, often only one or two K steps:
+// their time goes into each tile's load latency and output writes, not MFMAs. A 2-stage ring
+// of 128 x 128 tiles (64 KB of LDS) lets two workgroups share a CU and overlap one's loads
+// with the other's writes; measured faster than 3 stages or 256-wide tiles on every layer.
+constexpr int kWgradStages = 2;
+constexpr int kWgradBN = 128;
 constexpr int ZERO_ELEMS = 256;
 
 enum AKind : int { A_TOKEN, A_STORE, A_IDENT, AT_STORE, AT_IDENT };
@@ -117,7 +123,7 @@ __device__ __forceinline__ int tr_base(int lane, int mb) {
   return tr_off<W>(row, col);
 }
 
-template <int BN, int MODE, int AK, int BKIND, int EPI>
+template <int BN, int MODE, int AK, int BKIND, int EPI, int ST>
 __global__ __launch_bounds__(512) void bwd_gemm_kernel(BwdArgs a) {
   constexpr int BM = BBM, BK = 64, WM = 2, WN = 4, NW = WM * WN, NKS = BK / 16;
   constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
@@ -126,7 +132,8 @@ __global__ __launch_bounds__(512) void bwd_gemm_kernel(BwdArgs a) {
   constexpr int DMA_A = ASZ * 2 / 1024 / NW, DMA_B = BSZ * 2 / 1024 / NW;
   static_assert(DMA_A * 1024 * NW == ASZ * 2 && DMA_B * 1024 * NW == BSZ * 2, "even split");
   static_assert(FM >= 1 && FN >= 1, "wave tile covers whole fragments");
-  __shared__ __attribute__((aligned(1024))) bf16_t smem[3 * STAGE];
+  static_assert(ST >= 2 && ST * STAGE >= BM * BN, "ring holds the staged output tile");
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[ST * STAGE];
   __shared__ float red[EPI == EPI_DDOWN ? WN : 1][EPI == EPI_DDOWN ? BM : 1];
   __shared__ float gate_s[EPI == EPI_DDOWN ? BM : 1];
 
@@ -303,21 +310,24 @@ __global__ __launch_bounds__(512) void bwd_gemm_kernel(BwdArgs a) {
     }
   };
 
-  // ---- main loop: 3-stage ring, two steps in flight (as in the forward's ring kernel)
+  // ---- main loop: a ring of ST stages, ST-1 steps in flight (as in the forward's ring
+  // kernel); past the last step the loads repeat it into a stage nobody reads again
   if (KT > 0) {
-    issue_a(0, smem);
-    issue_b(0, smem + ASZ);
-    issue_a(KT > 1 ? 1 : 0, smem + STAGE);
-    issue_b(KT > 1 ? 1 : 0, smem + STAGE + ASZ);
+#pragma unroll
+    for (int s0 = 0; s0 < ST - 1; ++s0) {
+      const int ld = s0 < KT ? s0 : KT - 1;
+      issue_a(ld, smem + s0 * STAGE);
+      issue_b(ld, smem + s0 * STAGE + ASZ);
+    }
     for (int kt = 0; kt < KT; ++kt) {
-      __builtin_amdgcn_s_waitcnt(wait_vm(DMA_A + DMA_B));
+      __builtin_amdgcn_s_waitcnt(wait_vm((ST - 2) * (DMA_A + DMA_B)));
       __builtin_amdgcn_s_barrier();
       __builtin_amdgcn_sched_barrier(0);
-      const int nxt = kt + 2, ld = nxt < KT ? nxt : KT - 1;
-      bf16_t* st = smem + (nxt % 3) * STAGE;
+      const int nxt = kt + ST - 1, ld = nxt < KT ? nxt : KT - 1;
+      bf16_t* st = smem + (nxt % ST) * STAGE;
       issue_a(ld, st);
       issue_b(ld, st + ASZ);
-      const bf16_t* cs = smem + (kt % 3) * STAGE;
+      const bf16_t* cs = smem + (kt % ST) * STAGE;
       compute(cs, cs + ASZ);
     }
     __builtin_amdgcn_s_waitcnt(wait_vm(0));
@@ -387,6 +397,34 @@ __global__ __launch_bounds__(512) void bwd_gemm_kernel(BwdArgs a) {
     return;
   }
 
+  if (EPI == EPI_WBF16) {
+    // bf16 weight-gradient tile: staged through LDS (the ring is idle now) so that every lane
+    // writes whole 16-byte pieces of output rows. The tile lies in one output matrix (Msplit
+    // is a multiple of BM).
+    __syncthreads();                       // every wave is done with the ring
+    bf16_t* tile = smem;                   // [BM][BN]
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int lr = wm * TM + i * 32 + 8 * (r >> 2) + 4 * fkc + (r & 3);
+          tile[lr * BN + wn * TN + j * 32 + fr] = f32_to_bf16(acc[i][j][r]);
+        }
+    __syncthreads();
+    const bool second = m0 >= a.Msplit;
+    const int mm0 = second ? m0 - a.Msplit : m0;
+    bf16_t* base = shared_grp ? (second ? a.SW1 : a.SW0)
+                              : (second ? a.W1 : a.W0) + (size_t)g * a.Msplit * a.N;
+    constexpr int CH = BN / 8;              // 16-byte pieces per tile row
+    for (int idx = tid; idx < BM * CH; idx += NW * 64) {
+      const int row = idx / CH, ch = idx % CH;
+      *(u32x4*)(base + (size_t)(mm0 + row) * a.N + n0 + ch * 8) = *(const u32x4*)(tile + row * BN + ch * 8);
+    }
+    return;
+  }
+
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -404,13 +442,6 @@ __global__ __launch_bounds__(512) void bwd_gemm_kernel(BwdArgs a) {
                                           : a.out + (size_t)(off + rg) * a.N;
             dst[col] = val;
           }
-        } else if (EPI == EPI_WBF16) {
-          const int m = m0 + lr;
-          const bool second = m >= a.Msplit;
-          const int mm = second ? m - a.Msplit : m;
-          bf16_t* base = shared_grp ? (second ? a.SW1 : a.SW0)
-                                    : (second ? a.W1 : a.W0) + (size_t)g * a.Msplit * a.N;
-          base[(size_t)mm * a.N + col] = f32_to_bf16(val);
         } else {
           const int m = m0 + lr;
           if (m < a.Mvalid) a.Wf[(size_t)m * a.N + col] = val;
@@ -590,13 +621,16 @@ __global__ __launch_bounds__(256) void bwd_dx_kernel(const float* __restrict__ d
 template <int BN, int MODE, int AK, int BKIND, int EPI>
 hipError_t launch_gemm(const BwdArgs& a, int tiles, hipStream_t s) {
   if (tiles <= 0) return hipSuccess;
-  hipLaunchKernelGGL((bwd_gemm_kernel<BN, MODE, AK, BKIND, EPI>), dim3((tiles + 7) / 8 * 8),
+  constexpr int ST = MODE == M_WEIGHTS ? kWgradStages : 3;
+  hipLaunchKernelGGL((bwd_gemm_kernel<BN, MODE, AK, BKIND, EPI, ST>), dim3((tiles + 7) / 8 * 8),
                      dim3(512), 0, s, a);
   return hipGetLastError();
 }
 
 // BN for an output width: 256 when it divides, else 128
 inline int bn_for(int n) { return n % 256 == 0 ? 256 : 128; }
+// BN of the weight-gradient GEMMs (their K, a segment's rows, is short on fine-grained layers)
+inline int wgrad_bn(int n) { return kWgradBN == 256 ? bn_for(n) : 128; }
 
 }  // namespace
 
@@ -761,7 +795,7 @@ hipError_t launch_backward(const moe_problem& p, const BwdLayout& L, void* ws, c
     a.W0 = (bf16_t*)dw2;
     a.SW0 = (bf16_t*)dws2;
     a.Msplit = p.d;
-    const int bn = bn_for(p.d_ff);
+    const int bn = wgrad_bn(p.d_ff);
     const int tiles = G * (p.d / BBM) * (p.d_ff / bn);
     err = (bn == 256) ? launch_gemm<256, M_WEIGHTS, AT_STORE, BT_STORE, EPI_WBF16>(a, tiles, s)
                              : launch_gemm<128, M_WEIGHTS, AT_STORE, BT_STORE, EPI_WBF16>(a, tiles, s);
@@ -782,7 +816,7 @@ hipError_t launch_backward(const moe_problem& p, const BwdLayout& L, void* ws, c
     a.SW0 = (bf16_t*)dws1;
     a.SW1 = (bf16_t*)dws3;
     a.Msplit = p.d_ff;
-    const int bn = bn_for(p.d);
+    const int bn = wgrad_bn(p.d);
     const int tiles = G * (2 * p.d_ff / BBM) * (p.d / bn);
     err = (bn == 256) ? launch_gemm<256, M_WEIGHTS, AT_STORE, BT_STORE, EPI_WBF16>(a, tiles, s)
                              : launch_gemm<128, M_WEIGHTS, AT_STORE, BT_STORE, EPI_WBF16>(a, tiles, s);
@@ -834,7 +868,7 @@ hipError_t launch_backward(const moe_problem& p, const BwdLayout& L, void* ws, c
     a.ident_rows = p.T;
     a.Wf = dw_gate;
     a.Mvalid = p.E;
-    const int bn = bn_for(p.d);
+    const int bn = wgrad_bn(p.d);
     const int tiles = (L.E_pad / BBM) * (p.d / bn);
     // (T = 0: the K loop is empty and every tile writes zeros)
     err = (bn == 256) ? launch_gemm<256, M_WEIGHTS, AT_IDENT, BT_IDENT, EPI_WF32>(a, tiles, s)

@@ -35,6 +35,8 @@
 // values a 32x32x16 fragment takes. Such [k][m] rows are XOR-swizzled in 16-byte chunks by
 // 4 * (k % 4), so the 4 rows x 2 chunks of a 16-lane group (and the 4 x 4 of 32 lanes) hit
 // distinct bank groups. Contraction rows past a segment's end read a zero row.
+#include <type_traits>
+
 #include "moe_internal.h"
 #include "mfma_tiles.h"
 #include "topk.h"
@@ -54,6 +56,8 @@ constexpr int BBM = 128;   // rows of every backward m-tile (the schedule's BM)
 // with the other's writes; measured faster than 3 stages or 256-wide tiles on every layer.
 constexpr int kWgradStages = 2;
 constexpr int kWgradBN = 128;
+constexpr int kRowsBM = 256;      // m-tile of the row-tiled GEMMs (ragged, staggered rings)
+constexpr int kDeepRowsFrom = 0;  // < 0: never put the rows in the deep ring
 constexpr int ZERO_ELEMS = 256;
 
 enum AKind : int { A_TOKEN, A_STORE, A_IDENT, AT_STORE, AT_IDENT };
@@ -76,7 +80,8 @@ struct BwdArgs {
   int ident_rows;
   int Kvalid;               // B_WGATE: rows of B that exist (E)
   const int32_t* sorted_assign;
-  Schedule sc;              // BM = 128
+  Schedule sc;              // rows mode: the row-tile schedule; weights mode: the storage one
+  const int32_t* stor_start;   // the storage schedule's m-tile starts (128-row storage)
   float* out;               // EPI_ROWS: routed rows (sorted order) or identity rows
   float* out_shared;        // EPI_ROWS: the shared expert's rows (token order)
   bf16_t* W0;               // EPI_WBF16: routed dW, output rows < Msplit
@@ -123,19 +128,35 @@ __device__ __forceinline__ int tr_base(int lane, int mb) {
   return tr_off<W>(row, col);
 }
 
-template <int BN, int MODE, int AK, int BKIND, int EPI, int ST>
-__global__ __launch_bounds__(512) void bwd_gemm_kernel(BwdArgs a) {
-  constexpr int BM = BBM, BK = 64, WM = 2, WN = 4, NW = WM * WN, NKS = BK / 16;
+// The GEMM. BM x BN tiles, WM x WN waves, each a (BM/WM) x (BN/WN) block of 32x32 fragments.
+// Row fragments are dealt to the waves interleaved: fragment i of wave row wm covers tile rows
+// (i*WM + wm)*32 .. +32, so a ragged tile's rows with data spread over all SIMDs.
+// ST >= 2: a ring of ST stages of both operands, ST-1 steps in flight (weights mode).
+// ST == 0: staggered rings (rows mode): A, the rows, in 2 slots one step ahead; B, the
+// weights, in 3 slots two steps ahead; A issued first in each step so that the step's wait
+// leaves only B's latest loads in flight. The A row groups past a tile's last row with data
+// are then not loaded at all, and a wave skips the fragments that are all padding.
+template <int BM, int BN, int WM, int WN, int MODE, int AK, int BKIND, int EPI, int ST,
+          bool DEEPA = false>
+__global__ __launch_bounds__(WM * WN * 64) void bwd_gemm_kernel(BwdArgs a) {
+  constexpr int BK = 64, NW = WM * WN, NKS = BK / 16;
   constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
   constexpr bool ATR = AK == AT_STORE || AK == AT_IDENT;
-  constexpr int ASZ = BM * BK, BSZ = BN * BK, STAGE = ASZ + BSZ;
+  constexpr bool STAG = ST == 0;
+  constexpr int ASZ = BM * BK, BSZ = BN * BK;
+  // ring slots of A and B (staggered: the deep operand has 3, the shallow one 2)
+  constexpr int NA = STAG ? (DEEPA ? 3 : 2) : ST, NB = STAG ? (DEEPA ? 2 : 3) : ST;
   constexpr int DMA_A = ASZ * 2 / 1024 / NW, DMA_B = BSZ * 2 / 1024 / NW;
   static_assert(DMA_A * 1024 * NW == ASZ * 2 && DMA_B * 1024 * NW == BSZ * 2, "even split");
-  static_assert(FM >= 1 && FN >= 1, "wave tile covers whole fragments");
-  static_assert(ST >= 2 && ST * STAGE >= BM * BN, "ring holds the staged output tile");
-  __shared__ __attribute__((aligned(1024))) bf16_t smem[ST * STAGE];
-  __shared__ float red[EPI == EPI_DDOWN ? WN : 1][EPI == EPI_DDOWN ? BM : 1];
-  __shared__ float gate_s[EPI == EPI_DDOWN ? BM : 1];
+  static_assert(FM >= 1 && FN >= 1 && FM <= 3, "wave tile covers whole fragments");
+  static_assert(!STAG || (MODE == M_ROWS && !ATR), "staggered rings: rows mode only");
+  static_assert((NA * ASZ + NB * BSZ) * 2 <= 160 * 1024, "rings fit in LDS");
+  static_assert(NA * ASZ + NB * BSZ >= BM * BN, "the ring holds the staged output tile");
+  static_assert(EPI != EPI_DDOWN || (NA * ASZ + NB * BSZ) * 2 >= (WN + 1) * BM * 4,
+                "the ring holds the epilogue's row sums");
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[NA * ASZ + NB * BSZ];
+  bf16_t* const As = smem;
+  bf16_t* const Bs = smem + NA * ASZ;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -165,6 +186,8 @@ __global__ __launch_bounds__(512) void bwd_gemm_kernel(BwdArgs a) {
       rows = tc.rows;
       off = tc.off;
     }
+    // rows of this group are stored from storage row sbase (the 128-row storage schedule)
+    sbase = a.ident ? 0 : a.stor_start[g] * BBM;
   } else {
     const int G = a.ident ? 1 : a.sc.G;
     const int MT = a.M / BM, NTt = a.N / BN, total = G * MT * NTt;
@@ -178,10 +201,13 @@ __global__ __launch_bounds__(512) void bwd_gemm_kernel(BwdArgs a) {
     m0 = mt * BM;
     n0 = (rem - mt * NTt) * BN;
     rows = a.ident ? a.ident_rows : a.sc.grp_rows[g];
-    sbase = a.ident ? 0 : a.sc.mt_start[g] * BM;
+    sbase = a.ident ? 0 : a.sc.mt_start[g] * BBM;
   }
   const bool shared_grp = !a.ident && g >= a.E;
   const int KT = MODE == M_ROWS ? a.K / BK : (rows + BK - 1) / BK;
+  // rows of this tile that hold data (rows mode)
+  const int rows_here =
+      MODE == M_ROWS ? __builtin_amdgcn_readfirstlane(min(BM, rows - m_local * BM)) : BM;
 
   // ---- A loads
   // non-transposed [BM][BK] stage (rows mode): load i of this wave fills rows q*8 .. q*8+7
@@ -198,16 +224,15 @@ __global__ __launch_bounds__(512) void bwd_gemm_kernel(BwdArgs a) {
       const int row = q * 8 + lane / 8;
       const int lchunk = (swz<BK>(row, lane % 8) - row * BK) >> 3;
       const int rg = m_local * BM + row;
-      const bool valid = rg < rows;
+      const int rc = rg < rows ? rg : 0;       // padding rows read the group's first row
       int src;
       if (AK == A_TOKEN) {
-        if (shared_grp) src = valid ? rg : 0;
-        else src = a.sorted_assign[off + (valid ? rg : 0)] / a.k;
+        src = shared_grp ? rc : a.sorted_assign[off + rc] / a.k;
         src = (unsigned)src < (unsigned)a.T ? src : 0;
       } else if (AK == A_STORE) {
-        src = mt_global * BM + row;
+        src = sbase + rc;
       } else {
-        src = valid ? rg : 0;
+        src = rc;
       }
       aoff[i] = (uint32_t)src * (uint32_t)a.lda + lchunk * 8;
     } else {
@@ -215,11 +240,13 @@ __global__ __launch_bounds__(512) void bwd_gemm_kernel(BwdArgs a) {
       alch[i] = (lane % 16) ^ ((akrow[i] & 3) << 2);
     }
   }
-  auto issue_a = [&](int kt, bf16_t* dst) {
+  auto issue_a = [&](int kt, int slot) {
+    bf16_t* dst = As + slot * ASZ;
 #pragma unroll
     for (int i = 0; i < DMA_A; ++i) {
       const bf16_t* src;
       if (!ATR) {
+        if (STAG && !DEEPA && (wave * DMA_A + i) * 8 >= rows_here) continue;   // wave-uniform
         src = a.A + aoff[i] + kt * BK;
       } else {
         const int r = kt * BK + akrow[i];
@@ -249,7 +276,8 @@ __global__ __launch_bounds__(512) void bwd_gemm_kernel(BwdArgs a) {
     bmat0 = shared_grp ? a.S0 : a.B0 + (size_t)g * msz;
     bmat1 = shared_grp ? a.S1 : a.B1 + (size_t)g * msz;
   }
-  auto issue_b = [&](int kt, bf16_t* dst) {
+  auto issue_b = [&](int kt, int slot) {
+    bf16_t* dst = Bs + slot * BSZ;
 #pragma unroll
     for (int i = 0; i < DMA_B; ++i) {
       const int r = kt * BK + bkrow[i];
@@ -277,9 +305,9 @@ __global__ __launch_bounds__(512) void bwd_gemm_kernel(BwdArgs a) {
   int aoffs[NKS], abase[FM], bbase[FN];
 #pragma unroll
   for (int ks = 0; ks < NKS; ++ks)
-    aoffs[ks] = (wm * TM + fr) * BK + ((((2 * ks + fkc) ^ ((fr >> 1) & 7))) << 3);
+    aoffs[ks] = (wm * 32 + fr) * BK + ((((2 * ks + fkc) ^ ((fr >> 1) & 7))) << 3);
 #pragma unroll
-  for (int i = 0; i < FM; ++i) abase[i] = tr_base<BM>(lane, wm * TM + i * 32);
+  for (int i = 0; i < FM; ++i) abase[i] = tr_base<BM>(lane, (i * WM + wm) * 32);
 #pragma unroll
   for (int j = 0; j < FN; ++j) bbase[j] = tr_base<BN>(lane, wn * TN + j * 32);
 
@@ -291,56 +319,92 @@ __global__ __launch_bounds__(512) void bwd_gemm_kernel(BwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
 
-  auto compute = [&](const bf16_t* As, const bf16_t* Bs) {
-    __builtin_amdgcn_iglp_opt(1);
+  // the K loop for a wave whose first NF row fragments hold data
+  auto k_loop = [&](auto nf_tag) {
+    constexpr int NF = decltype(nf_tag)::value;
+    auto compute = [&](const bf16_t* Ast, const bf16_t* Bst) {
+      if constexpr (NF == 0) return;
+      __builtin_amdgcn_iglp_opt(1);
 #pragma unroll
-    for (int ks = 0; ks < NKS; ++ks) {
-      bf16x8 af[FM], bfv[FN];
+      for (int ks = 0; ks < NKS; ++ks) {
+        bf16x8 af[FM], bfv[FN];
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
-        af[i] = ATR ? tr_frag<BM>(As, abase[i], ks)
-                    : *(const bf16x8*)&As[aoffs[ks] + i * 32 * BK];
+        for (int i = 0; i < NF; ++i)
+          af[i] = ATR ? tr_frag<BM>(Ast, abase[i], ks)
+                      : *(const bf16x8*)&Ast[aoffs[ks] + i * WM * 32 * BK];
 #pragma unroll
-      for (int j = 0; j < FN; ++j) bfv[j] = tr_frag<BN>(Bs, bbase[j], ks);
+        for (int j = 0; j < FN; ++j) bfv[j] = tr_frag<BN>(Bst, bbase[j], ks);
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+        for (int i = 0; i < NF; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfv[j], acc[i][j], 0, 0, 0);
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfv[j], acc[i][j], 0, 0, 0);
+      }
+    };
+    if constexpr (STAG && !DEEPA) {
+      issue_a(0, 0);
+      issue_b(0, 0);
+      issue_b(KT > 1 ? 1 : 0, 1);
+      for (int kt = 0; kt < KT; ++kt) {
+        __builtin_amdgcn_s_waitcnt(wait_vm(DMA_B));
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        issue_a(kt + 1 < KT ? kt + 1 : KT - 1, (kt + 1) & 1);
+        issue_b(kt + 2 < KT ? kt + 2 : KT - 1, (kt + 2) % 3);
+        compute(As + (kt & 1) * ASZ, Bs + (kt % 3) * BSZ);
+      }
+    } else if constexpr (STAG) {          // rows deep, weights shallow
+      issue_b(0, 0);
+      issue_a(0, 0);
+      issue_a(KT > 1 ? 1 : 0, 1);
+      for (int kt = 0; kt < KT; ++kt) {
+        __builtin_amdgcn_s_waitcnt(wait_vm(DMA_A));
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        issue_b(kt + 1 < KT ? kt + 1 : KT - 1, (kt + 1) & 1);
+        issue_a(kt + 2 < KT ? kt + 2 : KT - 1, (kt + 2) % 3);
+        compute(As + (kt % 3) * ASZ, Bs + (kt & 1) * BSZ);
+      }
+    } else {
+#pragma unroll
+      for (int s0 = 0; s0 < ST - 1; ++s0) {
+        const int ld = s0 < KT ? s0 : KT - 1;
+        issue_a(ld, s0);
+        issue_b(ld, s0);
+      }
+      for (int kt = 0; kt < KT; ++kt) {
+        __builtin_amdgcn_s_waitcnt(wait_vm((ST - 2) * (DMA_A + DMA_B)));
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        const int nxt = kt + ST - 1, ld = nxt < KT ? nxt : KT - 1;
+        issue_a(ld, nxt % ST);
+        issue_b(ld, nxt % ST);
+        compute(As + (kt % ST) * ASZ, Bs + (kt % ST) * BSZ);
+      }
     }
   };
-
-  // ---- main loop: a ring of ST stages, ST-1 steps in flight (as in the forward's ring
-  // kernel); past the last step the loads repeat it into a stage nobody reads again
   if (KT > 0) {
-#pragma unroll
-    for (int s0 = 0; s0 < ST - 1; ++s0) {
-      const int ld = s0 < KT ? s0 : KT - 1;
-      issue_a(ld, smem + s0 * STAGE);
-      issue_b(ld, smem + s0 * STAGE + ASZ);
-    }
-    for (int kt = 0; kt < KT; ++kt) {
-      __builtin_amdgcn_s_waitcnt(wait_vm((ST - 2) * (DMA_A + DMA_B)));
-      __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-      const int nxt = kt + ST - 1, ld = nxt < KT ? nxt : KT - 1;
-      bf16_t* st = smem + (nxt % ST) * STAGE;
-      issue_a(ld, st);
-      issue_b(ld, st + ASZ);
-      const bf16_t* cs = smem + (kt % ST) * STAGE;
-      compute(cs, cs + ASZ);
-    }
+    // wave-uniform count of this wave's row fragments that hold data (rows mode, staggered)
+    const int nf = STAG && !DEEPA ? min(FM, max(0, (rows_here - wm * 32 + WM * 32 - 1) / (WM * 32)))
+                                  : FM;
+    if (nf >= FM) k_loop(std::integral_constant<int, FM>{});
+    else if (nf == 2) k_loop(std::integral_constant<int, (FM > 2 ? 2 : 0)>{});
+    else if (nf == 1) k_loop(std::integral_constant<int, (FM > 1 ? 1 : 0)>{});
+    else k_loop(std::integral_constant<int, 0>{});
     __builtin_amdgcn_s_waitcnt(wait_vm(0));
   }
 
   // ---- epilogues. 32x32 accumulator layout: lane holds column lane%32 and rows
   // 8*(r/4) + 4*(lane/32) + r%4 for r = 0..15 of each fragment.
+  __syncthreads();                         // every wave is done with the ring
   if (EPI == EPI_DDOWN) {
-    if (tid < BM) {
-      const int rg = m_local * BM + tid;
+    float* red = (float*)smem;             // [WN][BM] per-wave row sums of the gate gradient
+    float* gate_s = red + WN * BM;         // [BM] gate of each tile row
+    for (int r = tid; r < BM; r += NW * 64) {
+      const int rg = m_local * BM + r;
       float gv = 1.f;
       if (!shared_grp && rg < rows) gv = a.topk_w[a.sorted_assign[off + rg]];
-      gate_s[tid] = gv;
+      gate_s[r] = gv;
     }
     __syncthreads();
     const int N = a.N;
@@ -356,9 +420,9 @@ __global__ __launch_bounds__(512) void bwd_gemm_kernel(BwdArgs a) {
         const int col = n0 + wn * TN + j * 32 + fr;
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int lr = wm * TM + i * 32 + 8 * (r >> 2) + 4 * fkc + (r & 3);
+          const int lr = (i * WM + wm) * 32 + 8 * (r >> 2) + 4 * fkc + (r & 3);
           if (m_local * BM + lr < rows) {
-            const size_t s = (size_t)(mt_global * BM + lr);
+            const size_t s = (size_t)(sbase + m_local * BM + lr);
             const float u = a.U[s * N + col], v = a.V[s * N + col];
             const float dh = acc[i][j][r];
             const float sig = __builtin_amdgcn_rcpf(1.0f + __expf(-u));
@@ -382,18 +446,19 @@ __global__ __launch_bounds__(512) void bwd_gemm_kernel(BwdArgs a) {
         v += __shfl_xor(v, 4, 32);
         v += __shfl_xor(v, 2, 32);
         v += __shfl_xor(v, 1, 32);
-        if (fr == 0) red[wn][wm * TM + i * 32 + 8 * (r >> 2) + 4 * fkc + (r & 3)] = v;
+        if (fr == 0) red[wn * BM + (i * WM + wm) * 32 + 8 * (r >> 2) + 4 * fkc + (r & 3)] = v;
       }
     __syncthreads();
-    if (tid < BM && !shared_grp) {
-      const int rg = m_local * BM + tid;
-      if (rg < rows) {
-        float s = 0.f;
+    if (!shared_grp)
+      for (int r = tid; r < BM; r += NW * 64) {
+        const int rg = m_local * BM + r;
+        if (rg < rows) {
+          float sum = 0.f;
 #pragma unroll
-        for (int w = 0; w < WN; ++w) s += red[w][tid];
-        a.dgate_part[(size_t)(off + rg) * a.NT + n0 / BN] = s;
+          for (int w = 0; w < WN; ++w) sum += red[w * BM + r];
+          a.dgate_part[(size_t)(off + rg) * a.NT + n0 / BN] = sum;
+        }
       }
-    }
     return;
   }
 
@@ -401,7 +466,6 @@ __global__ __launch_bounds__(512) void bwd_gemm_kernel(BwdArgs a) {
     // bf16 weight-gradient tile: staged through LDS (the ring is idle now) so that every lane
     // writes whole 16-byte pieces of output rows. The tile lies in one output matrix (Msplit
     // is a multiple of BM).
-    __syncthreads();                       // every wave is done with the ring
     bf16_t* tile = smem;                   // [BM][BN]
 #pragma unroll
     for (int i = 0; i < FM; ++i)
@@ -409,7 +473,7 @@ __global__ __launch_bounds__(512) void bwd_gemm_kernel(BwdArgs a) {
       for (int j = 0; j < FN; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int lr = wm * TM + i * 32 + 8 * (r >> 2) + 4 * fkc + (r & 3);
+          const int lr = (i * WM + wm) * 32 + 8 * (r >> 2) + 4 * fkc + (r & 3);
           tile[lr * BN + wn * TN + j * 32 + fr] = f32_to_bf16(acc[i][j][r]);
         }
     __syncthreads();
@@ -420,7 +484,8 @@ __global__ __launch_bounds__(512) void bwd_gemm_kernel(BwdArgs a) {
     constexpr int CH = BN / 8;              // 16-byte pieces per tile row
     for (int idx = tid; idx < BM * CH; idx += NW * 64) {
       const int row = idx / CH, ch = idx % CH;
-      *(u32x4*)(base + (size_t)(mm0 + row) * a.N + n0 + ch * 8) = *(const u32x4*)(tile + row * BN + ch * 8);
+      *(u32x4*)(base + (size_t)(mm0 + row) * a.N + n0 + ch * 8) =
+          *(const u32x4*)(tile + row * BN + ch * 8);
     }
     return;
   }
@@ -432,12 +497,12 @@ __global__ __launch_bounds__(512) void bwd_gemm_kernel(BwdArgs a) {
       const int col = n0 + wn * TN + j * 32 + fr;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int lr = wm * TM + i * 32 + 8 * (r >> 2) + 4 * fkc + (r & 3);
+        const int lr = (i * WM + wm) * 32 + 8 * (r >> 2) + 4 * fkc + (r & 3);
         const float val = acc[i][j][r];
         if (EPI == EPI_ROWS) {
           const int rg = m_local * BM + lr;
           if (rg < rows) {
-            float* dst = a.ident ? a.out + (size_t)rg * a.N
+            float* dst = a.ident         ? a.out + (size_t)rg * a.N
                          : shared_grp     ? a.out_shared + (size_t)rg * a.N
                                           : a.out + (size_t)(off + rg) * a.N;
             dst[col] = val;
@@ -505,13 +570,16 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const float* __restrict__
   }
 }
 
-// Router backward, one wave per token (4 per workgroup). Lane e (+64 i) recomputes the logit
-// and the softmax probability of expert e exactly as the forward's router does; lanes j < k
-// hold slot j's gate gradient (the sum of its per-n-tile partials, 0 if the slot was dropped).
+// Router backward, one wave per token (each wave takes RT_TOK tokens in turn, so a workgroup
+// covers 4 * RT_TOK). Lane e (+64 i) recomputes the logit and the softmax probability of expert
+// e exactly as the forward's router does; lanes j < k hold slot j's gate gradient (the sum of
+// its per-n-tile partials, 0 if the slot was dropped).
 // d l[e] = sum over slots j choosing e of g_j (dg_j - sum_j' g_j' dg_j')          (gates)
 //        + p_e (w_e - sum_e' p_e' w_e'),  w_e = dL alpha E counts_pre[e] / (T k T)  (balance)
-// Writes d l in bf16 ([T, E_pad], zero past E) and per-workgroup column sums (fp32, for the
-// logit offset's gradient).
+// Writes d l in bf16 ([T, E_pad], zero past E) and per-workgroup column sums (fp32, tokens in
+// order within each wave, then the waves in order) for the logit offset's gradient.
+constexpr int RT_TOK = 4;
+
 __global__ __launch_bounds__(256) void bwd_router_kernel(
     const float* __restrict__ part, int KS, int T, int E, int E16, int k,
     const float* __restrict__ logit_bias, const int32_t* __restrict__ ids,
@@ -520,9 +588,11 @@ __global__ __launch_bounds__(256) void bwd_router_kernel(
     float bal_coef, int E_pad, bf16_t* __restrict__ dlog, float* __restrict__ dlb_part) {
   __shared__ float colsum[4][256];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int t = blockIdx.x * 4 + wave;
-  float dl[4] = {0.f, 0.f, 0.f, 0.f};
-  if (t < T) {                          // uniform across the wave
+  float csum[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int tt = 0; tt < RT_TOK; ++tt) {
+    const int t = (blockIdx.x * 4 + wave) * RT_TOK + tt;
+    if (t >= T) break;                  // uniform across the wave
+    float dl[4] = {0.f, 0.f, 0.f, 0.f};
     float lg[4];
     bool live[4];
 #pragma unroll
@@ -575,15 +645,16 @@ __global__ __launch_bounds__(256) void bwd_router_kernel(
     for (int i = 0; i < 4; ++i) {
       const int e = lane + 64 * i;
       if (e < E_pad) dlog[(size_t)t * E_pad + e] = f32_to_bf16(live[i] ? dl[i] : 0.f);
+      csum[i] += dl[i];
     }
   }
+  if (!dlb_part) return;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) colsum[wave][lane + 64 * i] = dl[i];
+  for (int i = 0; i < 4; ++i) colsum[wave][lane + 64 * i] = csum[i];
   __syncthreads();
-  if (dlb_part)
-    for (int e = threadIdx.x; e < E; e += 256)
-      dlb_part[(size_t)blockIdx.x * E + e] =
-          ((colsum[0][e] + colsum[1][e]) + colsum[2][e]) + colsum[3][e];
+  for (int e = threadIdx.x; e < E; e += 256)
+    dlb_part[(size_t)blockIdx.x * E + e] =
+        ((colsum[0][e] + colsum[1][e]) + colsum[2][e]) + colsum[3][e];
 }
 
 // dx[t] = router share + shared expert's rows + the kept slots' rows in slot order.
@@ -618,19 +689,31 @@ __global__ __launch_bounds__(256) void bwd_dx_kernel(const float* __restrict__ d
   }
 }
 
-template <int BN, int MODE, int AK, int BKIND, int EPI>
-hipError_t launch_gemm(const BwdArgs& a, int tiles, hipStream_t s) {
+// Row-tiled GEMMs (dgrads, router dgrad): 256 x BN tiles, 8 waves (4 x 2), staggered rings.
+template <int BN, int AK, int BKIND, int EPI>
+hipError_t launch_rows(const BwdArgs& a, int tiles, bool deep_rows, hipStream_t s) {
   if (tiles <= 0) return hipSuccess;
-  constexpr int ST = MODE == M_WEIGHTS ? kWgradStages : 3;
-  hipLaunchKernelGGL((bwd_gemm_kernel<BN, MODE, AK, BKIND, EPI, ST>), dim3((tiles + 7) / 8 * 8),
-                     dim3(512), 0, s, a);
+  if (deep_rows)
+    hipLaunchKernelGGL((bwd_gemm_kernel<kRowsBM, BN, 4, 2, M_ROWS, AK, BKIND, EPI, 0, true>),
+                       dim3((tiles + 7) / 8 * 8), dim3(512), 0, s, a);
+  else
+    hipLaunchKernelGGL((bwd_gemm_kernel<kRowsBM, BN, 4, 2, M_ROWS, AK, BKIND, EPI, 0, false>),
+                       dim3((tiles + 7) / 8 * 8), dim3(512), 0, s, a);
+  return hipGetLastError();
+}
+// Weight-gradient GEMMs: 128 x kWgradBN tiles, 8 waves (2 x 4), a kWgradStages ring.
+template <int AK, int BKIND, int EPI>
+hipError_t launch_weights(const BwdArgs& a, int tiles, hipStream_t s) {
+  if (tiles <= 0) return hipSuccess;
+  hipLaunchKernelGGL((bwd_gemm_kernel<BBM, kWgradBN, 2, 4, M_WEIGHTS, AK, BKIND, EPI,
+                                      kWgradStages>),
+                     dim3((tiles + 7) / 8 * 8), dim3(512), 0, s, a);
   return hipGetLastError();
 }
 
 // BN for an output width: 256 when it divides, else 128
 inline int bn_for(int n) { return n % 256 == 0 ? 256 : 128; }
-// BN of the weight-gradient GEMMs (their K, a segment's rows, is short on fine-grained layers)
-inline int wgrad_bn(int n) { return kWgradBN == 256 ? bn_for(n) : 128; }
+
 
 }  // namespace
 
@@ -649,11 +732,16 @@ BwdLayout backward_layout(const moe_problem& p) {
   L.max_mt = max_mtiles((long long)n, p.T, p.E, p.n_shared, BBM);
   const size_t srows = (size_t)L.max_mt * BBM;
   L.NT_down = p.d_ff / bn_for(p.d_ff);
-  L.nblk_router = ceil_div(p.T, 4);
+  L.nblk_router = ceil_div(p.T, 4 * RT_TOK);
   L.grp_rows = take((size_t)G * 4);
   L.grp_off = take((size_t)G * 4);
   L.mt_start = take((size_t)(G + 1) * 4);
   L.mt_group = take((size_t)L.max_mt * 4);
+  L.max_mt_rows = max_mtiles((long long)n, p.T, p.E, p.n_shared, kRowsBM);
+  L.r_grp_rows = take((size_t)G * 4);
+  L.r_grp_off = take((size_t)G * 4);
+  L.r_mt_start = take((size_t)(G + 1) * 4);
+  L.r_mt_group = take((size_t)L.max_mt_rows * 4);
   L.logits_part = take(route_partial_bytes(p));
   L.dlb_part = take((size_t)L.nblk_router * p.E * 4);
   L.zero = take(ZERO_ELEMS * 2);
@@ -694,6 +782,14 @@ hipError_t launch_backward(const moe_problem& p, const BwdLayout& L, void* ws, c
   sc.max_mtiles = L.max_mt;
   sc.G = G;
   sc.BM = BBM;
+  Schedule sr;                        // row tiles of the row-tiled GEMMs
+  sr.grp_rows = (int32_t*)at(L.r_grp_rows);
+  sr.grp_off = (int32_t*)at(L.r_grp_off);
+  sr.mt_start = (int32_t*)at(L.r_mt_start);
+  sr.mt_group = (int32_t*)at(L.r_mt_group);
+  sr.max_mtiles = L.max_mt_rows;
+  sr.G = G;
+  sr.BM = kRowsBM;
   bf16_t* H = (bf16_t*)at(L.H);
   float* U = (float*)at(L.U);
   float* V = (float*)at(L.V);
@@ -721,6 +817,7 @@ hipError_t launch_backward(const moe_problem& p, const BwdLayout& L, void* ws, c
   // 1. schedule (128-row m-tiles) and the gate-up recompute (h, u, v in storage rows)
   MOE_TRY(mark());
   MOE_TRY(launch_schedule(p, offsets, sc, s));
+  MOE_TRY(launch_schedule(p, offsets, sr, s));
   MOE_TRY(launch_expert_ffn(p, x, w1, w3, w2, ws1, ws3, ws2, sorted_assign, sc, H, nullptr,
                             nullptr, nullptr, s, nullptr, 0, U, V));
   MOE_TRY(mark());
@@ -737,11 +834,15 @@ hipError_t launch_backward(const moe_problem& p, const BwdLayout& L, void* ws, c
   c.T = p.T;
   c.sorted_assign = sorted_assign;
   c.sc = sc;
+  c.stor_start = sc.mt_start;
   c.zero = zero;
-  const int mt_max = L.max_mt;
+  BwdArgs cr = c;                     // row-tiled GEMMs walk the row-tile schedule
+  cr.sc = sr;
+  // rows in the deep ring when the weight tiles are shared in L2 by several m-tiles
+  const bool deep_rows = kDeepRowsFrom >= 0 && gemm_wide(p);
   // 3. dgrad-down + SwiGLU backward: d h' = dy_t W2, then du, dv, d g partials
   {
-    BwdArgs a = c;
+    BwdArgs a = cr;
     a.A = dyb;
     a.lda = p.d;
     a.B0 = (const bf16_t*)w2;
@@ -756,15 +857,15 @@ hipError_t launch_backward(const moe_problem& p, const BwdLayout& L, void* ws, c
     a.DUV = DUV;
     a.dgate_part = dgate_part;
     a.NT = L.NT_down;
-    const int tiles = mt_max * L.NT_down;
-    err = (L.NT_down * 256 == p.d_ff) ? launch_gemm<256, M_ROWS, A_TOKEN, B_W2, EPI_DDOWN>(a, tiles, s)
-                             : launch_gemm<128, M_ROWS, A_TOKEN, B_W2, EPI_DDOWN>(a, tiles, s);
+    const int tiles = L.max_mt_rows * L.NT_down;
+    err = (L.NT_down * 256 == p.d_ff) ? launch_rows<256, A_TOKEN, B_W2, EPI_DDOWN>(a, tiles, deep_rows, s)
+                                      : launch_rows<128, A_TOKEN, B_W2, EPI_DDOWN>(a, tiles, deep_rows, s);
     MOE_TRY(err);
   }
   MOE_TRY(mark());
   // 4. dgrad-x: (du | dv) (W1; W3) -> per-row dx (sorted order) and the shared rows
   {
-    BwdArgs a = c;
+    BwdArgs a = cr;
     a.A = DUV;
     a.lda = 2 * p.d_ff;
     a.B0 = (const bf16_t*)w1;
@@ -777,9 +878,9 @@ hipError_t launch_backward(const moe_problem& p, const BwdLayout& L, void* ws, c
     a.out = dx_rows;
     a.out_shared = dx_shared;
     const int bn = bn_for(p.d);
-    const int tiles = mt_max * (p.d / bn);
-    err = (bn == 256) ? launch_gemm<256, M_ROWS, A_STORE, B_W13, EPI_ROWS>(a, tiles, s)
-                             : launch_gemm<128, M_ROWS, A_STORE, B_W13, EPI_ROWS>(a, tiles, s);
+    const int tiles = L.max_mt_rows * (p.d / bn);
+    err = (bn == 256) ? launch_rows<256, A_STORE, B_W13, EPI_ROWS>(a, tiles, deep_rows, s)
+                      : launch_rows<128, A_STORE, B_W13, EPI_ROWS>(a, tiles, deep_rows, s);
     MOE_TRY(err);
   }
   MOE_TRY(mark());
@@ -795,10 +896,8 @@ hipError_t launch_backward(const moe_problem& p, const BwdLayout& L, void* ws, c
     a.W0 = (bf16_t*)dw2;
     a.SW0 = (bf16_t*)dws2;
     a.Msplit = p.d;
-    const int bn = wgrad_bn(p.d_ff);
-    const int tiles = G * (p.d / BBM) * (p.d_ff / bn);
-    err = (bn == 256) ? launch_gemm<256, M_WEIGHTS, AT_STORE, BT_STORE, EPI_WBF16>(a, tiles, s)
-                             : launch_gemm<128, M_WEIGHTS, AT_STORE, BT_STORE, EPI_WBF16>(a, tiles, s);
+    const int tiles = G * (p.d / BBM) * (p.d_ff / kWgradBN);
+    err = launch_weights<AT_STORE, BT_STORE, EPI_WBF16>(a, tiles, s);
     MOE_TRY(err);
   }
   MOE_TRY(mark());
@@ -816,10 +915,8 @@ hipError_t launch_backward(const moe_problem& p, const BwdLayout& L, void* ws, c
     a.SW0 = (bf16_t*)dws1;
     a.SW1 = (bf16_t*)dws3;
     a.Msplit = p.d_ff;
-    const int bn = wgrad_bn(p.d);
-    const int tiles = G * (2 * p.d_ff / BBM) * (p.d / bn);
-    err = (bn == 256) ? launch_gemm<256, M_WEIGHTS, AT_STORE, BT_STORE, EPI_WBF16>(a, tiles, s)
-                             : launch_gemm<128, M_WEIGHTS, AT_STORE, BT_STORE, EPI_WBF16>(a, tiles, s);
+    const int tiles = G * (2 * p.d_ff / BBM) * (p.d / kWgradBN);
+    err = launch_weights<AT_STORE, BT_STORE, EPI_WBF16>(a, tiles, s);
     MOE_TRY(err);
   }
   MOE_TRY(mark());
@@ -849,9 +946,9 @@ hipError_t launch_backward(const moe_problem& p, const BwdLayout& L, void* ws, c
     a.ident_rows = p.T;
     a.out = dx_router;
     const int bn = bn_for(p.d);
-    const int tiles = ceil_div(p.T, BBM) * (p.d / bn);
-    err = (bn == 256) ? launch_gemm<256, M_ROWS, A_IDENT, B_WGATE, EPI_ROWS>(a, tiles, s)
-                             : launch_gemm<128, M_ROWS, A_IDENT, B_WGATE, EPI_ROWS>(a, tiles, s);
+    const int tiles = ceil_div(p.T, kRowsBM) * (p.d / bn);
+    err = (bn == 256) ? launch_rows<256, A_IDENT, B_WGATE, EPI_ROWS>(a, tiles, true, s)
+                      : launch_rows<128, A_IDENT, B_WGATE, EPI_ROWS>(a, tiles, true, s);
     MOE_TRY(err);
   }
   MOE_TRY(mark());
@@ -868,11 +965,9 @@ hipError_t launch_backward(const moe_problem& p, const BwdLayout& L, void* ws, c
     a.ident_rows = p.T;
     a.Wf = dw_gate;
     a.Mvalid = p.E;
-    const int bn = wgrad_bn(p.d);
-    const int tiles = (L.E_pad / BBM) * (p.d / bn);
+    const int tiles = (L.E_pad / BBM) * (p.d / kWgradBN);
     // (T = 0: the K loop is empty and every tile writes zeros)
-    err = (bn == 256) ? launch_gemm<256, M_WEIGHTS, AT_IDENT, BT_IDENT, EPI_WF32>(a, tiles, s)
-                             : launch_gemm<128, M_WEIGHTS, AT_IDENT, BT_IDENT, EPI_WF32>(a, tiles, s);
+    err = launch_weights<AT_IDENT, BT_IDENT, EPI_WF32>(a, tiles, s);
     MOE_TRY(err);
   }
   MOE_TRY(mark());

@@ -148,9 +148,10 @@ hipError_t launch_bias_update(const moe_problem& p, const int32_t* counts_pre, f
 // Workspace of the layer backward (byte offsets; bf16 storage only).
 struct BwdLayout {
   size_t grp_rows, grp_off, mt_start, mt_group, logits_part, dlb_part, zero;
+  size_t r_grp_rows, r_grp_off, r_mt_start, r_mt_group;   // the row-tile schedule
   size_t H, U, V, DUV, DO, XS, dyb, dgate_part, dx_rows, dx_shared, dlog, dx_router;
   size_t total;
-  int max_mt, E_pad, NT_down, nblk_router;
+  int max_mt, max_mt_rows, E_pad, NT_down, nblk_router;
 };
 BwdLayout backward_layout(const moe_problem& p);
 hipError_t launch_backward(const moe_problem& p, const BwdLayout& L, void* ws, const void* x,

@@ -157,3 +157,47 @@ def test_expert_choice_capacity_matches_oracle(moe):
         p = moe.make_problem(T, d, E, k, 256, capacity_factor=cf)
         assert moe.expert_choice_capacity(p) == oracle.expert_choice_capacity(cf, T, k, E)
     assert moe.expert_choice_workspace_bytes(moe.make_problem(4096, 256, 8, 2, 256)) > 0
+
+
+def test_backward_validation_returns_before_any_launch(moe):
+    """moe_backward's argument errors come back on the host, before anything is enqueued."""
+    lib = moe.lib()
+    f = ctypes.c_float
+    fake = ctypes.c_void_p(0x1000)          # never dereferenced: validation fails first
+    null = None
+    p = moe.make_problem(16, 256, 8, 2, 256)
+
+    def call(prob, ptrs=None, alpha=0.01, dL=1.0, ws_bytes=1 << 40, staged=None):
+        ptrs = list(ptrs if ptrs is not None else [fake] * 16)
+        outs = [fake, fake, null, fake, fake, fake, null, null, null]   # dx .. dws2
+        args = [ctypes.byref(prob)] + ptrs + [f(alpha), f(dL)] + outs + [fake, ws_bytes, null]
+        if staged is not None:
+            return lib.moe_backward_staged(*args, staged)
+        return lib.moe_backward(*args)
+
+    # fp32 storage and k > 16 are not supported
+    assert call(moe.make_problem(16, 256, 8, 2, 256, dtype="f32")) == moe.MOE_EUNSUPPORTED
+    assert call(moe.make_problem(16, 256, 32, 17, 256)) == moe.MOE_EUNSUPPORTED
+    # a missing required input (x) or a non-finite alpha / dL
+    ptrs = [fake] * 16
+    ptrs[0] = null
+    assert call(p, ptrs) == moe.MOE_EINVAL
+    assert call(p, alpha=float("nan")) == moe.MOE_EINVAL
+    assert call(p, dL=float("inf")) == moe.MOE_EINVAL
+    # shared expert declared but its weights (and gradient outputs) missing
+    ps = moe.make_problem(16, 256, 8, 2, 256, n_shared=1, d_ff_shared=256)
+    ptrs = [fake] * 16
+    ptrs[6] = ptrs[7] = ptrs[8] = null
+    assert call(ps, ptrs) == moe.MOE_EINVAL
+    # workspace too small
+    assert call(p, ws_bytes=16) == moe.MOE_EWORKSPACE
+    # staged: a NULL events array
+    assert lib.moe_backward_staged(ctypes.byref(p), *([fake] * 16), f(0.01), f(1.0), fake, fake,
+                                   null, fake, fake, fake, null, null, null, fake, 1 << 40, null,
+                                   null) == moe.MOE_EINVAL
+    # workspace size: bf16 only, grows with T
+    a = moe.backward_workspace_bytes(moe.make_problem(16, 256, 8, 2, 256))
+    b = moe.backward_workspace_bytes(moe.make_problem(1024, 256, 8, 2, 256))
+    assert 0 < a < b
+    with pytest.raises(moe.MoEError):
+        moe.backward_workspace_bytes(moe.make_problem(16, 256, 8, 2, 256, dtype="f32"))

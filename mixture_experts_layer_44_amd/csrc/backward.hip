@@ -515,6 +515,189 @@ __global__ __launch_bounds__(WM * WN * 64) void bwd_gemm_kernel(BwdArgs a) {
     }
 }
 
+// Persistent weight-gradient GEMM (bf16 output, storage-row operands): workgroup run r takes
+// output tiles (group, 128-row m-tile, 128-column n-tile) r, r + nwg, r + 2 nwg, ... (so every
+// workgroup gets a mix of long and short segments, and at any moment the workgroups of one XCD
+// work on consecutive tiles that share their row operand in L2), and walks all of their K
+// steps (a segment's rows, 64 at a time) as one stream through a 4-slot ring, three steps in
+// flight across tile boundaries. A tile's last step is followed by its epilogue:
+// the tile goes through a dedicated LDS buffer and out in 16-byte row pieces. A tile whose
+// group has no rows still takes one step of zero rows (its gradient is zero).
+
+struct WTile {
+  int g, m0, n0, rows, sbase, kt_n;
+};
+
+__device__ __forceinline__ WTile wgrad_tile(const BwdArgs& a, int L, int MT, int NT) {
+  WTile t;
+  t.g = L / (MT * NT);
+  const int rem = L - t.g * MT * NT;
+  const int mt = rem / NT;
+  t.m0 = mt * BBM;
+  t.n0 = (rem - mt * NT) * 128;
+  t.rows = a.sc.grp_rows[t.g];
+  t.sbase = a.sc.mt_start[t.g] * BBM;
+  t.kt_n = max(1, (t.rows + 63) / 64);
+  return t;
+}
+
+// WG_SLOTS = 4: three steps in flight, the output stage in its own 32 KB (160 KB, one
+// workgroup per CU). WG_SLOTS = 2: one step in flight, the output staged in the slot the
+// tile's last step just used (64 KB, two workgroups per CU).
+template <int WG_SLOTS>
+__global__ __launch_bounds__(512) void bwd_wgrad_kernel(BwdArgs a) {
+  constexpr int BM = BBM, BN = 128, BK = 64, WM = 2, WN = 4, NW = 8, NKS = BK / 16;
+  constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
+  constexpr int ASZ = BM * BK, BSZ = BN * BK, SLOT = ASZ + BSZ;
+  constexpr int DMA_A = ASZ * 2 / 1024 / NW, DMA_B = BSZ * 2 / 1024 / NW;
+  constexpr bool OWN_STAGE = WG_SLOTS > 2;
+  static_assert(SLOT >= BM * BN, "a ring slot holds the output tile");
+  static_assert((WG_SLOTS * SLOT + (OWN_STAGE ? BM * BN : 0)) * 2 <= 160 * 1024, "LDS budget");
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[WG_SLOTS * SLOT + (OWN_STAGE ? BM * BN : 0)];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int MT = a.M / BM, NT = a.N / BN, total = a.sc.G * MT * NT;
+  // workgroup b runs on XCD b % 8; run (b % 8) * per + b / 8 keeps an XCD's runs consecutive
+  const int nwg = gridDim.x, per = nwg >> 3;
+  const int L0 = (blockIdx.x & 7) * per + (blockIdx.x >> 3);
+  if (L0 >= total) return;
+
+  // per-lane load geometry (transposed [64 k][128] stages for both operands)
+  int akrow[DMA_A], alch[DMA_A], bkrow[DMA_B], blch[DMA_B];
+#pragma unroll
+  for (int i = 0; i < DMA_A; ++i) {
+    akrow[i] = (wave * DMA_A + i) * 4 + lane / 16;
+    alch[i] = (lane % 16) ^ ((akrow[i] & 3) << 2);
+  }
+#pragma unroll
+  for (int i = 0; i < DMA_B; ++i) {
+    bkrow[i] = (wave * DMA_B + i) * 4 + lane / 16;
+    blch[i] = (lane % 16) ^ ((bkrow[i] & 3) << 2);
+  }
+  auto issue = [&](const WTile& t, int kt, int slot) {
+    bf16_t* dA = smem + slot * SLOT;
+    bf16_t* dB = dA + ASZ;
+#pragma unroll
+    for (int i = 0; i < DMA_A; ++i) {
+      const int r = kt * BK + akrow[i];
+      const bf16_t* src = r < t.rows
+          ? a.A + (uint32_t)(t.sbase + r) * (uint32_t)a.lda + t.m0 + alch[i] * 8
+          : a.zero + alch[i] * 8;
+      __builtin_amdgcn_global_load_lds((const void*)src,
+                                       (lds_ptr_t)(dA + (wave * DMA_A + i) * 512), 16, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < DMA_B; ++i) {
+      const int r = kt * BK + bkrow[i];
+      const bf16_t* src = r < t.rows
+          ? a.B0 + (uint32_t)(t.sbase + r) * (uint32_t)a.ldb + t.n0 + blch[i] * 8
+          : a.zero + blch[i] * 8;
+      __builtin_amdgcn_global_load_lds((const void*)src,
+                                       (lds_ptr_t)(dB + (wave * DMA_B + i) * 512), 16, 0, 0);
+    }
+  };
+
+  int abase[FM], bbase[FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) abase[i] = tr_base<BM>(lane, (i * WM + wm) * 32);
+#pragma unroll
+  for (int j = 0; j < FN; ++j) bbase[j] = tr_base<BN>(lane, wn * TN + j * 32);
+  const int fr = lane & 31, fkc = lane >> 5;
+
+  f32x16 acc[FM][FN];
+  auto zero_acc = [&]() {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+  };
+  zero_acc();
+
+  // issue side: tile iL, step ikt (past the last tile: repeat the last step into a dead slot)
+  int iL = L0, ikt = 0;
+  WTile it = wgrad_tile(a, iL, MT, NT);
+  WTile last_it = it;
+  int last_kt = 0;
+  auto issue_next = [&](int slot) {
+    if (iL < total) {
+      issue(it, ikt, slot);
+      last_it = it;
+      last_kt = ikt;
+      if (++ikt == it.kt_n) {
+        ikt = 0;
+        iL += nwg;
+        if (iL < total) it = wgrad_tile(a, iL, MT, NT);
+      }
+    } else {
+      issue(last_it, last_kt, slot);
+    }
+  };
+#pragma unroll
+  for (int s = 0; s < WG_SLOTS - 1; ++s) issue_next(s);
+
+  // compute side
+  int cL = L0, ckt = 0;
+  WTile ct = wgrad_tile(a, cL, MT, NT);
+  for (int step = 0; cL < total; ++step) {
+    __builtin_amdgcn_s_waitcnt(wait_vm((WG_SLOTS - 2) * (DMA_A + DMA_B)));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    issue_next((step + WG_SLOTS - 1) % WG_SLOTS);
+    const bf16_t* As = smem + (step % WG_SLOTS) * SLOT;
+    const bf16_t* Bs = As + ASZ;
+    __builtin_amdgcn_iglp_opt(1);
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      bf16x8 af[FM], bfv[FN];
+#pragma unroll
+      for (int i = 0; i < FM; ++i) af[i] = tr_frag<BM>(As, abase[i], ks);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) bfv[j] = tr_frag<BN>(Bs, bbase[j], ks);
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfv[j], acc[i][j], 0, 0, 0);
+    }
+    if (++ckt < ct.kt_n) continue;
+    // ---- epilogue of tile cL: bf16 through the output stage, then 16-byte row pieces.
+    // (The previous epilogue's reads of the stage finished before this step's barrier. With the
+    // stage in this step's slot, every wave must first be done with its MFMA reads of it; the
+    // slot is loaded again only after the next step's barrier.)
+    bf16_t* const outst = OWN_STAGE ? smem + WG_SLOTS * SLOT : smem + (step % WG_SLOTS) * SLOT;
+    if (!OWN_STAGE) __syncthreads();
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int lr = (i * WM + wm) * 32 + 8 * (r >> 2) + 4 * fkc + (r & 3);
+          outst[lr * BN + wn * TN + j * 32 + fr] = f32_to_bf16(acc[i][j][r]);
+        }
+    zero_acc();
+    __syncthreads();
+    const bool shared_grp = ct.g >= a.E;
+    const bool second = ct.m0 >= a.Msplit;
+    const int mm0 = second ? ct.m0 - a.Msplit : ct.m0;
+    bf16_t* base = shared_grp ? (second ? a.SW1 : a.SW0)
+                              : (second ? a.W1 : a.W0) + (size_t)ct.g * a.Msplit * a.N;
+    for (int idx = tid; idx < BM * BN / 8; idx += NW * 64) {
+      const int row = idx / (BN / 8), ch = idx % (BN / 8);
+      *(u32x4*)(base + (size_t)(mm0 + row) * a.N + ct.n0 + ch * 8) =
+          *(const u32x4*)(outst + row * BN + ch * 8);
+    }
+    ckt = 0;
+    cL += nwg;
+    if (cL < total) ct = wgrad_tile(a, cL, MT, NT);
+  }
+  __builtin_amdgcn_s_waitcnt(wait_vm(0));   // the dead loads past the last step
+}
+
 // ------------------------------------------------------------------ small kernels
 // Items 0..T-1: dy row t -> bf16. Items T..: storage rows s of the grouped layout: routed row
 // (group g, row r) -> assignment a = sorted_assign[off + r], token t = a / k, gate g_a:
@@ -711,6 +894,20 @@ hipError_t launch_weights(const BwdArgs& a, int tiles, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Persistent weight-gradient GEMM: kWgradPerCU workgroups per CU.
+constexpr int kWgradPerCU = 2;
+hipError_t launch_wgrad(const BwdArgs& a, hipStream_t s) {
+  constexpr int kCUs = 256;                 // MI355X compute units
+  const long long total = (long long)a.sc.G * (a.M / BBM) * (a.N / 128);
+  if (total <= 0) return hipSuccess;
+  const int nwg = (int)std::min<long long>(kCUs * kWgradPerCU, (total + 7) / 8 * 8);
+  if (kWgradPerCU == 1)
+    hipLaunchKernelGGL(bwd_wgrad_kernel<4>, dim3(nwg), dim3(512), 0, s, a);
+  else
+    hipLaunchKernelGGL(bwd_wgrad_kernel<2>, dim3(nwg), dim3(512), 0, s, a);
+  return hipGetLastError();
+}
+
 // BN for an output width: 256 when it divides, else 128
 inline int bn_for(int n) { return n % 256 == 0 ? 256 : 128; }
 
@@ -896,8 +1093,7 @@ hipError_t launch_backward(const moe_problem& p, const BwdLayout& L, void* ws, c
     a.W0 = (bf16_t*)dw2;
     a.SW0 = (bf16_t*)dws2;
     a.Msplit = p.d;
-    const int tiles = G * (p.d / BBM) * (p.d_ff / kWgradBN);
-    err = launch_weights<AT_STORE, BT_STORE, EPI_WBF16>(a, tiles, s);
+    err = launch_wgrad(a, s);
     MOE_TRY(err);
   }
   MOE_TRY(mark());
@@ -915,8 +1111,7 @@ hipError_t launch_backward(const moe_problem& p, const BwdLayout& L, void* ws, c
     a.SW0 = (bf16_t*)dws1;
     a.SW1 = (bf16_t*)dws3;
     a.Msplit = p.d_ff;
-    const int tiles = G * (2 * p.d_ff / BBM) * (p.d / kWgradBN);
-    err = launch_weights<AT_STORE, BT_STORE, EPI_WBF16>(a, tiles, s);
+    err = launch_wgrad(a, s);
     MOE_TRY(err);
   }
   MOE_TRY(mark());

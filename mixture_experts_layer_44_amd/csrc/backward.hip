@@ -15,18 +15,22 @@
 //   dx += d l W_gate, dW_gate = d l^T x, d logit_bias = column sums of d l.
 //
 // Storage. Every per-row activation lives in "storage rows": group g's rows r = 0..rows_g-1
-// at row mt_start[g] * 128 + r of a [m-tiles * 128, width] buffer (the 128-row schedule of the
-// grouped GEMMs; the shared expert is group E). The recompute of the gate-up GEMM writes
+// at row mt_start[g] * SB + r of a [m-tiles * SB, width] buffer, where SB and mt_start are the
+// forward's own m-tile schedule (the shared expert is group E). The recompute of the gate-up
+// GEMM (the forward's kernel, tile for tile) writes
 // h (bf16) and u, v (fp32) there; a prep kernel writes g * dy (bf16) and the gathered x rows
 // (bf16) there, and dy once in bf16 in token order.
 //
-// GEMMs (one template, bf16 MFMA 32x32x16, fp32 accumulation, 128 x BN tiles, 8 waves, BK 64,
-// a 3-stage ring of direct global->LDS loads):
+// GEMMs (bf16 MFMA 32x32x16, fp32 accumulation, BK 64, direct global->LDS loads):
 //   dgrad-down  [rows x d_ff] = dy_tok [rows x d] . W2_e [d x d_ff]   + SwiGLU backward epilogue
 //   dgrad-x     [rows x d]    = (du|dv) [rows x 2 d_ff] . (W1_e;W3_e) [2 d_ff x d]
+//   router      dx_r [T x d]  = d l [T x E] . W_gate [E x d]
+//     -- row-tiled (bwd_gemm_kernel): 256 x BN tiles, 8 waves of 64 x 128, staggered rings,
+//        ragged last tiles
 //   wgrad-down  dW2_e [d x d_ff]     = (g dy)^T [d x rows] . h [rows x d_ff]
 //   wgrad-up    (dW1_e;dW3_e) [2 d_ff x d] = (du|dv)^T . x_gathered [rows x d]
-//   router      dx_r [T x d] = d l [T x E] . W_gate [E x d];  dW_gate = d l^T x  (K = T)
+//     -- persistent (bwd_wgrad_kernel): 128 x 128 tiles streamed through a 2-slot ring
+//   router      dW_gate = d l^T x  (K = T) -- bwd_gemm_kernel's weights mode
 // Every weight and activation stays in its forward layout in HBM. An operand whose contraction
 // index is its row index ("transposed": the weights in dgrad, everything in wgrad) is staged
 // into LDS as [k][m] rows, as it lies in memory, and read with ds_read_b64_tr_b16: within each
@@ -49,11 +53,10 @@ typedef short v4s __attribute__((ext_vector_type(4)));
 typedef short v8s __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) v4s* lds_v4s_ptr;
 
-constexpr int BBM = 128;   // rows of every backward m-tile (the schedule's BM)
-// The weight-gradient GEMMs contract over a segment's rows, often only one or two K steps:
-// their time goes into each tile's load latency and output writes, not MFMAs. A 2-stage ring
-// of 128 x 128 tiles (64 KB of LDS) lets two workgroups share a CU and overlap one's loads
-// with the other's writes; measured faster than 3 stages or 256-wide tiles on every layer.
+constexpr int BBM = 128;   // rows of a weight-gradient m-tile (rows of the weight matrix)
+// The router's weight gradient (K = T) runs as a launched 128 x 128 tile with a 2-stage ring
+// (64 KB of LDS, two workgroups per CU). The experts' weight gradients use the persistent
+// kernel (bwd_wgrad_kernel).
 constexpr int kWgradStages = 2;
 constexpr int kWgradBN = 128;
 constexpr int kRowsBM = 256;      // m-tile of the row-tiled GEMMs (ragged, staggered rings)
@@ -62,7 +65,7 @@ constexpr int ZERO_ELEMS = 256;
 
 enum AKind : int { A_TOKEN, A_STORE, A_IDENT, AT_STORE, AT_IDENT };
 enum BKind : int { B_W2, B_W13, B_WGATE, BT_STORE, BT_IDENT };
-enum EpiKind : int { EPI_DDOWN, EPI_ROWS, EPI_WBF16, EPI_WF32 };
+enum EpiKind : int { EPI_DDOWN, EPI_ROWS, EPI_WF32 };
 enum ModeKind : int { M_ROWS, M_WEIGHTS };
 
 struct BwdArgs {
@@ -81,10 +84,12 @@ struct BwdArgs {
   int Kvalid;               // B_WGATE: rows of B that exist (E)
   const int32_t* sorted_assign;
   Schedule sc;              // rows mode: the row-tile schedule; weights mode: the storage one
-  const int32_t* stor_start;   // the storage schedule's m-tile starts (128-row storage)
+  const int32_t* stor_start;   // the storage schedule's m-tile starts
+  int stor_bm;                 // its m-tile height: group g's row r is storage row
+                               // stor_start[g] * stor_bm + r
   float* out;               // EPI_ROWS: routed rows (sorted order) or identity rows
   float* out_shared;        // EPI_ROWS: the shared expert's rows (token order)
-  bf16_t* W0;               // EPI_WBF16: routed dW, output rows < Msplit
+  bf16_t* W0;               // bf16 weight gradient (persistent kernel): routed, rows < Msplit
   bf16_t* W1;               //            routed dW, output rows >= Msplit
   bf16_t* SW0;              //            shared expert, rows < Msplit
   bf16_t* SW1;              //            shared expert, rows >= Msplit
@@ -151,7 +156,6 @@ __global__ __launch_bounds__(WM * WN * 64) void bwd_gemm_kernel(BwdArgs a) {
   static_assert(FM >= 1 && FN >= 1 && FM <= 3, "wave tile covers whole fragments");
   static_assert(!STAG || (MODE == M_ROWS && !ATR), "staggered rings: rows mode only");
   static_assert((NA * ASZ + NB * BSZ) * 2 <= 160 * 1024, "rings fit in LDS");
-  static_assert(NA * ASZ + NB * BSZ >= BM * BN, "the ring holds the staged output tile");
   static_assert(EPI != EPI_DDOWN || (NA * ASZ + NB * BSZ) * 2 >= (WN + 1) * BM * 4,
                 "the ring holds the epilogue's row sums");
   __shared__ __attribute__((aligned(1024))) bf16_t smem[NA * ASZ + NB * BSZ];
@@ -186,8 +190,8 @@ __global__ __launch_bounds__(WM * WN * 64) void bwd_gemm_kernel(BwdArgs a) {
       rows = tc.rows;
       off = tc.off;
     }
-    // rows of this group are stored from storage row sbase (the 128-row storage schedule)
-    sbase = a.ident ? 0 : a.stor_start[g] * BBM;
+    // rows of this group are stored from storage row sbase (the storage schedule)
+    sbase = a.ident ? 0 : a.stor_start[g] * a.stor_bm;
   } else {
     const int G = a.ident ? 1 : a.sc.G;
     const int MT = a.M / BM, NTt = a.N / BN, total = G * MT * NTt;
@@ -201,7 +205,7 @@ __global__ __launch_bounds__(WM * WN * 64) void bwd_gemm_kernel(BwdArgs a) {
     m0 = mt * BM;
     n0 = (rem - mt * NTt) * BN;
     rows = a.ident ? a.ident_rows : a.sc.grp_rows[g];
-    sbase = a.ident ? 0 : a.sc.mt_start[g] * BBM;
+    sbase = a.ident ? 0 : a.stor_start[g] * a.stor_bm;
   }
   const bool shared_grp = !a.ident && g >= a.E;
   const int KT = MODE == M_ROWS ? a.K / BK : (rows + BK - 1) / BK;
@@ -462,34 +466,6 @@ __global__ __launch_bounds__(WM * WN * 64) void bwd_gemm_kernel(BwdArgs a) {
     return;
   }
 
-  if (EPI == EPI_WBF16) {
-    // bf16 weight-gradient tile: staged through LDS (the ring is idle now) so that every lane
-    // writes whole 16-byte pieces of output rows. The tile lies in one output matrix (Msplit
-    // is a multiple of BM).
-    bf16_t* tile = smem;                   // [BM][BN]
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int lr = (i * WM + wm) * 32 + 8 * (r >> 2) + 4 * fkc + (r & 3);
-          tile[lr * BN + wn * TN + j * 32 + fr] = f32_to_bf16(acc[i][j][r]);
-        }
-    __syncthreads();
-    const bool second = m0 >= a.Msplit;
-    const int mm0 = second ? m0 - a.Msplit : m0;
-    bf16_t* base = shared_grp ? (second ? a.SW1 : a.SW0)
-                              : (second ? a.W1 : a.W0) + (size_t)g * a.Msplit * a.N;
-    constexpr int CH = BN / 8;              // 16-byte pieces per tile row
-    for (int idx = tid; idx < BM * CH; idx += NW * 64) {
-      const int row = idx / CH, ch = idx % CH;
-      *(u32x4*)(base + (size_t)(mm0 + row) * a.N + n0 + ch * 8) =
-          *(const u32x4*)(tile + row * BN + ch * 8);
-    }
-    return;
-  }
-
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -536,7 +512,7 @@ __device__ __forceinline__ WTile wgrad_tile(const BwdArgs& a, int L, int MT, int
   t.m0 = mt * BBM;
   t.n0 = (rem - mt * NT) * 128;
   t.rows = a.sc.grp_rows[t.g];
-  t.sbase = a.sc.mt_start[t.g] * BBM;
+  t.sbase = a.stor_start[t.g] * a.stor_bm;
   t.kt_n = max(1, (t.rows + 63) / 64);
   return t;
 }
@@ -713,7 +689,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const float* __restrict__
                                                        bf16_t* __restrict__ XS,
                                                        bf16_t* __restrict__ zero) {
   if (blockIdx.x == 0 && threadIdx.x < ZERO_ELEMS) zero[threadIdx.x] = 0;
-  const int total = T + sc.mt_start[sc.G] * BBM;
+  const int SB = sc.BM;                 // storage rows per m-tile
+  const int total = T + sc.mt_start[sc.G] * SB;
   const int d4 = d >> 2;
   for (int item = blockIdx.x; item < total; item += gridDim.x) {
     if (item < T) {
@@ -729,8 +706,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const float* __restrict__
       continue;
     }
     const int s = item - T;
-    const int mt = s / BBM, g = sc.mt_group[mt];
-    const int r = (mt - sc.mt_start[g]) * BBM + s % BBM;
+    const int mt = s / SB, g = sc.mt_group[mt];
+    const int r = (mt - sc.mt_start[g]) * SB + s % SB;
     if (r >= sc.grp_rows[g]) continue;
     int t = r;
     float gate = 1.f;
@@ -884,7 +861,7 @@ hipError_t launch_rows(const BwdArgs& a, int tiles, bool deep_rows, hipStream_t 
                        dim3((tiles + 7) / 8 * 8), dim3(512), 0, s, a);
   return hipGetLastError();
 }
-// Weight-gradient GEMMs: 128 x kWgradBN tiles, 8 waves (2 x 4), a kWgradStages ring.
+// The router's weight-gradient GEMM: 128 x kWgradBN tiles, 8 waves (2 x 4), a kWgradStages ring.
 template <int AK, int BKIND, int EPI>
 hipError_t launch_weights(const BwdArgs& a, int tiles, hipStream_t s) {
   if (tiles <= 0) return hipSuccess;
@@ -926,8 +903,11 @@ BwdLayout backward_layout(const moe_problem& p) {
   const size_t n = (size_t)p.T * p.k;
   const int G = p.E + p.n_shared;
   L.E_pad = ceil_div(p.E, 128) * 128;
-  L.max_mt = max_mtiles((long long)n, p.T, p.E, p.n_shared, BBM);
-  const size_t srows = (size_t)L.max_mt * BBM;
+  // storage rows follow the forward's own m-tile class, so the recompute is the forward's
+  // gate-up GEMM, tile for tile
+  L.stor_bm = gemm_bm(p);
+  L.max_mt = max_mtiles((long long)n, p.T, p.E, p.n_shared, L.stor_bm);
+  const size_t srows = (size_t)L.max_mt * L.stor_bm;
   L.NT_down = p.d_ff / bn_for(p.d_ff);
   L.nblk_router = ceil_div(p.T, 4 * RT_TOK);
   L.grp_rows = take((size_t)G * 4);
@@ -978,7 +958,7 @@ hipError_t launch_backward(const moe_problem& p, const BwdLayout& L, void* ws, c
   sc.mt_group = (int32_t*)at(L.mt_group);
   sc.max_mtiles = L.max_mt;
   sc.G = G;
-  sc.BM = BBM;
+  sc.BM = L.stor_bm;
   Schedule sr;                        // row tiles of the row-tiled GEMMs
   sr.grp_rows = (int32_t*)at(L.r_grp_rows);
   sr.grp_off = (int32_t*)at(L.r_grp_off);
@@ -1011,7 +991,8 @@ hipError_t launch_backward(const moe_problem& p, const BwdLayout& L, void* ws, c
     if ((err = (call)) != hipSuccess) \
       return err;                      \
   } while (0)
-  // 1. schedule (128-row m-tiles) and the gate-up recompute (h, u, v in storage rows)
+  // 1. schedules (storage = the forward's class; 256-row tiles) and the gate-up recompute
+  //    (h, u, v in storage rows)
   MOE_TRY(mark());
   MOE_TRY(launch_schedule(p, offsets, sc, s));
   MOE_TRY(launch_schedule(p, offsets, sr, s));
@@ -1019,7 +1000,7 @@ hipError_t launch_backward(const moe_problem& p, const BwdLayout& L, void* ws, c
                             nullptr, nullptr, s, nullptr, 0, U, V));
   MOE_TRY(mark());
   // 2. dy in bf16, g dy and the gathered x rows in storage rows
-  hipLaunchKernelGGL(bwd_prep_kernel, dim3(std::min(p.T + L.max_mt * BBM, 16384)), dim3(256), 0,
+  hipLaunchKernelGGL(bwd_prep_kernel, dim3(std::min(p.T + L.max_mt * L.stor_bm, 16384)), dim3(256), 0,
                      s, dy, (const bf16_t*)x, sorted_assign, topk_w, sc, p.T, p.d, p.k, p.E, dyb,
                      DO, XS, zero);
   MOE_TRY(hipGetLastError());
@@ -1032,6 +1013,7 @@ hipError_t launch_backward(const moe_problem& p, const BwdLayout& L, void* ws, c
   c.sorted_assign = sorted_assign;
   c.sc = sc;
   c.stor_start = sc.mt_start;
+  c.stor_bm = L.stor_bm;
   c.zero = zero;
   BwdArgs cr = c;                     // row-tiled GEMMs walk the row-tile schedule
   cr.sc = sr;

@@ -91,6 +91,8 @@ CASES = [
     W("bwd_long_segments", T=1600, d=512, E=4, k=2, d_ff=384, seed=507, n_shared=1,
       d_ff_shared=384),
     W("bwd_k_eq_E", T=100, d=128, E=8, k=8, d_ff=128, seed=508),
+    # ~150 rows per expert: the recompute runs the forward's ragged 192-row class
+    W("bwd_mid192", T=600, d=512, E=8, k=2, d_ff=384, seed=511, n_shared=1, d_ff_shared=384),
 ]
 
 

@@ -122,6 +122,62 @@ __device__ __forceinline__ bf16x8 tr_frag(const bf16_t* st, int base, int ks) {
   return __builtin_bit_cast(bf16x8, c);
 }
 
+// The same reads for NF operand blocks at once, written as one asm block that ends with its own
+// lgkmcnt wait (so its outputs are complete when it ends). The outputs are early-clobber: a read
+// may return while a later read of the block has not yet taken its address. The builtin above makes the compiler
+// drain every in-flight global->LDS load before the read (it cannot tell the read from the
+// stages those loads fill), which serialises the ring; the ring's own waits and barriers
+// already order the stage writes before these reads.
+__device__ __forceinline__ uint32_t lds_byte_addr(const bf16_t* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const bf16_t*)p;
+}
+template <int W, int NF>
+__device__ __forceinline__ void tr_frags(const bf16_t* st, const int (&base)[NF], int ks,
+                                         bf16x8 (&out)[NF]) {
+  static_assert(NF == 1 || NF == 2 || NF == 4, "1, 2 or 4 operand blocks");
+  constexpr int O0 = 0, O1 = 4 * W * 2;       // byte offsets of the two 4-row reads
+  const int kofs = ks * 16 * W;
+  v4s r[2 * NF];
+  uint32_t ad[NF];
+#pragma unroll
+  for (int f = 0; f < NF; ++f) ad[f] = lds_byte_addr(st + base[f] + kofs);
+  if constexpr (NF == 1) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %2 offset:%3\n\t"
+        "ds_read_b64_tr_b16 %1, %2 offset:%4\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1])
+        : "v"(ad[0]), "i"(O0), "i"(O1));
+  } else if constexpr (NF == 2) {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %4 offset:%6\n\t"
+        "ds_read_b64_tr_b16 %1, %4 offset:%7\n\t"
+        "ds_read_b64_tr_b16 %2, %5 offset:%6\n\t"
+        "ds_read_b64_tr_b16 %3, %5 offset:%7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+        : "v"(ad[0]), "v"(ad[1]), "i"(O0), "i"(O1));
+  } else {
+    asm volatile(
+        "ds_read_b64_tr_b16 %0, %8 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %1, %8 offset:%13\n\t"
+        "ds_read_b64_tr_b16 %2, %9 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %3, %9 offset:%13\n\t"
+        "ds_read_b64_tr_b16 %4, %10 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %5, %10 offset:%13\n\t"
+        "ds_read_b64_tr_b16 %6, %11 offset:%12\n\t"
+        "ds_read_b64_tr_b16 %7, %11 offset:%13\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3]), "=&v"(r[4]), "=&v"(r[5]), "=&v"(r[6]),
+          "=&v"(r[7])
+        : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3]), "i"(O0), "i"(O1));
+  }
+#pragma unroll
+  for (int f = 0; f < NF; ++f)
+    out[f] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(r[2 * f], r[2 * f + 1], 0, 1, 2,
+                                                                3, 4, 5, 6, 7));
+}
+
 // This lane's element offset, in a transposed [k][W] stage, of the first of the 4 rows it
 // points at for the operand block whose first column is mb (sub-step 0, first read):
 // lane i of each 16-lane group points at row 8*(group/2) + i/4, column mb + 16*(group%2) + 4*(i%4).
@@ -328,16 +384,16 @@ __global__ __launch_bounds__(WM * WN * 64) void bwd_gemm_kernel(BwdArgs a) {
     constexpr int NF = decltype(nf_tag)::value;
     auto compute = [&](const bf16_t* Ast, const bf16_t* Bst) {
       if constexpr (NF == 0) return;
-      __builtin_amdgcn_iglp_opt(1);
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         bf16x8 af[FM], bfv[FN];
+        if constexpr (ATR) {
+          tr_frags<BM, FM>(Ast, abase, ks, af);
+        } else {
 #pragma unroll
-        for (int i = 0; i < NF; ++i)
-          af[i] = ATR ? tr_frag<BM>(Ast, abase[i], ks)
-                      : *(const bf16x8*)&Ast[aoffs[ks] + i * WM * 32 * BK];
-#pragma unroll
-        for (int j = 0; j < FN; ++j) bfv[j] = tr_frag<BN>(Bst, bbase[j], ks);
+          for (int i = 0; i < NF; ++i) af[i] = *(const bf16x8*)&Ast[aoffs[ks] + i * WM * 32 * BK];
+        }
+        tr_frags<BN, FN>(Bst, bbase, ks, bfv);
 #pragma unroll
         for (int i = 0; i < NF; ++i)
 #pragma unroll
@@ -625,14 +681,11 @@ __global__ __launch_bounds__(512) void bwd_wgrad_kernel(BwdArgs a) {
     issue_next((step + WG_SLOTS - 1) % WG_SLOTS);
     const bf16_t* As = smem + (step % WG_SLOTS) * SLOT;
     const bf16_t* Bs = As + ASZ;
-    __builtin_amdgcn_iglp_opt(1);
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
       bf16x8 af[FM], bfv[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) af[i] = tr_frag<BM>(As, abase[i], ks);
-#pragma unroll
-      for (int j = 0; j < FN; ++j) bfv[j] = tr_frag<BN>(Bs, bbase[j], ks);
+      tr_frags<BM, FM>(As, abase, ks, af);
+      tr_frags<BN, FN>(Bs, bbase, ks, bfv);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll

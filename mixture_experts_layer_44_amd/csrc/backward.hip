@@ -50,8 +50,6 @@ namespace moe {
 namespace {
 
 typedef short v4s __attribute__((ext_vector_type(4)));
-typedef short v8s __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) v4s* lds_v4s_ptr;
 
 constexpr int BBM = 128;   // rows of a weight-gradient m-tile (rows of the weight matrix)
 // The router's weight gradient (K = T) runs as a launched 128 x 128 tile with a 2-stage ring
@@ -110,24 +108,15 @@ __device__ __forceinline__ int tr_off(int row, int col) {
   return row * W + ((((col >> 3) ^ ((row & 3) << 2))) << 3) + (col & 7);
 }
 
-// One 8 x bf16 MFMA operand from a transposed [k][W] stage: rows (ks*16 + 8*(lane/32)) .. +7,
-// column mb + lane%32. `base` is this lane's precomputed offset for block mb (see below).
-template <int W>
-__device__ __forceinline__ bf16x8 tr_frag(const bf16_t* st, int base, int ks) {
-  auto p0 = (lds_v4s_ptr)(__attribute__((address_space(3))) char*)(st + base + ks * 16 * W);
-  auto p1 = (lds_v4s_ptr)(__attribute__((address_space(3))) char*)(st + base + ks * 16 * W + 4 * W);
-  const v4s lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p0);
-  const v4s hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(p1);
-  const v8s c = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-  return __builtin_bit_cast(bf16x8, c);
-}
-
-// The same reads for NF operand blocks at once, written as one asm block that ends with its own
-// lgkmcnt wait (so its outputs are complete when it ends). The outputs are early-clobber: a read
-// may return while a later read of the block has not yet taken its address. The builtin above makes the compiler
-// drain every in-flight global->LDS load before the read (it cannot tell the read from the
-// stages those loads fill), which serialises the ring; the ring's own waits and barriers
-// already order the stage writes before these reads.
+// MFMA operands from a transposed [k][W] stage: for each of NF operand blocks (first column
+// base-derived, see tr_base), lane l gets rows ks*16 + 8*(l/32) .. +7 of column mb + l%32, as
+// two 4-row ds_read_b64_tr_b16 reads. All of a sub-step's reads are one asm block that ends with
+// its own lgkmcnt wait, so its outputs are complete when it ends; they are early-clobber, since
+// a read may return while a later read of the block has not yet taken its address.
+// (With the compiler's ds_read_tr16_b64 builtin, the compiler put a full vmcnt(0) wait before
+// the first read of every K step: it cannot tell the read from the stages that the in-flight
+// global->LDS loads fill, so every step drained the ring. The ring's own waits and barriers
+// already order the stage writes before these reads.)
 __device__ __forceinline__ uint32_t lds_byte_addr(const bf16_t* p) {
   return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const bf16_t*)p;
 }

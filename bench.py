@@ -8,7 +8,9 @@ SwiGLU -> grouped down GEMM -> combine) over one batch of synthetic input
 already resident in HBM. W untimed warm-up steps, then exactly K steps
 between two device synchronisations. A second pass of K steps records HIP
 events on the launch stream between the stages, for the per-stage times and
-the dominant kernel's average launch duration (its roofline). Prints ONE
+the dominant kernel's average launch duration (its roofline). A third, cold
+pass writes a 1 GiB buffer before each step, outside its events, so no step
+finds the last one's data in L2 or the Infinity Cache ("cold": medians). Prints ONE
 JSON line on stdout: tokens/s of the whole job, that roofline, and the fp64
 CPU oracle timed on a bounded sample of the same workload (1 core).
 
@@ -24,6 +26,7 @@ import hashlib
 import json
 import os
 import re
+import statistics
 import sys
 import time
 
@@ -417,6 +420,8 @@ def main(argv=None):
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="post-process two rocprofv3 --pmc counter CSVs into "
                          "profiles/traffic_<stage>_<workload>.json and exit (no GPU)")
+    ap.add_argument("--scrub", choices=("read", "write"), default="read",
+                    help="how the cold pass evicts the caches before each step")
     ap.add_argument("--traffic-command", default="", help="command recorded with --write-traffic")
     args = ap.parse_args(argv)
 
@@ -518,6 +523,27 @@ def main(argv=None):
     log(f"[bench] {ms_per_step:.4f} ms/step, {tokens_per_s:,.0f} tokens/s "
         f"(stage-event pass: {sum(stage_ms.values()):.4f} ms/step)")
 
+    # cold pass: before each step, outside its events, write a 1 GiB buffer (more than the 256 MB
+    # Infinity Cache plus the 8 x 4 MB of L2), so no step finds the previous step's weights or
+    # rows in a cache. Per-step and per-stage medians (the events add a few microseconds each).
+    scrub = torch.ones(1 << 28, dtype=torch.int32, device=dev)
+    torch.cuda.synchronize()
+    for s_ in range(args.steps):
+        if args.scrub == "write":
+            scrub.fill_(s_)
+        else:
+            scrub.max()
+        moe.forward_staged(p, g["x"], g["w_gate"], g["w1"], g["w3"], g["w2"], handles[s_], y=y, **kw)
+    torch.cuda.synchronize()
+    del scrub
+    cold_stage = {name: statistics.median(events[s][i].elapsed_time(events[s][i + 1])
+                                          for s in range(args.steps))
+                  for i, name in enumerate(moe.STAGES)}
+    cold_steps = [events[s][0].elapsed_time(events[s][len(moe.STAGES)]) for s in range(args.steps)]
+    log("[bench] cold stage ms (median): " + ", ".join(f"{k}={v:.4f}" for k, v in cold_stage.items()))
+    log(f"[bench] cold step (caches scrubbed): median {statistics.median(cold_steps):.4f} ms, "
+        f"min {min(cold_steps):.4f} ms")
+
     # dominant kernel roofline
     dom = max(("gate_up", "down"), key=lambda s: stage_ms[s])
     kwk = kernel_work(w, counts, dom)
@@ -540,6 +566,15 @@ def main(argv=None):
     roof["avg_launch_ms"] = stage_ms[dom]
     roof["algorithmic_per_launch"] = {"flops": kwk["flops"], "bytes": kwk["bytes"]}
 
+    cold_dom_s = cold_stage[dom] * 1e-3
+    cold = {"scrub_bytes": 1 << 30, "ms_per_step_median": statistics.median(cold_steps),
+            "ms_per_step_min": min(cold_steps),
+            "stage_ms_median": {k: round(v, 5) for k, v in cold_stage.items()},
+            "dominant_achieved": (kwk["flops"] / cold_dom_s / 1e12 if roof["unit"] == "TFLOP/s"
+                                  else kwk["bytes"] / cold_dom_s / 1e9),
+            "dominant_unit": roof["unit"]}
+    cold["dominant_frac"] = cold["dominant_achieved"] / roof["peak"]
+
     lw = algorithmic_work(w, counts)
     t_layer = ms_per_step * 1e-3
     layer = {"flops": lw["flops"], "bytes": lw["bytes"], "kept_rows": lw["kept"],
@@ -561,7 +596,7 @@ def main(argv=None):
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
             "dtype": "bf16" if bf16 else "f32", "data": "synthetic", "config": cfg,
-            "roofline": roof, "cpu_baseline": cpu, "layer": layer,
+            "roofline": roof, "cpu_baseline": cpu, "layer": layer, "cold": cold,
             "launch": "hip_graph" if args.graph else "eager"}
     print(json.dumps(line), flush=True)
     return 0

@@ -82,6 +82,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs args) 
   constexpr int STAGE = ROWS * BK;                 // bf16 elements per stage
   constexpr int DMA_WAVE = ROWS * CHUNKS / 64 / NW; // 1 KB loads per wave per stage
   static_assert(DMA_WAVE * 64 * NW == ROWS * CHUNKS, "loads split evenly over the waves");
+  static_assert((STAGES - 1) * DMA_WAVE <= 63, "the loads in flight fit the vmcnt counter");
   constexpr int FEAT = GATEUP ? BNB / 2 : BNB;     // output features per n-tile
   static_assert(!GATEUP || FN % 2 == 0, "u and v fragments pair up");
   static_assert(BM % RPI == 0 && (BNB / 2) % RPI == 0, "a 1 KB load covers rows of one matrix");
@@ -488,6 +489,156 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_st_kernel(GemmArgs arg
     }
 }
 
+// ------------------------------------------------------------------ decode class
+// With a few rows per expert the layer streams each touched expert's weights once, and its
+// pace is set by HBM latency times the bytes in flight, not by MFMA work. A workgroup takes
+// one m-tile of up to 32 rows (a second 16-row fragment only when it holds rows) and 32
+// (gate-up) or 64 (down) output features. Its four waves split K in four: each wave streams
+// its quarter of the tile's weight rows (and the A rows) straight into registers, several
+// steps of 64 ahead, with no LDS ring and no barrier, and accumulates its own partial sums
+// with v_mfma_f32_16x16x32_bf16. The four partials are added through LDS in wave order
+// (deterministic), then the SwiGLU (gate-up) or the fp32 store (down) follows.
+// MFMA 16x16x32 operands: lane l holds row (A) or column (B) l%16 and k = 8*(l/16) .. +7 of
+// the 32-wide block, so one 16-byte load per lane reads 16 rows x 64 contiguous bytes. The
+// result: lane l holds column l%16, rows 4*(l/16) .. +3.
+// KTW, the steps per wave (K / 256), is a template argument: the K loop is unrolled whole, so
+// the ring slots and the last loads are fixed at compile time and the compiler's vmcnt waits
+// are exact (with a rolled loop it drained every load at the loop head).
+constexpr int kDecBM = 32, kDecMaxSteps = 8;
+// output features per workgroup: gate-up 32 (16-row blocks W1, W1, W3, W3), down 64
+constexpr int dec_feat(bool gateup) { return gateup ? 32 : 64; }
+// steps in flight: as many as about 200 VGPRs of operands hold (40 per step with one A
+// fragment, 48 with two)
+constexpr int dec_depth(int nf, int steps) {
+  const int d = nf == 1 ? 5 : 4;
+  return d < steps ? d : steps;
+}
+
+template <bool GATEUP, int KTW>
+__global__ __launch_bounds__(256) void gemm_bf16_dec_kernel(GemmArgs args) {
+  constexpr int NBLK = 4;                    // 16-row B blocks: gate-up W1, W1, W3, W3; down W2
+  constexpr int FEAT = dec_feat(GATEUP);
+  constexpr int RS = NBLK * 16 + 4;          // padded fp32 row of a wave's partial sums in LDS
+  __shared__ float red[4][kDecBM * RS];
+
+  TileCoord tc;
+  if (!tile_coord(args.sc, args.N / FEAT, FEAT, tc)) return;
+  const bool shared_grp = tc.g >= args.E;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int K = args.K, N = args.N;          // K == KTW * 256 (checked by the launcher)
+  const int rows_here = __builtin_amdgcn_readfirstlane(min(kDecBM, tc.rows - tc.m_local * kDecBM));
+  const int r16 = lane & 15, kq = lane >> 4;
+  const int kbase = wave * (KTW * 64) + kq * 8;   // this wave's K range starts at wave*K/4
+
+  const bf16_t* bp[NBLK];
+#pragma unroll
+  for (int b = 0; b < NBLK; ++b) {
+    const bool second = GATEUP && b >= 2;
+    const bf16_t* mat;
+    if (GATEUP)
+      mat = shared_grp ? (second ? args.S1 : args.S0)
+                       : (second ? args.B1 : args.B0) + (size_t)tc.g * N * K;
+    else
+      mat = shared_grp ? args.S0 : args.B0 + (size_t)tc.g * N * K;
+    const int row = tc.n0 + (GATEUP ? (b & 1) : b) * 16 + r16;
+    bp[b] = mat + (size_t)row * K + kbase;
+  }
+  const bf16_t* ap[kDecBM / 16];
+#pragma unroll
+  for (int f = 0; f < kDecBM / 16; ++f) {
+    int srow;
+    if (GATEUP) {
+      const int r = tc.m_local * kDecBM + f * 16 + r16;
+      const int rr = r < tc.rows ? r : 0;             // padding rows repeat the first row
+      const int tok = shared_grp ? rr : args.sorted_assign[tc.off + rr] / args.k;
+      srow = (unsigned)tok < (unsigned)args.T ? tok : 0;
+    } else {
+      srow = tc.mt_global * kDecBM + f * 16 + r16;     // padding rows: results not stored
+    }
+    ap[f] = args.A + (size_t)srow * K + kbase;
+  }
+
+  auto run = [&](auto nf_tag) {
+    constexpr int NF = decltype(nf_tag)::value;
+    constexpr int D = dec_depth(NF, KTW);
+    f32x4 acc[NF][NBLK];
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+      for (int b = 0; b < NBLK; ++b) acc[f][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // A and B of a step are issued together, D steps ahead: vector-memory loads retire in
+    // order, so an A load issued after a later step's B loads would make its wait cover them.
+    bf16x8 bq[D][NBLK][2], aq[D][NF][2];
+    auto load = [&](int d, int kt) {
+#pragma unroll
+      for (int b = 0; b < NBLK; ++b)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) bq[d][b][s] = *(const bf16x8*)(bp[b] + kt * 64 + s * 32);
+#pragma unroll
+      for (int f = 0; f < NF; ++f)
+#pragma unroll
+        for (int s = 0; s < 2; ++s) aq[d][f][s] = *(const bf16x8*)(ap[f] + kt * 64 + s * 32);
+    };
+#pragma unroll
+    for (int d = 0; d < D; ++d) load(d, d);
+#pragma unroll
+    for (int kt = 0; kt < KTW; ++kt) {
+      const int d = kt % D;
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+#pragma unroll
+        for (int f = 0; f < NF; ++f)
+#pragma unroll
+          for (int b = 0; b < NBLK; ++b)
+            acc[f][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aq[d][f][s], bq[d][b][s], acc[f][b],
+                                                                0, 0, 0);
+      if (kt + D < KTW) load(d, kt + D);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    float* my = red[wave];
+#pragma unroll
+    for (int f = 0; f < NF; ++f)
+#pragma unroll
+      for (int b = 0; b < NBLK; ++b)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) my[(f * 16 + 4 * kq + i) * RS + b * 16 + r16] = acc[f][b][i];
+  };
+  static_assert(kDecBM == 32, "one or two 16-row fragments");
+  if (rows_here > 16) run(std::integral_constant<int, 2>{});
+  else run(std::integral_constant<int, 1>{});
+  __syncthreads();
+
+  // the four partials, added in wave order; thread t takes output feature t%FEAT of rows
+  // t/FEAT + (256/FEAT)*i
+  const int col = tid % FEAT;
+  for (int row = tid / FEAT; row < rows_here; row += 256 / FEAT) {
+    const float* r0 = &red[0][row * RS];
+    if (GATEUP) {
+      float u = r0[col], v = r0[32 + col];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) {
+        u += red[w][row * RS + col];
+        v += red[w][row * RS + 32 + col];
+      }
+      const size_t o = (size_t)(tc.mt_global * kDecBM + row) * N + tc.n0 + col;
+      args.H[o] = f32_to_bf16(silu_f(u) * v);
+      if (args.U) {
+        args.U[o] = u;
+        args.V[o] = v;
+      }
+    } else {
+      float y = r0[col];
+#pragma unroll
+      for (int w = 1; w < 4; ++w) y += red[w][row * RS + col];
+      const int rg = tc.m_local * kDecBM + row;
+      float* dst = shared_grp ? args.shared_out + (size_t)rg * N
+                              : args.out_rows + (size_t)(tc.off + rg) * N;
+      dst[tc.n0 + col] = y;
+    }
+  }
+}
+
 // ------------------------------------------------------------------ fp32 path (VALU)
 constexpr int BM32 = kGemmBM32, BN32 = 64, BK32 = 16;
 
@@ -601,7 +752,7 @@ static double expected_rows(const moe_problem& p) {
 int gemm_bm(const moe_problem& p) {
   if (p.dtype != MOE_BF16) return kGemmBM32;
   if (gemm_wide(p)) return 256;
-  if (gemm_small(p)) return 32;
+  if (gemm_small(p)) return gemm_dec(p) ? kDecBM : 32;
   if (p.d % 256 || p.capacity_factor > 0) return 128;
   const double r = expected_rows(p);
   if (r <= 100.0) return 128;
@@ -614,7 +765,7 @@ int gemm_bm(const moe_problem& p) {
 int gemm_bm_exact(const moe_problem& p, int C) {
   if (p.dtype != MOE_BF16) return kGemmBM32;
   if (gemm_wide(p)) return 256;
-  if (gemm_small(p)) return 32;
+  if (gemm_small(p)) return gemm_dec(p) ? kDecBM : 32;
   if (p.d % 256) return 128;
   int best = 128, tiles = ceil_div(C, 128);
   for (int bm : {192, 256})
@@ -642,6 +793,35 @@ int down_ksplit(const moe_problem& p) {
 }
 
 bool gemm_small(const moe_problem& p) { return p.dtype == MOE_BF16 && expected_rows(p) <= 48.0; }
+
+// the small class takes the decode kernel when both K ranges split into four whole 64-steps,
+// at most kDecMaxSteps each
+bool gemm_dec(const moe_problem& p) {
+  return gemm_small(p) && p.d % 256 == 0 && p.d_ff % 256 == 0 && p.d <= 256 * kDecMaxSteps &&
+         p.d_ff <= 256 * kDecMaxSteps;
+}
+
+// the decode kernel for K = steps * 256, steps in 1 .. kDecMaxSteps
+template <bool GATEUP, int STEPS = 1>
+void launch_dec_k(int steps, dim3 grid, hipStream_t s, const GemmArgs& a) {
+  if constexpr (STEPS <= kDecMaxSteps) {
+    if (steps == STEPS)
+      hipLaunchKernelGGL((gemm_bf16_dec_kernel<GATEUP, STEPS>), grid, dim3(256), 0, s, a);
+    else
+      launch_dec_k<GATEUP, STEPS + 1>(steps, grid, s, a);
+  }
+}
+
+hipError_t launch_dec(const moe_problem& p, const GemmArgs& a, const GemmArgs& b, hipStream_t s,
+                      hipEvent_t between, bool up_only) {
+  if (!gemm_dec(p) || a.sc.BM != kDecBM) return hipErrorInvalidValue;
+  launch_dec_k<true>(p.d / 256, dim3(grid_for(a.sc.max_mtiles, p.d_ff / dec_feat(true))), s, a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || up_only) return err;
+  if (between && (err = hipEventRecord(between, s)) != hipSuccess) return err;
+  launch_dec_k<false>(p.d_ff / 256, dim3(grid_for(b.sc.max_mtiles, p.d / dec_feat(false))), s, b);
+  return hipGetLastError();
+}
 
 template <int BM, int BNB_UP, int WM_UP, int WN_UP, int BNB_DN, int WM_DN, int WN_DN, int BK, int ST>
 hipError_t launch_bf16(const moe_problem& p, const GemmArgs& a, const GemmArgs& b, hipStream_t s,
@@ -720,6 +900,7 @@ hipError_t launch_expert_ffn(const moe_problem& p, const void* x, const void* w1
       return launch_bf16_st<256, 256, 4, 2, 256, 4, 2, false>(p, a, b, s, between, up_only);
     if (sc.BM == 256) return launch_bf16_st<256, 256, 4, 2, 256, 4, 2, true>(p, a, b, s, between, up_only);
     if (sc.BM == 192) return launch_bf16_st<192, 256, 2, 4, 256, 2, 4, true>(p, a, b, s, between, up_only);
+    if (sc.BM == kDecBM && gemm_dec(p)) return launch_dec(p, a, b, s, between, up_only);
     if (sc.BM == 32) return launch_bf16<32, 256, 1, 4, 128, 1, 4, 64, 4>(p, a, b, s, between, up_only);
     // down tiles of 256 output features need d % 256 == 0 (the entry points accept d % 128)
     if (p.d % 256 == 0) return launch_bf16_st<128, 256, 2, 4, 256, 2, 4, true>(p, a, b, s, between, up_only);

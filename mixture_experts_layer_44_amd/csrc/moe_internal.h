@@ -55,6 +55,7 @@ int max_mtiles(long long n_rows, int T, int E, int n_shared, int BM);
 // narrow (128) or small (32)
 bool gemm_wide(const moe_problem& p);
 bool gemm_small(const moe_problem& p);
+bool gemm_dec(const moe_problem& p);     // small class on the decode kernel (32-row m-tiles)
 int gemm_bm(const moe_problem& p);
 int gemm_bm_exact(const moe_problem& p, int C);   // all segments of exactly C rows
 int grid_for(int mtiles, int nt);

@@ -56,6 +56,13 @@ SMALL = [
     W("bf16_mid192_two", T=1400, d=256, E=8, k=2, d_ff=256, seed=116),
     # ragged 256-row tiles (~230 rows per expert) with a selection bias
     W("bf16_mid256", T=920, d=256, E=8, k=2, d_ff=256, seed=117, sel_bias=True),
+    # decode class (<= 48 rows per expert, d and d_ff multiples of 256): K split over the four
+    # waves; segments of 1..32 rows and longer ones (several 32-row m-tiles) under Zipf routing,
+    # one or two 16-row fragments, a shared expert of T rows, and K of 1, 3 and 8 wave steps
+    W("bf16_dec_zipf", T=200, d=512, E=32, k=4, d_ff=768, seed=118, zipf_s=1.1),
+    W("bf16_dec_shared", T=70, d=2048, E=64, k=2, d_ff=256, seed=119, n_shared=1, d_ff_shared=256,
+      sel_bias=True),
+    W("bf16_dec_cap", T=96, d=256, E=16, k=4, d_ff=512, seed=120, capacity_factor=1.0, zipf_s=1.1),
 ]
 
 

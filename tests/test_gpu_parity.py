@@ -63,6 +63,12 @@ SMALL = [
     W("bf16_dec_shared", T=70, d=2048, E=64, k=2, d_ff=256, seed=119, n_shared=1, d_ff_shared=256,
       sel_bias=True),
     W("bf16_dec_cap", T=96, d=256, E=16, k=4, d_ff=512, seed=120, capacity_factor=1.0, zipf_s=1.1),
+    # the remaining per-wave step counts of the decode kernel: 4, 5, 6 and 7 (gate-up K = d)
+    # with 6, 4, 7 and 5 (down K = d_ff)
+    W("bf16_dec_k4", T=24, d=1024, E=16, k=2, d_ff=1536, seed=121),
+    W("bf16_dec_k5", T=24, d=1280, E=16, k=2, d_ff=1024, seed=122, n_shared=1, d_ff_shared=1024),
+    W("bf16_dec_k6", T=40, d=1536, E=16, k=4, d_ff=1792, seed=123),
+    W("bf16_dec_k7", T=40, d=1792, E=16, k=4, d_ff=1280, seed=124, capacity_factor=1.0),
 ]
 
 

@@ -7,117 +7,138 @@
 // handbook, "Load balancing" (the balancing bias only chooses experts).
 //
 // Two launches:
-//  logits: grid (token tiles of 32) x (expert groups of 64) x (KS slices of d). A workgroup
-//          of 4 waves computes a 32 x 64 block of partial logits over its d slice with
-//          v_mfma_f32_16x16x32_bf16 (fp32 accumulate); waves take 16-expert tiles and, when
-//          the group has fewer than 4 tiles, split the slice further, their partials summed
-//          in a fixed order through LDS. Loads are issued four k-steps ahead of the MFMAs.
-//          KS is chosen on the host so that the grid has >= ~512 workgroups; the fp32
+//  logits: grid (token tiles of 64) x (expert groups of 64) x (KS slices of d). A workgroup
+//          of 4 waves computes a 64 x 64 block of partial logits over its d slice with
+//          v_mfma_f32_16x16x32_bf16 (fp32 accumulate): each wave takes the whole block over a
+//          quarter of the slice (4 token rows and up to 4 expert rows loaded per 16 MFMAs, so
+//          every x and W_gate byte a workgroup needs is loaded once), and the four partials
+//          are added in wave order through LDS. Loads are issued four k-steps ahead of the
+//          MFMAs. KS is chosen on the host so that the grid has >= ~512 workgroups; the fp32
 //          partials [KS][T][E_pad] never round to bf16.
 //  topk:   one wave per token. Sums the KS partials in slice order (run-to-run identical),
 //          adds logit_bias, softmax, keys = logits (+ sel_bias), k rounds of a 64-lane
 //          arg-max (larger key first, lower expert index on equal keys), gates = kept p /
 //          their sum; per-workgroup sums of p for prob_sum.
+#include <type_traits>
+
 #include "topk.h"
 
 namespace moe {
 
 namespace {
 
-constexpr int TM = 32;        // tokens per logits workgroup
+constexpr int TM = 64;        // tokens per logits workgroup
 constexpr int EN = 64;        // experts per logits workgroup
 constexpr int UNROLL = 4;     // k-steps of loads in flight per wave
 constexpr int TOPK_TOK = 16;  // tokens per top-k workgroup (4 waves x 4)
 
-// partial logits of a 32-token x 64-expert block over the d slice blockIdx.z
+// partial logits of a 64-token x 64-expert block over the d slice blockIdx.z
 template <bool BF16>
 __global__ __launch_bounds__(256) void route_logits_kernel(const void* __restrict__ xv,
                                                            const void* __restrict__ wv, int T,
                                                            int d, int E, int E_pad, int KS,
                                                            float* __restrict__ part) {
-  __shared__ float red[4][TM][16];   // per-wave partials when waves split the slice
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int tok0 = blockIdx.x * TM;
   const int e0 = blockIdx.y * EN;
   const int ntiles = min(EN, E_pad - e0) / 16;      // 1..4 expert tiles in this group
-  const int wsplit = 4 / ntiles >= 4 ? 4 : (4 / ntiles >= 2 ? 2 : 1);   // waves per tile
   const int slice = d / KS, k_begin = blockIdx.z * slice;
   float* out = part + (size_t)blockIdx.z * T * E_pad;
 
   if constexpr (BF16) {
+    constexpr int RS = EN + 4;                        // padded row of a wave's partials
+    __shared__ float red[4][TM * RS];
     const bf16_t* x = (const bf16_t*)xv;
     const bf16_t* w = (const bf16_t*)wv;
-    const int tile = wave / wsplit, sub = wave % wsplit;   // this wave's expert tile, sub-slice
-    const bool active = tile < ntiles;
-    const int sub_len = slice / wsplit;
-    const int kb0 = k_begin + sub * sub_len;
+    const int sub_len = slice / 4;                    // this wave's quarter of the slice
+    const int kb0 = k_begin + wave * sub_len;
     const int r = lane & 15, kq = (lane >> 4) * 8;
-    const int e = e0 + tile * 16 + r;
-    const bool b_ok = active && e < E;
-    const bf16_t* bp = w + (size_t)(b_ok ? e : 0) * d + kq;
-    const bool a0_ok = tok0 + r < T, a1_ok = tok0 + 16 + r < T;
-    const bf16_t* ap0 = x + (size_t)(a0_ok ? tok0 + r : 0) * d + kq;
-    const bf16_t* ap1 = x + (size_t)(a1_ok ? tok0 + 16 + r : 0) * d + kq;
-    f32x4 acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
     const bf16x8 z8 = {};
-    if (active) {
-      // walk the slice starting at a per-workgroup offset (wrapping): rows are d*2 bytes
+    // The block for NT expert tiles. Operand rows past T or E read row 0 and are zeroed.
+    auto run = [&](auto nt_tag) {
+      constexpr int NT = decltype(nt_tag)::value;
+      const bf16_t* ap[4];
+      bool a_ok[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int t = tok0 + 16 * i + r;
+        a_ok[i] = t < T;
+        ap[i] = x + (size_t)(a_ok[i] ? t : 0) * d + kq;
+      }
+      const bf16_t* bp[NT];
+      bool b_ok[NT];
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const int e = e0 + 16 * j + r;
+        b_ok[j] = e < E;
+        bp[j] = w + (size_t)(b_ok[j] ? e : 0) * d + kq;
+      }
+      f32x4 acc[4][NT];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < NT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      // walk the sub-slice starting at a per-workgroup offset (wrapping): rows are d*2 bytes
       // apart, and workgroups reading the same k offset at once collide on memory channels
       const int nsteps = sub_len / 32;
       const int rot = (blockIdx.x + blockIdx.y * 7) % nsteps;
       auto kpos = [&](int step) { return kb0 + ((step + rot) % nsteps) * 32; };
+      auto mma = [&](const bf16x8 (&a)[4], const bf16x8 (&b)[NT]) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bf16x8 av = a_ok[i] ? a[i] : z8;
+#pragma unroll
+          for (int j = 0; j < NT; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, b_ok[j] ? b[j] : z8, acc[i][j],
+                                                                0, 0, 0);
+        }
+      };
       int st = 0;
       for (; st + UNROLL <= nsteps; st += UNROLL) {
-        bf16x8 a0[UNROLL], a1[UNROLL], b[UNROLL];
+        bf16x8 a[UNROLL][4], b[UNROLL][NT];
 #pragma unroll
         for (int u = 0; u < UNROLL; ++u) {
           const int kb = kpos(st + u);
-          a0[u] = *(const bf16x8*)(ap0 + kb);
-          a1[u] = *(const bf16x8*)(ap1 + kb);
-          b[u] = *(const bf16x8*)(bp + kb);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) a[u][i] = *(const bf16x8*)(ap[i] + kb);
+#pragma unroll
+          for (int j = 0; j < NT; ++j) b[u][j] = *(const bf16x8*)(bp[j] + kb);
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int u = 0; u < UNROLL; ++u) {
-          const bf16x8 bb = b_ok ? b[u] : z8;
-          acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a0_ok ? a0[u] : z8, bb, acc0, 0, 0, 0);
-          acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a1_ok ? a1[u] : z8, bb, acc1, 0, 0, 0);
-        }
+        for (int u = 0; u < UNROLL; ++u) mma(a[u], b[u]);
       }
       for (; st < nsteps; ++st) {
         const int kb = kpos(st);
-        const bf16x8 bb = b_ok ? *(const bf16x8*)(bp + kb) : z8;
-        const bf16x8 x0 = a0_ok ? *(const bf16x8*)(ap0 + kb) : z8;
-        const bf16x8 x1 = a1_ok ? *(const bf16x8*)(ap1 + kb) : z8;
-        acc0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x0, bb, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(x1, bb, acc1, 0, 0, 0);
-      }
-    }
-    // C layout (16x16): lane holds column (expert) lane%16, rows (tokens) 4*(lane/16)+j
-    if (wsplit > 1) {
-      if (active) {
+        bf16x8 a[4], b[NT];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          red[wave][(lane >> 4) * 4 + j][lane & 15] = acc0[j];
-          red[wave][16 + (lane >> 4) * 4 + j][lane & 15] = acc1[j];
-        }
-      }
-      __syncthreads();
-      // thread -> (token, expert) of this group; sum the sub-slices of its tile in order
-      for (int idx = tid; idx < TM * ntiles * 16; idx += 256) {
-        const int tr = idx / (ntiles * 16), ec = idx % (ntiles * 16);
-        const int t_ = ec / 16, c = ec % 16;
-        float s = 0.f;
-        for (int q = 0; q < wsplit; ++q) s += red[t_ * wsplit + q][tr][c];
-        if (tok0 + tr < T) out[(size_t)(tok0 + tr) * E_pad + e0 + ec] = s;
-      }
-    } else if (active) {
+        for (int i = 0; i < 4; ++i) a[i] = *(const bf16x8*)(ap[i] + kb);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int t0 = tok0 + (lane >> 4) * 4 + j, t1 = t0 + 16;
-        if (t0 < T) out[(size_t)t0 * E_pad + e0 + tile * 16 + (lane & 15)] = acc0[j];
-        if (t1 < T) out[(size_t)t1 * E_pad + e0 + tile * 16 + (lane & 15)] = acc1[j];
+        for (int j = 0; j < NT; ++j) b[j] = *(const bf16x8*)(bp[j] + kb);
+        mma(a, b);
       }
+      // C layout (16x16): lane holds column (expert) lane%16, rows (tokens) 4*(lane/16)+q
+      float* my = red[wave];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < NT; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            my[(16 * i + 4 * (lane >> 4) + q) * RS + 16 * j + (lane & 15)] = acc[i][j][q];
+    };
+    if (ntiles >= 4) run(std::integral_constant<int, 4>{});
+    else if (ntiles == 3) run(std::integral_constant<int, 3>{});
+    else if (ntiles == 2) run(std::integral_constant<int, 2>{});
+    else run(std::integral_constant<int, 1>{});
+    __syncthreads();
+    // thread -> (token, expert) of this block; the four quarters added in wave order
+    const int ecount = ntiles * 16;
+    for (int idx = tid; idx < TM * ecount; idx += 256) {
+      const int tr = idx / ecount, ec = idx % ecount;
+      const float s = ((red[0][tr * RS + ec] + red[1][tr * RS + ec]) + red[2][tr * RS + ec]) +
+                      red[3][tr * RS + ec];
+      if (tok0 + tr < T) out[(size_t)(tok0 + tr) * E_pad + e0 + ec] = s;
     }
   } else {
     const float* x = (const float*)xv;
@@ -200,10 +221,10 @@ int route_ksplit(const moe_problem& p) {
   const int E_pad = ceil_div(p.E, 16) * 16;
   const long long base = (long long)ceil_div(p.T, TM) * ceil_div(E_pad, EN);
   int ks = 1;
-  // split d while the grid is small and each slice keeps >= 256 columns (whole 32-column
-  // k-steps for every wave of a workgroup that also splits its slice 4 ways)
-  while (base * ks < 512 && ks < 16 && p.d % (ks * 2 * 128) == 0 && p.d / (ks * 2) >= 256)
-    ks *= 2;
+  // split d while the grid is small and each slice keeps >= 128 columns (a whole 32-column
+  // k-step for each of the 4 waves that split a workgroup's slice); at most 16 slices, the
+  // most sum_partials adds
+  while (base * ks < 512 && ks < 16 && p.d % (ks * 2 * 128) == 0) ks *= 2;
   return ks;
 }
 

@@ -17,21 +17,25 @@ namespace {
 
 constexpr int NWAVE = 16;
 
-// exclusive scan of v over the first 512 threads (others pass 0); all 1024 threads call it
-__device__ int scan512(int v, int* tmp, int* total) {
-  const int tid = threadIdx.x;
-  if (tid < 512) tmp[tid] = v;
-  __syncthreads();
-  for (int o = 1; o < 512; o <<= 1) {
-    int add = (tid < 512 && tid >= o) ? tmp[tid - o] : 0;
-    __syncthreads();
-    if (tid < 512) tmp[tid] += add;
-    __syncthreads();
+// exclusive scan of v over the first 320 threads (5 waves; the values live in threads < 257,
+// the others pass 0); all 1024 threads call it. Each wave scans its 64 values with shuffles,
+// then adds the totals of the waves before it.
+__device__ int scan320(int v, int* wsum, int* total) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
   }
-  const int incl = tid < 512 ? tmp[tid] : 0;
-  *total = tmp[511];
+  if (lane == 63 && wave < 5) wsum[wave] = x;
   __syncthreads();
-  return incl - v;
+  int base = 0;
+#pragma unroll
+  for (int w = 0; w < 5; ++w) base += w < wave ? wsum[w] : 0;
+  *total = wsum[0] + wsum[1] + wsum[2] + wsum[3] + wsum[4];
+  __syncthreads();   // wsum is reused by the next call
+  return base + x - v;
 }
 
 __global__ __launch_bounds__(1024) void align_small_kernel(
@@ -43,14 +47,22 @@ __global__ __launch_bounds__(1024) void align_small_kernel(
   __shared__ int s_ids[1024];
   __shared__ int wcnt[NWAVE][256];    // assignments of expert e in wave w
   __shared__ int s_off[257];
-  __shared__ int tmp[512];
+  __shared__ int wsum[5];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = T * k;
 
   // probability sums: the top-k workgroups' partials, added in workgroup order
   if (prob_sum && tid < E) {
     float s = 0.f;
-    for (int b = 0; b < nblk; ++b) s += psum_part[(size_t)b * E + tid];
+    int b = 0;
+    for (; b + 8 <= nblk; b += 8) {   // eight loads in flight, added in block order
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = psum_part[(size_t)(b + u) * E + tid];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += v[u];
+    }
+    for (; b < nblk; ++b) s += psum_part[(size_t)b * E + tid];
     prob_sum[tid] = s;
   }
   if (tid < n) s_ids[tid] = ids[tid];
@@ -81,7 +93,7 @@ __global__ __launch_bounds__(1024) void align_small_kernel(
     kept = (cap >= 0 && c > cap) ? cap : c;
   }
   int total;
-  const int off = scan512(tid < E ? kept : 0, tmp, &total);
+  const int off = scan320(tid < E ? kept : 0, wsum, &total);
   if (tid < E) {
     counts_pre[tid] = c;
     counts[tid] = kept;
@@ -113,7 +125,7 @@ __global__ __launch_bounds__(1024) void align_small_kernel(
   else if (tid < G) rows = T;
   const int mts = (rows + sc.BM - 1) / sc.BM;
   int mt_total;
-  const int base = scan512(tid < G ? mts : 0, tmp, &mt_total);
+  const int base = scan320(tid < G ? mts : 0, wsum, &mt_total);
   if (tid < G) {
     const int m0 = min(base, sc.max_mtiles);
     const int m1 = min(base + mts, sc.max_mtiles);

@@ -6,14 +6,16 @@
 // their original positions with their weights); "MoE Architecture" §2 "Load Balancing"
 // (L = alpha * E * sum_i f_i p_i).
 //
-// combine: one workgroup per token row, 16-byte loads/stores along d; slots are added in
-// slot order after the shared row, so y is bit-reproducible from run to run.
+// combine: one workgroup per token row, 16-byte loads/stores along d; the loads of up to 8
+// slots are issued together, and the slots are added in slot order after the shared row, so y
+// is bit-reproducible from run to run.
 #include "moe_internal.h"
 
 namespace moe {
 
 namespace {
 
+template <int NS>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ out_rows,
                                                       const float* __restrict__ out_rows_b,
                                                       const int32_t* __restrict__ assign_pos,
@@ -29,27 +31,60 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     wt[threadIdx.x] = topk_w[(size_t)t * k + threadIdx.x];
   }
   __syncthreads();
+  // the first NS slots of this token in registers (the same in every lane)
+  int r8[NS];
+  float g8[NS];
+#pragma unroll
+  for (int u = 0; u < NS; ++u) {
+    const int r = u < k ? pos[u] : -1;
+    r8[u] = r >= 0 && r < n ? r : -1;
+    g8[u] = u < k ? wt[u] : 0.f;
+  }
   const int d4 = d >> 2;
   for (int c = threadIdx.x; c < d4; c += 256) {
     f32x4 acc = shared_out ? *(const f32x4*)(shared_out + (size_t)t * d + 4 * c)
                            : f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
-      const int r = pos[j];
-      if (r >= 0 && r < n) {
-        f32x4 v = *(const f32x4*)(out_rows + (size_t)r * d + 4 * c);
-        if (out_rows_b) {   // the down GEMM's two K halves
-          const f32x4 vb = *(const f32x4*)(out_rows_b + (size_t)r * d + 4 * c);
-          v[0] += vb[0];
-          v[1] += vb[1];
-          v[2] += vb[2];
-          v[3] += vb[3];
-        }
-        const float g = wt[j];
-        acc[0] = fmaf(g, v[0], acc[0]);
-        acc[1] = fmaf(g, v[1], acc[1]);
-        acc[2] = fmaf(g, v[2], acc[2]);
-        acc[3] = fmaf(g, v[3], acc[3]);
+    // The loads of the kept slots among the first NS are all issued before they are added in
+    // slot order (a dropped slot loads nothing: out_rows may hold only kept rows).
+    f32x4 v[NS], vb[NS];
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      v[u] = vb[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+      if (r8[u] < 0) continue;
+      const size_t o = (size_t)r8[u] * d + 4 * c;
+      v[u] = *(const f32x4*)(out_rows + o);
+      if (out_rows_b) vb[u] = *(const f32x4*)(out_rows_b + o);   // the down GEMM's two K halves
+    }
+#pragma unroll
+    for (int u = 0; u < NS; ++u) {
+      if (r8[u] < 0) continue;
+      if (out_rows_b) {
+        v[u][0] += vb[u][0];
+        v[u][1] += vb[u][1];
+        v[u][2] += vb[u][2];
+        v[u][3] += vb[u][3];
       }
+      acc[0] = fmaf(g8[u], v[u][0], acc[0]);
+      acc[1] = fmaf(g8[u], v[u][1], acc[1]);
+      acc[2] = fmaf(g8[u], v[u][2], acc[2]);
+      acc[3] = fmaf(g8[u], v[u][3], acc[3]);
+    }
+    for (int j = NS; j < k; ++j) {   // slots past the first NS, one at a time
+      const int r = pos[j];
+      if (r < 0 || r >= n) continue;
+      f32x4 w = *(const f32x4*)(out_rows + (size_t)r * d + 4 * c);
+      if (out_rows_b) {
+        const f32x4 vb = *(const f32x4*)(out_rows_b + (size_t)r * d + 4 * c);
+        w[0] += vb[0];
+        w[1] += vb[1];
+        w[2] += vb[2];
+        w[3] += vb[3];
+      }
+      const float g = wt[j];
+      acc[0] = fmaf(g, w[0], acc[0]);
+      acc[1] = fmaf(g, w[1], acc[1]);
+      acc[2] = fmaf(g, w[2], acc[2]);
+      acc[3] = fmaf(g, w[3], acc[3]);
     }
     *(f32x4*)(y + (size_t)t * d + 4 * c) = acc;
   }
@@ -121,8 +156,10 @@ hipError_t launch_combine(const moe_problem& p, const float* out_rows, const flo
                           const int32_t* assign_pos, const float* topk_w, const float* shared_out,
                           float* y, hipStream_t s) {
   if (p.T == 0) return hipSuccess;
-  hipLaunchKernelGGL(combine_kernel, dim3(p.T), dim3(256), 0, s, out_rows, out_rows_b, assign_pos,
-                     topk_w, shared_out, p.d, p.k, y);
+  // slots whose loads are issued together: enough for k up to 8, few registers for small k
+  auto kern = p.k <= 2 ? combine_kernel<2> : (p.k <= 4 ? combine_kernel<4> : combine_kernel<8>);
+  hipLaunchKernelGGL(kern, dim3(p.T), dim3(256), 0, s, out_rows, out_rows_b, assign_pos, topk_w,
+                     shared_out, p.d, p.k, y);
   return hipGetLastError();
 }
 

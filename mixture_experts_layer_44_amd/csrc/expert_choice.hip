@@ -202,21 +202,32 @@ __global__ __launch_bounds__(256) void ec_combine_kernel(const int32_t* __restri
   for (int c = tid; c < d4; c += 256) {
     f32x4 acc = shared_out ? *(const f32x4*)(shared_out + (size_t)t * d + 4 * c)
                            : f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < n; ++j) {
-      const size_t off = (size_t)rows[j] * d + 4 * c;
-      f32x4 v = *(const f32x4*)(out_rows + off);
-      if (out_rows_b) {
-        const f32x4 vb = *(const f32x4*)(out_rows_b + off);
-        v[0] += vb[0];
-        v[1] += vb[1];
-        v[2] += vb[2];
-        v[3] += vb[3];
+    // four rows at a time: their loads are issued together, then they are added in order
+    for (int j0 = 0; j0 < n; j0 += 4) {
+      f32x4 v[4], vb[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        v[u] = vb[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (j0 + u >= n) continue;   // uniform
+        const size_t off = (size_t)rows[j0 + u] * d + 4 * c;
+        v[u] = *(const f32x4*)(out_rows + off);
+        if (out_rows_b) vb[u] = *(const f32x4*)(out_rows_b + off);
       }
-      const float g = wts[j];
-      acc[0] = fmaf(g, v[0], acc[0]);
-      acc[1] = fmaf(g, v[1], acc[1]);
-      acc[2] = fmaf(g, v[2], acc[2]);
-      acc[3] = fmaf(g, v[3], acc[3]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (j0 + u >= n) continue;
+        if (out_rows_b) {
+          v[u][0] += vb[u][0];
+          v[u][1] += vb[u][1];
+          v[u][2] += vb[u][2];
+          v[u][3] += vb[u][3];
+        }
+        const float g = wts[j0 + u];
+        acc[0] = fmaf(g, v[u][0], acc[0]);
+        acc[1] = fmaf(g, v[u][1], acc[1]);
+        acc[2] = fmaf(g, v[u][2], acc[2]);
+        acc[3] = fmaf(g, v[u][3], acc[3]);
+      }
     }
     *(f32x4*)(y + (size_t)t * d + 4 * c) = acc;
   }

@@ -481,7 +481,10 @@ def main(argv=None):
     torch.cuda.synchronize()
     handles = [[e.cuda_event for e in evs] for evs in events]
 
-    fwd = moe.PreparedForward(p, g["x"], g["w_gate"], g["w1"], g["w3"], g["w2"], y=y, **kw)
+    # a workload that asks for the balance statistics gets them in every timed step
+    bal = w.balance_alpha if w.balance_alpha > 0 else None
+    fwd = moe.PreparedForward(p, g["x"], g["w_gate"], g["w1"], g["w3"], g["w2"], y=y,
+                              balance_alpha=bal, **kw)
     step = fwd
     if args.graph:
         fwd()                                         # first call outside the capture
@@ -591,7 +594,8 @@ def main(argv=None):
         cpu.pop("seconds")
 
     cfg = {"workload": w.name, "T": w.T, "d": w.d, "E": w.E, "k": w.k, "d_ff": w.d_ff,
-           "n_shared": w.n_shared, "capacity_factor": w.capacity_factor, "seed": w.seed}
+           "n_shared": w.n_shared, "capacity_factor": w.capacity_factor, "seed": w.seed,
+           "balance_stats": bal is not None}
     line = {"metric": METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1,
             "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
             "higher_is_better": True, "scaling": "weak", "vs_baseline": None,

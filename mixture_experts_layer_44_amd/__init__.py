@@ -460,7 +460,7 @@ class PreparedForward:
     of the layer; this keeps it to one foreign call."""
 
     def __init__(self, p: Problem, x, w_gate, w1, w3, w2, logit_bias=None, sel_bias=None,
-                 ws1=None, ws3=None, ws2=None, ws=None, y=None):
+                 ws1=None, ws3=None, ws2=None, ws=None, y=None, balance_alpha=None):
         dev, dt = x.device, _dt(p)
         _need(x, "x", (p.T, p.d), dt, dev)
         _need(w_gate, "w_gate", (p.E, p.d), dt, dev)
@@ -480,15 +480,35 @@ class PreparedForward:
         ws = _workspace(p, dev, ws)
         self.p, self.y, self.ws, self.dev = p, y, ws, dev
         self._keep = (x, w_gate, w1, w3, w2, logit_bias, sel_bias, ws1, ws3, ws2)
+        # balance_alpha: each call also writes the balance statistics f, P and L (moe_balance on
+        # the call's counts_pre and prob_sum), kept as attributes f, P, L
+        self.balance_alpha = balance_alpha
+        cpre = psum = None
+        if balance_alpha is not None:
+            cpre = torch.empty((p.E,), dtype=torch.int32, device=dev)
+            psum = torch.empty((p.E,), dtype=torch.float32, device=dev)
+            self.f = torch.empty((p.E,), dtype=torch.float32, device=dev)
+            self.P = torch.empty((p.E,), dtype=torch.float32, device=dev)
+            self.L = torch.empty((1,), dtype=torch.float32, device=dev)
+            self._bal_args = (ctypes.byref(p), _ptr(cpre), _ptr(psum), ctypes.c_float(balance_alpha),
+                              _ptr(self.f), _ptr(self.P), _ptr(self.L))
+        self.counts_pre, self.prob_sum = cpre, psum
         self._args = (ctypes.byref(p), _ptr(x), _ptr(w_gate), _ptr(logit_bias), _ptr(sel_bias),
                       _ptr(w1), _ptr(w3), _ptr(w2), _ptr(ws1), _ptr(ws3), _ptr(ws2), _ptr(y),
-                      None, None, None, None, None, None, None, None, _ptr(ws), ws.numel())
+                      None, None, _ptr(psum), _ptr(cpre), None, None, None, None, _ptr(ws),
+                      ws.numel())   # topk_ids, topk_w, prob_sum, counts_pre, counts, offsets,
+                                    # sorted_assign, assign_pos
         self._fn = _lib.moe_forward
 
     def __call__(self):
-        st = self._fn(*self._args, torch.cuda.current_stream(self.dev).cuda_stream)
+        stream = torch.cuda.current_stream(self.dev).cuda_stream
+        st = self._fn(*self._args, stream)
         if st != MOE_OK:
             raise MoEError("moe_forward", st)
+        if self.balance_alpha is not None:
+            st = _lib.moe_balance(*self._bal_args, stream)
+            if st != MOE_OK:
+                raise MoEError("moe_balance", st)
         return self.y
 
 

@@ -205,13 +205,35 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
   }
 }
 
-// prob_sum[e] = sum over top-k workgroups (in order) of their partial sums
-__global__ __launch_bounds__(256) void psum_reduce_kernel(const float* __restrict__ part, int nblk,
-                                                          int E, float* __restrict__ out) {
-  for (int e = threadIdx.x; e < E; e += 256) {
+// out[e] = sum over the nblk rows of a [nblk][E] table of per-workgroup partial sums (the top-k
+// workgroups' probability sums, or the backward's logit-bias gradient). A fixed tree, so the
+// result is identical from run to run: thread (c, e) adds the rows of chunk c of C = 1024/E
+// in order, eight loads in flight; then thread e adds the C chunk sums in order.
+__global__ __launch_bounds__(1024) void psum_reduce_kernel(const float* __restrict__ part, int nblk,
+                                                           int E, float* __restrict__ out) {
+  __shared__ float csum[1024];
+  const int tid = threadIdx.x;
+  const int C = 1024 / E;   // E <= 256: at least 4 chunks
+  const int c = tid / E, e = tid % E;
+  if (c < C) {
+    const int b0 = (int)((long long)nblk * c / C), b1 = (int)((long long)nblk * (c + 1) / C);
     float s = 0.f;
-    for (int b = 0; b < nblk; ++b) s += part[(size_t)b * E + e];
-    out[e] = s;
+    int b = b0;
+    for (; b + 8 <= b1; b += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = part[(size_t)(b + u) * E + e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += v[u];
+    }
+    for (; b < b1; ++b) s += part[(size_t)b * E + e];
+    csum[tid] = s;   // = csum[c * E + e]
+  }
+  __syncthreads();
+  if (tid < E) {
+    float t = 0.f;
+    for (int q = 0; q < C; ++q) t += csum[q * E + tid];
+    out[tid] = t;
   }
 }
 
@@ -270,7 +292,7 @@ hipError_t launch_route_logits(const moe_problem& p, const void* x, const void* 
 
 hipError_t launch_psum_reduce(const float* psum_part, int nblk, int E, float* prob_sum,
                               hipStream_t s) {
-  hipLaunchKernelGGL(psum_reduce_kernel, dim3(1), dim3(256), 0, s, psum_part, nblk, E, prob_sum);
+  hipLaunchKernelGGL(psum_reduce_kernel, dim3(1), dim3(1024), 0, s, psum_part, nblk, E, prob_sum);
   return hipGetLastError();
 }
 
@@ -285,7 +307,7 @@ hipError_t launch_route(const moe_problem& p, const void* x, const void* w_gate,
                           prob_sum ? psum_part : nullptr, s);
   if (err != hipSuccess) return err;
   if (!prob_sum) return hipSuccess;
-  hipLaunchKernelGGL(psum_reduce_kernel, dim3(1), dim3(256), 0, s, psum_part, nblk, p.E, prob_sum);
+  hipLaunchKernelGGL(psum_reduce_kernel, dim3(1), dim3(1024), 0, s, psum_part, nblk, p.E, prob_sum);
   return hipGetLastError();
 }
 

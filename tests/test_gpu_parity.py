@@ -240,6 +240,33 @@ def test_balance_statistics():
     assert L_o > 0.01        # a skewed router is above the balanced value alpha
 
 
+def test_prepared_forward_balance_statistics():
+    """The timed step with balance outputs (PreparedForward(balance_alpha=...)): y as the plain
+    forward, f / P / L as the oracle, also with many top-k workgroups (T = 16384 rows of partial
+    probability sums, the tree reduction's chunks longer than its 8-load batches)."""
+    import mixture_experts_layer_44_amd as moe
+    for w in (W("bal_prepared", T=2000, d=256, E=64, k=2, d_ff=128, seed=205,
+                capacity_factor=1.25, zipf_s=1.1),
+              W("bal_prepared_big", T=16384, d=128, E=24, k=2, d_ff=128, seed=206, zipf_s=1.1)):
+        inp = workloads.generate(w)
+        g = {k: (None if v is None else v.cuda()) for k, v in inp.items()}
+        p = moe.problem_for(w)
+        fwd = moe.PreparedForward(p, g["x"], g["w_gate"], g["w1"], g["w3"], g["w2"],
+                                  logit_bias=g["logit_bias"], balance_alpha=0.01)
+        y = fwd().clone()
+        y_ref, r = moe.forward(p, g["x"], g["w_gate"], g["w1"], g["w3"], g["w2"],
+                               logit_bias=g["logit_bias"], return_routing=True)
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_ref)
+        assert torch.equal(fwd.counts_pre, r["counts_pre"])
+        _, _, probs, _ = O.route(f64(inp["x"]), f64(inp["w_gate"]), w.k, f64(inp["logit_bias"]))
+        f_o, P_o, L_o = O.balance(O.align(r["topk_ids"].cpu().numpy(), w.E)["counts_pre"], probs,
+                                  w.T, w.k, 0.01)
+        np.testing.assert_allclose(fwd.f.cpu().numpy(), f_o, rtol=1e-6, atol=1e-7)
+        np.testing.assert_allclose(fwd.P.cpu().numpy(), P_o, rtol=1e-4, atol=1e-6)
+        assert abs(fwd.L.item() - L_o) <= 1e-4 * abs(L_o)
+
+
 def test_workspace_reuse_across_shapes():
     """One workspace sized for a large problem serves a smaller one; stale contents are ignored."""
     import mixture_experts_layer_44_amd as moe

@@ -45,6 +45,7 @@ class Workload:
     capacity_factor: float = 0.0   # <= 0: no capacity limit
     sel_bias: bool = False         # selection-only per-expert bias ~ U(-0.1, 0.1)
     zipf_s: float = 0.0            # per-expert logit offset -s*ln(e+1); 0 = none
+    balance_alpha: float = 0.0     # > 0: the layer also outputs f, P and L_balance (this alpha)
     weight_std: float = 0.02
 
     def with_tokens(self, T: int, seed: Optional[int] = None) -> "Workload":
@@ -74,7 +75,7 @@ WORKLOADS: Dict[str, Workload] = {
         _decode(1), _decode(8), _decode(32), _decode(128),
         # skewed routing with a capacity limit and dropping
         Workload(name="skew_cap", T=16384, d=4096, E=64, k=2, d_ff=1408, seed=44005,
-                 capacity_factor=1.25, zipf_s=1.1),
+                 capacity_factor=1.25, zipf_s=1.1, balance_alpha=0.01),
         # the handbook page's naive-vs-grouped check shape (fp32, 1 shared expert)
         Workload(name="handbook_fp32", T=50, d=64, E=16, k=4, d_ff=128, seed=44006,
                  dtype="f32", n_shared=1, d_ff_shared=128),

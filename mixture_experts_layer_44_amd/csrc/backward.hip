@@ -79,6 +79,9 @@ struct BwdArgs {
   int E, k, T;
   int ident;                // 1: one group of ident_rows rows in identity order (router)
   int ident_rows;
+  int ident_split;          // weights mode with ident: that group cut into this many groups of
+  int ident_chunk;          // ident_chunk consecutive rows (the last one shorter), each writing
+                            // its own [Mvalid, N] slice of Wf
   int Kvalid;               // B_WGATE: rows of B that exist (E)
   const int32_t* sorted_assign;
   Schedule sc;              // rows mode: the row-tile schedule; weights mode: the storage one
@@ -238,7 +241,7 @@ __global__ __launch_bounds__(WM * WN * 64) void bwd_gemm_kernel(BwdArgs a) {
     // rows of this group are stored from storage row sbase (the storage schedule)
     sbase = a.ident ? 0 : a.stor_start[g] * a.stor_bm;
   } else {
-    const int G = a.ident ? 1 : a.sc.G;
+    const int G = a.ident ? a.ident_split : a.sc.G;
     const int MT = a.M / BM, NTt = a.N / BN, total = G * MT * NTt;
     const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3, per = (total + 7) >> 3;
     if (slot >= per) return;
@@ -249,8 +252,13 @@ __global__ __launch_bounds__(WM * WN * 64) void bwd_gemm_kernel(BwdArgs a) {
     const int mt = rem / NTt;
     m0 = mt * BM;
     n0 = (rem - mt * NTt) * BN;
-    rows = a.ident ? a.ident_rows : a.sc.grp_rows[g];
-    sbase = a.ident ? 0 : a.stor_start[g] * a.stor_bm;
+    if (a.ident) {
+      sbase = g * a.ident_chunk;
+      rows = max(0, min(a.ident_chunk, a.ident_rows - sbase));
+    } else {
+      rows = a.sc.grp_rows[g];
+      sbase = a.stor_start[g] * a.stor_bm;
+    }
   }
   const bool shared_grp = !a.ident && g >= a.E;
   const int KT = MODE == M_ROWS ? a.K / BK : (rows + BK - 1) / BK;
@@ -530,7 +538,7 @@ __global__ __launch_bounds__(WM * WN * 64) void bwd_gemm_kernel(BwdArgs a) {
           }
         } else {
           const int m = m0 + lr;
-          if (m < a.Mvalid) a.Wf[(size_t)m * a.N + col] = val;
+          if (m < a.Mvalid) a.Wf[((size_t)g * a.Mvalid + m) * a.N + col] = val;
         }
       }
     }
@@ -904,6 +912,23 @@ hipError_t launch_rows(const BwdArgs& a, int tiles, bool deep_rows, hipStream_t 
   return hipGetLastError();
 }
 // The router's weight-gradient GEMM: 128 x kWgradBN tiles, 8 waves (2 x 4), a kWgradStages ring.
+// out[i] = sum over the S splits, in split order, of part[s][i] (float4 per thread)
+__global__ __launch_bounds__(256) void bwd_split_sum_kernel(const float* __restrict__ part, int S,
+                                                           long long n4, float* __restrict__ out) {
+  for (long long i = (long long)blockIdx.x * 256 + threadIdx.x; i < n4;
+       i += (long long)gridDim.x * 256) {
+    f32x4 acc = ((const f32x4*)part)[i];
+    for (int sp = 1; sp < S; ++sp) {
+      const f32x4 v = ((const f32x4*)part)[(size_t)sp * n4 + i];
+      acc[0] += v[0];
+      acc[1] += v[1];
+      acc[2] += v[2];
+      acc[3] += v[3];
+    }
+    ((f32x4*)out)[i] = acc;
+  }
+}
+
 template <int AK, int BKIND, int EPI>
 hipError_t launch_weights(const BwdArgs& a, int tiles, hipStream_t s) {
   if (tiles <= 0) return hipSuccess;
@@ -976,6 +1001,16 @@ BwdLayout backward_layout(const moe_problem& p) {
   L.dx_shared = take((size_t)p.n_shared * p.T * p.d * 4);
   L.dlog = take((size_t)p.T * L.E_pad * 2);
   L.dx_router = take((size_t)p.T * p.d * 4);
+  // The router weight gradient (K = T) has only (E_pad/128) x (d/128) output tiles: its K is
+  // cut into splits of whole 64-row steps, enough for ~256 workgroups, at least 512 rows each;
+  // the splits' fp32 partials are added in split order.
+  {
+    const int tiles = (L.E_pad / BBM) * (p.d / kWgradBN);
+    int split = std::max(1, std::min(ceil_div(256, std::max(tiles, 1)), p.T / 512));
+    L.wgate_rows = ceil_div(std::max(p.T, 1), split * 64) * 64;
+    L.wgate_split = ceil_div(std::max(p.T, 1), L.wgate_rows);
+    L.wgate_part = take(L.wgate_split > 1 ? (size_t)L.wgate_split * p.E * p.d * 4 : 0);
+  }
   L.total = off;
   return L;
 }
@@ -1182,12 +1217,21 @@ hipError_t launch_backward(const moe_problem& p, const BwdLayout& L, void* ws, c
     a.N = p.d;
     a.ident = 1;
     a.ident_rows = p.T;
-    a.Wf = dw_gate;
+    a.ident_split = L.wgate_split;
+    a.ident_chunk = L.wgate_rows;
+    float* part = L.wgate_split > 1 ? (float*)at(L.wgate_part) : dw_gate;
+    a.Wf = part;
     a.Mvalid = p.E;
-    const int tiles = (L.E_pad / BBM) * (p.d / kWgradBN);
-    // (T = 0: the K loop is empty and every tile writes zeros)
+    const int tiles = L.wgate_split * (L.E_pad / BBM) * (p.d / kWgradBN);
+    // (T = 0: one split whose K loop is empty, so every tile writes zeros)
     err = launch_weights<AT_IDENT, BT_IDENT, EPI_WF32>(a, tiles, s);
     MOE_TRY(err);
+    if (L.wgate_split > 1) {
+      const long long n4 = (long long)p.E * p.d / 4;
+      hipLaunchKernelGGL(bwd_split_sum_kernel, dim3((unsigned)std::min<long long>(ceil_div(n4, 256), 1024)),
+                         dim3(256), 0, s, part, L.wgate_split, n4, dw_gate);
+      MOE_TRY(hipGetLastError());
+    }
   }
   MOE_TRY(mark());
   // 10. dx

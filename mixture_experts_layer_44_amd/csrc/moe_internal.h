@@ -151,8 +151,10 @@ struct BwdLayout {
   size_t grp_rows, grp_off, mt_start, mt_group, logits_part, dlb_part, zero;
   size_t r_grp_rows, r_grp_off, r_mt_start, r_mt_group;   // the row-tile schedule
   size_t H, U, V, DUV, DO, XS, dyb, dgate_part, dx_rows, dx_shared, dlog, dx_router;
+  size_t wgate_part;   // the router weight gradient's per-split fp32 partials (wgate_split > 1)
   size_t total;
   int max_mt, max_mt_rows, E_pad, NT_down, nblk_router, stor_bm;
+  int wgate_split, wgate_rows;   // token splits of that GEMM's K, and the rows of each
 };
 BwdLayout backward_layout(const moe_problem& p);
 hipError_t launch_backward(const moe_problem& p, const BwdLayout& L, void* ws, const void* x,

@@ -93,6 +93,8 @@ CASES = [
     W("bwd_k_eq_E", T=100, d=128, E=8, k=8, d_ff=128, seed=508),
     # ~150 rows per expert: the recompute runs the forward's ragged 192-row class
     W("bwd_mid192", T=600, d=512, E=8, k=2, d_ff=384, seed=511, n_shared=1, d_ff_shared=384),
+    # the router weight gradient's K (T = 4096) cut into 8 token splits
+    W("bwd_router_split", T=4096, d=256, E=8, k=2, d_ff=128, seed=512, zipf_s=1.1),
 ]
 
 

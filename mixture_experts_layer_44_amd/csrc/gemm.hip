@@ -12,16 +12,20 @@
 //          token order (shared).
 //
 // Tile classes, chosen on the host per problem from the expected rows per expert r:
-//   small   (r <= 48)     gemm_bf16_kernel, BM=32, BNB=256 / 128, BK=64, 4-stage ring, 4 waves
-//                         (1x4): many workgroups stream the touched experts' weights (decode).
+//   decode  (r <= 48, d and d_ff multiples of 256 up to 2048) gemm_bf16_dec_kernel: 32-row
+//                         m-tiles x 32 (gate-up) / 64 (down) features, the 4 waves splitting K
+//                         and streaming their operands straight into registers.
+//   small   (r <= 48, other d / d_ff) gemm_bf16_kernel, BM=32, BNB=256 / 128, BK=64, 4-stage
+//                         ring, 4 waves (1x4): many workgroups stream the touched experts' weights.
 //   ragged  (48 < r < 768) gemm_bf16_st_kernel, BM=128 / 192 (8 waves, 2x4) or 256 (4x2),
 //                         BNB=256, BK=64; B in the deep ring, A in the shallow one; the rows of
 //                         a tile past its segment's end are neither loaded nor multiplied.
 //   wide    (r >= 768)    gemm_bf16_st_kernel, BM=256, BNB=256, 8 waves (4x2), A in the deep
 //                         ring (the weight tiles are shared in L2 by several m-tiles).
 //   d % 256 != 0          gemm_bf16_kernel, BM=128, BNB=256 / 128, BK=64, 3-stage ring.
-// Each wave owns a block of 32x32 MFMA tiles (v_mfma_f32_32x32x16_bf16, fp32 accumulators).
-// Two waves per SIMD: while one waits for its LDS fragments the other issues MFMAs.
+// Except in the decode class, each wave owns a block of 32x32 MFMA tiles
+// (v_mfma_f32_32x32x16_bf16, fp32 accumulators), two waves per SIMD: while one waits for its
+// LDS fragments the other issues MFMAs.
 // BNB counts B rows: the gate-up B tile holds the W1 rows and then the W3 rows of the same
 // BNB/2 features, and each wave reads the u and v fragments of the same features, so the
 // SwiGLU epilogue has u and v of an output in the same lane.

@@ -50,12 +50,12 @@ COPY_PATTERN = r"copyBuffer"   # the runtime's blit kernel (the calibration copy
 def gemm_stage(kernel_name: str):
     """'gate_up' / 'down' for a grouped-GEMM kernel name as rocprofv3 prints it, else None.
     The gate-up flag is the 7th template argument of gemm_bf16_kernel, the 5th of
-    gemm_bf16_st_kernel and the only one of gemm_f32_kernel."""
-    m = re.search(r"gemm_(bf16_st|bf16|f32)_kernel<([^>]*)>", kernel_name)
+    gemm_bf16_st_kernel and the first of gemm_bf16_dec_kernel and gemm_f32_kernel."""
+    m = re.search(r"gemm_(bf16_st|bf16_dec|bf16|f32)_kernel<([^>]*)>", kernel_name)
     if not m:
         return None
     args = [a.strip() for a in m.group(2).split(",")]
-    pos = {"bf16": 6, "bf16_st": 4, "f32": 0}[m.group(1)]
+    pos = {"bf16": 6, "bf16_st": 4, "bf16_dec": 0, "f32": 0}[m.group(1)]
     if len(args) <= pos or args[pos] not in ("true", "false"):
         return None
     return "gate_up" if args[pos] == "true" else "down"

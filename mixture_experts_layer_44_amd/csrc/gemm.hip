@@ -20,8 +20,9 @@
 //   ragged  (48 < r < 768) gemm_bf16_st_kernel, BM=128 / 192 (8 waves, 2x4) or 256 (4x2),
 //                         BNB=256, BK=64; B in the deep ring, A in the shallow one; the rows of
 //                         a tile past its segment's end are neither loaded nor multiplied.
-//   wide    (r >= 768)    gemm_bf16_st_kernel, BM=256, BNB=256, 8 waves (4x2), A in the deep
-//                         ring (the weight tiles are shared in L2 by several m-tiles).
+//   wide    (r >= 768)    gemm_bf16_kernel, BM=256, BNB=256, 8 waves (4x2), 2 stages with
+//                         register staging (the weight tiles are shared in L2 by several
+//                         m-tiles; the loads run faster through registers than straight to LDS).
 //   d % 256 != 0          gemm_bf16_kernel, BM=128, BNB=256 / 128, BK=64, 3-stage ring.
 // Except in the decode class, each wave owns a block of 32x32 MFMA tiles
 // (v_mfma_f32_32x32x16_bf16, fp32 accumulators), two waves per SIMD: while one waits for its
@@ -32,17 +33,21 @@
 //
 // Main loop of gemm_bf16_kernel: a ring of STAGES LDS buffers, each one K step of BK for all
 // BM + BNB rows, filled by direct global->LDS loads (global_load_lds_dwordx4, 16 bytes per
-// lane, 1 KB per instruction) with no register staging. STAGES-1 steps are in flight while the MFMAs
-// consume one; each step is one wait for this wave's loads of the step, one barrier, the
-// loads of step kt+STAGES-1 into the buffer freed by step kt-1, and the MFMAs of step kt.
-// Past the last step the loads repeat the last step into a buffer nobody reads again, so
-// the loop has no branches. Each LDS row is BK*2 bytes (BK/8 chunks of 16); chunk c of row r
-// sits in a swizzled slot (see swz) so 16 consecutive rows at one logical chunk cover all 16
-// 16-byte bank groups of a 256-byte LDS cycle.
+// lane, 1 KB per instruction). STAGES-1 steps are in flight while the MFMAs consume one; each
+// step is one wait for this wave's loads of the step, one barrier, the loads of step
+// kt+STAGES-1 into the buffer freed by step kt-1, and the MFMAs of step kt. Past the last step
+// the loads repeat the last step into a buffer nobody reads again, so the loop has no
+// branches. With RS (register staging, 2 stages) the same 16-byte pieces go through registers
+// instead: loaded during step kt, stored into the other stage at its end. Each LDS row is
+// BK*2 bytes (BK/8 chunks of 16); chunk c of row r sits in a swizzled slot (see swz) so 16
+// consecutive rows at one logical chunk cover all 16 16-byte bank groups of a 256-byte LDS
+// cycle.
 //
-// In gemm_bf16_kernel and the wide class, rows of an m-tile past the end of its segment are
-// loaded from the segment's first row; their results land only in padding rows of H (gate-up)
-// or are not stored (down).
+// In gemm_bf16_kernel, rows of an m-tile past the end of its segment are loaded from the
+// segment's first row; their results land only in padding rows of H (gate-up) or are not
+// stored (down). The wide class keeps them on purpose: with every tile the same length, the
+// m-tiles that share a weight tile stay in step and meet in L2 (skipping the padding of a
+// segment's last tile doubled FETCH_SIZE at unchanged time).
 //
 // Work order: tiles are numbered group-major, then n-tile, then m-tile, so neighbouring
 // tiles share a weight tile (B) or a row block (A). Workgroups are dealt round-robin to
@@ -75,7 +80,7 @@ struct GemmArgs {
   float* V;
 };
 
-template <int BM, int BNB, int WM, int WN, int BK, int STAGES, bool GATEUP>
+template <int BM, int BNB, int WM, int WN, int BK, int STAGES, bool GATEUP, bool RS = false>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs args) {
   constexpr int NW = WM * WN;
   constexpr int CHUNKS = BK / 8;                   // 16-byte chunks per row per stage
@@ -92,8 +97,12 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs args) 
   static_assert(BM % RPI == 0 && (BNB / 2) % RPI == 0, "a 1 KB load covers rows of one matrix");
   __shared__ __attribute__((aligned(1024))) bf16_t smem[STAGES * STAGE];
 
+  // with the K range split in two (down GEMM only), work unit = (half, tile), as in the
+  // staggered kernel below
+  const int S = GATEUP ? 1 : args.ksplit;
   TileCoord tc;
-  if (!tile_coord(args.sc, args.N / FEAT, FEAT, tc)) return;
+  int half = 0;
+  if (!tile_coord(args.sc, args.N / FEAT, FEAT, tc, S, &half)) return;
   const bool shared_grp = tc.g >= args.E;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -134,10 +143,11 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs args) 
       src_off[i] = (uint32_t)(second ? br - BNB / 2 : br) * (uint32_t)K + lchunk * 8;
     }
   }
-  const int KT = K / BK;
+  const int KT = K / BK / S;                       // steps of this work unit
+  const int k0 = half * KT * BK;                    // its first K element
   auto issue = [&](int kt, int st) {
     bf16_t* dst = smem + st * STAGE;
-    const int kk = kt * BK;
+    const int kk = k0 + kt * BK;
 #pragma unroll
     for (int i = 0; i < DMA_WAVE; ++i) {
       const int q = wave * DMA_WAVE + i;
@@ -202,18 +212,51 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs args) 
     }
   };
 
+  if constexpr (RS) {
+    // Register-staged: each lane loads its 16-byte pieces of step kt+1 into registers while
+    // step kt computes, then stores them (ds_write_b128, the same places the direct loads
+    // fill) into the other stage; one barrier per step.
+    static_assert(STAGES == 2, "two stages: compute one while the other is written");
+    u32x4 stg[DMA_WAVE];
+    auto load_regs = [&](int kt) {
 #pragma unroll
-  for (int s = 0; s < STAGES - 1; ++s) issue(s < KT ? s : KT - 1, s);
-  for (int kt = 0; kt < KT; ++kt) {
-    // this wave's loads of step kt are done once at most STAGES-2 steps remain in flight;
-    // then one barrier makes every wave's part visible and retires step kt-1's buffer. (A
-    // bare s_barrier: a release fence here would also drain the loads still in flight.)
-    __builtin_amdgcn_s_waitcnt(wait_vm((STAGES - 2) * DMA_WAVE));
+      for (int i = 0; i < DMA_WAVE; ++i)
+        stg[i] = *(const u32x4*)(src_base[i] + src_off[i] + k0 + kt * BK);
+    };
+    auto write_regs = [&](int st) {
+      bf16_t* dst = smem + st * STAGE;
+#pragma unroll
+      for (int i = 0; i < DMA_WAVE; ++i)
+        *(u32x4*)(dst + (wave * DMA_WAVE + i) * RPI * BK + lane * 8) = stg[i];
+    };
+    load_regs(0);
+    write_regs(0);
+    load_regs(KT > 1 ? 1 : 0);
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's stores are in LDS
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    const int nxt = kt + STAGES - 1;
-    issue(nxt < KT ? nxt : KT - 1, nxt % STAGES);
-    compute(smem + (kt % STAGES) * STAGE);
+    for (int kt = 0; kt < KT; ++kt) {
+      compute(smem + (kt & 1) * STAGE);
+      write_regs((kt + 1) & 1);            // step kt+1 (past the end: a copy nobody reads)
+      load_regs(kt + 2 < KT ? kt + 2 : KT - 1);
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else {
+#pragma unroll
+    for (int s = 0; s < STAGES - 1; ++s) issue(s < KT ? s : KT - 1, s);
+    for (int kt = 0; kt < KT; ++kt) {
+      // this wave's loads of step kt are done once at most STAGES-2 steps remain in flight;
+      // then one barrier makes every wave's part visible and retires step kt-1's buffer. (A
+      // bare s_barrier: a release fence here would also drain the loads still in flight.)
+      __builtin_amdgcn_s_waitcnt(wait_vm((STAGES - 2) * DMA_WAVE));
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      const int nxt = kt + STAGES - 1;
+      issue(nxt < KT ? nxt : KT - 1, nxt % STAGES);
+      compute(smem + (kt % STAGES) * STAGE);
+    }
   }
   __builtin_amdgcn_s_waitcnt(wait_vm(0));
 
@@ -241,7 +284,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs args) 
           const int rg = tc.m_local * BM + lr;
           if (rg < tc.rows) {
             float* dst = shared_grp ? args.shared_out + (size_t)rg * N
-                                    : args.out_rows + (size_t)(tc.off + rg) * N;
+                                    : (half ? args.out_rows_b : args.out_rows) +
+                                          (size_t)(tc.off + rg) * N;
             dst[col] = acc[i][j][r];
           }
         }
@@ -250,22 +294,19 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs args) 
 }
 
 // ------------------------------------------------------------------ staggered rings
-// With one K step of loads in flight (a 2-stage ring) a large tile is paced by the latency of
-// its loads under full load, not by its MFMAs, and a third full stage does not fit in 160 KB
-// of LDS. Here both operands still go straight to LDS, but in two rings of different depth:
-// the "shallow" operand in 2 slots, issued one step ahead, and the "deep" operand in 3 slots,
-// issued two steps ahead. Which one is deep depends on where its data lives: the weights
-// (B) when they stream from HBM (small experts, each weight tile read by one m-tile), the
-// gathered rows (A) when the weight tiles are shared in L2 by several m-tiles.
-//   step kt: wait until only this wave's deep loads issued in step kt-1 are outstanding (so the
-//            shallow loads of step kt, issued before them, and the deep loads of step kt,
-//            issued earlier, have landed); barrier; issue shallow(kt+1) and then deep(kt+2);
-//            MFMAs of step kt.
-// Vector-memory loads retire in order, so issuing the shallow operand first is what lets the
-// wait leave the deep loads in flight; the same ordering is why a deeper ring would not help:
-// every wait retires all loads issued before the shallow operand's loads of that step. Every slot written in step kt was last read in step
-// kt-1, which all waves finished before this step's barrier.
-template <int BM, int BNB, int WM, int WN, bool GATEUP, bool DEEPB>
+// The ragged classes: each weight tile streams from HBM for about one m-tile, so the weights
+// (B) need more latency tolerance than a 2-stage ring gives, and a third full stage does not
+// fit in 160 KB of LDS. Both operands go straight to LDS, in two rings of different depth: the
+// gathered rows (A, "shallow") in 2 slots, issued one step ahead, and the weights (B, "deep")
+// in 3 slots, issued two steps ahead.
+//   step kt: wait until only this wave's B loads issued in step kt-1 are outstanding (so the A
+//            loads of step kt, issued before them, and the B loads of step kt, issued earlier,
+//            have landed); barrier; issue A(kt+1) and then B(kt+2); MFMAs of step kt.
+// Vector-memory loads retire in order, so issuing A first is what lets the wait leave the B
+// loads in flight; the same ordering is why a deeper ring would not help: every wait retires
+// all loads issued before that step's A loads. Every slot written in step kt was last read in
+// step kt-1, which all waves finished before this step's barrier.
+template <int BM, int BNB, int WM, int WN, bool GATEUP>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_st_kernel(GemmArgs args) {
   constexpr int BK = 64, NKS = BK / 16;
   constexpr int NW = WM * WN;
@@ -280,7 +321,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_st_kernel(GemmArgs arg
   static_assert(!GATEUP || FN % 2 == 0, "u and v fragments pair up");
   static_assert((BNB / 2) % RPI == 0, "a B row group stays within one matrix");
   constexpr int DS = 3;                                     // slots of the deep ring
-  constexpr int NA = DEEPB ? 2 : DS, NB = DEEPB ? DS : 2;   // ring slots of A and B
+  constexpr int NA = 2, NB = DS;                            // ring slots of A and B
   static_assert((NA * ASLOT + NB * BSLOT) * 2 <= 160 * 1024, "rings fit in LDS");
   __shared__ __attribute__((aligned(1024))) bf16_t smem[NA * ASLOT + NB * BSLOT];
   bf16_t* const As = smem;
@@ -350,7 +391,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_st_kernel(GemmArgs arg
     bf16_t* dst = As + slot * ASLOT;
 #pragma unroll
     for (int i = 0; i < DMA_A; ++i) {
-      if (DEEPB && (wave * DMA_A + i) * RPI >= rows_here) continue;   // wave-uniform
+      if ((wave * DMA_A + i) * RPI >= rows_here) continue;   // wave-uniform
       __builtin_amdgcn_global_load_lds((const void*)(args.A + aoff[i] + k0 + kt * BK),
                                        (lds_ptr_t)(dst + (wave * DMA_A + i) * RPI * BK), 16, 0, 0);
     }
@@ -396,15 +437,9 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_st_kernel(GemmArgs arg
   };
 
   // prologue: shallow(0), deep(0), deep(1)
-  auto issue_shallow = [&](int kt) {
-    if (DEEPB) issue_a(kt, kt & 1);
-    else issue_b(kt, kt & 1);
-  };
-  auto issue_deep = [&](int kt) {
-    if (DEEPB) issue_b(kt, kt % DS);
-    else issue_a(kt, kt % DS);
-  };
-  constexpr int DEEP_OPS = DEEPB ? DMA_B : DMA_A;
+  auto issue_shallow = [&](int kt) { issue_a(kt, kt & 1); };
+  auto issue_deep = [&](int kt) { issue_b(kt, kt % DS); };
+  constexpr int DEEP_OPS = DMA_B;
   // The K loop for a wave whose first NF row fragments hold data: the others are all padding
   // rows, so their LDS reads and MFMAs are skipped (NF = 0: the wave only loads and waits).
   auto k_loop = [&](auto nf_tag) {
@@ -447,12 +482,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_st_kernel(GemmArgs arg
       }
     }
   };
-  // Padding work is skipped only with A as the shallow operand (the ragged classes). The wide
-  // class keeps every tile the same length: a segment's last tile finishing early let the
-  // following tiles start out of step, and the m-tiles that share a weight tile then stopped
-  // meeting in L2 (FETCH_SIZE doubled at unchanged time).
   static_assert(FM <= 3, "the K-loop dispatch covers up to three row fragments per wave");
-  const int nf = DEEPB ? min(FM, max(0, (rows_here - wm * 32 + WM * 32 - 1) / (WM * 32))) : FM;
+  const int nf = min(FM, max(0, (rows_here - wm * 32 + WM * 32 - 1) / (WM * 32)));
   if (nf >= FM) k_loop(std::integral_constant<int, FM>{});
   else if (nf == 2) k_loop(std::integral_constant<int, (FM > 2 ? 2 : 0)>{});
   else if (nf == 1) k_loop(std::integral_constant<int, (FM > 1 ? 1 : 0)>{});
@@ -827,33 +858,34 @@ hipError_t launch_dec(const moe_problem& p, const GemmArgs& a, const GemmArgs& b
   return hipGetLastError();
 }
 
-template <int BM, int BNB_UP, int WM_UP, int WN_UP, int BNB_DN, int WM_DN, int WN_DN, int BK, int ST>
+template <int BM, int BNB_UP, int WM_UP, int WN_UP, int BNB_DN, int WM_DN, int WN_DN, int BK, int ST,
+          bool RS = false>
 hipError_t launch_bf16(const moe_problem& p, const GemmArgs& a, const GemmArgs& b, hipStream_t s,
                        hipEvent_t between, bool up_only) {
   if (p.d_ff % (BNB_UP / 2) || p.d % BNB_DN) return hipErrorInvalidValue;   // n-tiles cover N
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BNB_UP, WM_UP, WN_UP, BK, ST, true>),
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BNB_UP, WM_UP, WN_UP, BK, ST, true, RS>),
                      dim3(grid_for(a.sc.max_mtiles, p.d_ff / (BNB_UP / 2))), dim3(WM_UP * WN_UP * 64),
                      0, s, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || up_only) return err;
   if (between && (err = hipEventRecord(between, s)) != hipSuccess) return err;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BNB_DN, WM_DN, WN_DN, BK, ST, false>),
-                     dim3(grid_for(b.sc.max_mtiles, p.d / BNB_DN)), dim3(WM_DN * WN_DN * 64), 0, s,
-                     b);
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BNB_DN, WM_DN, WN_DN, BK, ST, false, RS>),
+                     dim3(grid_for(b.sc.max_mtiles * b.ksplit, p.d / BNB_DN)),
+                     dim3(WM_DN * WN_DN * 64), 0, s, b);
   return hipGetLastError();
 }
 
-template <int BM, int BNB_UP, int WM_UP, int WN_UP, int BNB_DN, int WM_DN, int WN_DN, bool DEEPB>
+template <int BM, int BNB_UP, int WM_UP, int WN_UP, int BNB_DN, int WM_DN, int WN_DN>
 hipError_t launch_bf16_st(const moe_problem& p, const GemmArgs& a, const GemmArgs& b,
                           hipStream_t s, hipEvent_t between, bool up_only) {
   if (p.d_ff % (BNB_UP / 2) || p.d % BNB_DN) return hipErrorInvalidValue;   // n-tiles cover N
-  hipLaunchKernelGGL((gemm_bf16_st_kernel<BM, BNB_UP, WM_UP, WN_UP, true, DEEPB>),
+  hipLaunchKernelGGL((gemm_bf16_st_kernel<BM, BNB_UP, WM_UP, WN_UP, true>),
                      dim3(grid_for(a.sc.max_mtiles, p.d_ff / (BNB_UP / 2))), dim3(WM_UP * WN_UP * 64),
                      0, s, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || up_only) return err;
   if (between && (err = hipEventRecord(between, s)) != hipSuccess) return err;
-  hipLaunchKernelGGL((gemm_bf16_st_kernel<BM, BNB_DN, WM_DN, WN_DN, false, DEEPB>),
+  hipLaunchKernelGGL((gemm_bf16_st_kernel<BM, BNB_DN, WM_DN, WN_DN, false>),
                      dim3(grid_for(b.sc.max_mtiles * b.ksplit, p.d / BNB_DN)),
                      dim3(WM_DN * WN_DN * 64), 0, s, b);
   return hipGetLastError();
@@ -901,13 +933,13 @@ hipError_t launch_expert_ffn(const moe_problem& p, const void* x, const void* w1
     b.out_rows_b = out_rows_b;
     if (!up_only && b.ksplit == 2 && !out_rows_b) return hipErrorInvalidValue;
     if (sc.BM == 256 && gemm_wide(p))
-      return launch_bf16_st<256, 256, 4, 2, 256, 4, 2, false>(p, a, b, s, between, up_only);
-    if (sc.BM == 256) return launch_bf16_st<256, 256, 4, 2, 256, 4, 2, true>(p, a, b, s, between, up_only);
-    if (sc.BM == 192) return launch_bf16_st<192, 256, 2, 4, 256, 2, 4, true>(p, a, b, s, between, up_only);
+      return launch_bf16<256, 256, 4, 2, 256, 4, 2, 64, 2, true>(p, a, b, s, between, up_only);
+    if (sc.BM == 256) return launch_bf16_st<256, 256, 4, 2, 256, 4, 2>(p, a, b, s, between, up_only);
+    if (sc.BM == 192) return launch_bf16_st<192, 256, 2, 4, 256, 2, 4>(p, a, b, s, between, up_only);
     if (sc.BM == kDecBM && gemm_dec(p)) return launch_dec(p, a, b, s, between, up_only);
     if (sc.BM == 32) return launch_bf16<32, 256, 1, 4, 128, 1, 4, 64, 4>(p, a, b, s, between, up_only);
     // down tiles of 256 output features need d % 256 == 0 (the entry points accept d % 128)
-    if (p.d % 256 == 0) return launch_bf16_st<128, 256, 2, 4, 256, 2, 4, true>(p, a, b, s, between, up_only);
+    if (p.d % 256 == 0) return launch_bf16_st<128, 256, 2, 4, 256, 2, 4>(p, a, b, s, between, up_only);
     return launch_bf16<128, 256, 2, 4, 128, 2, 4, 64, 3>(p, a, b, s, between, up_only);
   }
   if (up_only) return hipErrorInvalidValue;   // the backward runs on bf16 storage only

@@ -50,6 +50,9 @@ def test_gemm_stage_names():
     assert bench.gemm_stage("moe::gemm_bf16_st_kernel<256, 256, 4, 2, false, false>(x)") == "down"
     assert bench.gemm_stage("moe::gemm_bf16_kernel<128, 256, 2, 4, 64, 3, true>(x)") == "gate_up"
     assert bench.gemm_stage("moe::gemm_bf16_kernel<32, 128, 1, 4, 64, 4, false>(x)") == "down"
+    assert bench.gemm_stage("moe::gemm_bf16_kernel<256, 256, 4, 2, 64, 2, true, true>(x)") == "gate_up"
+    assert bench.gemm_stage("moe::gemm_bf16_dec_kernel<true, 8>(x)") == "gate_up"
+    assert bench.gemm_stage("moe::gemm_bf16_dec_kernel<false, 3>(x)") == "down"
     assert bench.gemm_stage("moe::gemm_f32_kernel<false>(x)") == "down"
     assert bench.gemm_stage("__amd_rocclr_copyBuffer") is None
     assert bench.gemm_stage("moe::combine_kernel(float const*)") is None

@@ -272,13 +272,15 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs args) 
       for (int r = 0; r < 16; ++r) {
         const int lr = wm * TM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         if (GATEUP) {
-          const float u = acc[i][j][r];
-          const float v = acc[i][j + FN / 2][r];
-          const size_t o = (size_t)(tc.mt_global * BM + lr) * N + col;
-          args.H[o] = f32_to_bf16(silu_f(u) * v);
-          if (args.U) {
-            args.U[o] = u;
-            args.V[o] = v;
+          if (tc.m_local * BM + lr < tc.rows) {   // padding rows of H are never read
+            const float u = acc[i][j][r];
+            const float v = acc[i][j + FN / 2][r];
+            const size_t o = (size_t)(tc.mt_global * BM + lr) * N + col;
+            args.H[o] = f32_to_bf16(silu_f(u) * v);
+            if (args.U) {
+              args.U[o] = u;
+              args.V[o] = v;
+            }
           }
         } else {
           const int rg = tc.m_local * BM + lr;

@@ -58,7 +58,6 @@ constexpr int BBM = 128;   // rows of a weight-gradient m-tile (rows of the weig
 constexpr int kWgradStages = 2;
 constexpr int kWgradBN = 128;
 constexpr int kRowsBM = 256;      // m-tile of the row-tiled GEMMs (ragged, staggered rings)
-constexpr int kDeepRowsFrom = 0;  // < 0: never put the rows in the deep ring
 constexpr int ZERO_ELEMS = 256;
 
 enum AKind : int { A_TOKEN, A_STORE, A_IDENT, AT_STORE, AT_IDENT };
@@ -97,7 +96,7 @@ struct BwdArgs {
   int Msplit;
   float* Wf;                // EPI_WF32: [Mvalid, N]
   int Mvalid;
-  const float* U;           // EPI_DDOWN: u, v (fp32 storage rows, width N)
+  const float* U;           // EPI_DDOWN: u, v (fp32 storage rows, width N, fragment order)
   const float* V;
   const float* topk_w;
   bf16_t* DUV;              //            du | dv (bf16 storage rows, width 2N)
@@ -170,6 +169,24 @@ __device__ __forceinline__ void tr_frags(const bf16_t* st, const int (&base)[NF]
                                                                 3, 4, 5, 6, 7));
 }
 
+// The same reads through the compiler builtin, for kernels with no global->LDS loads in flight
+// (register-staged rings): the compiler then places the LDS waits itself, and the reads of one
+// sub-step can overlap the MFMAs of the previous one.
+template <int W, int NF>
+__device__ __forceinline__ void tr_frags_bi(const bf16_t* st, const int (&base)[NF], int ks,
+                                            bf16x8 (&out)[NF]) {
+  typedef __attribute__((address_space(3))) v4s lds_v4s;
+  const int kofs = ks * 16 * W;
+#pragma unroll
+  for (int f = 0; f < NF; ++f) {
+    const __attribute__((address_space(3))) bf16_t* p =
+        (const __attribute__((address_space(3))) bf16_t*)(st + base[f] + kofs);
+    const v4s r0 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)p);
+    const v4s r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s*)(p + 4 * W));
+    out[f] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(r0, r1, 0, 1, 2, 3, 4, 5, 6, 7));
+  }
+}
+
 // This lane's element offset, in a transposed [k][W] stage, of the first of the 4 rows it
 // points at for the operand block whose first column is mb (sub-step 0, first read):
 // lane i of each 16-lane group points at row 8*(group/2) + i/4, column mb + 16*(group%2) + 4*(i%4).
@@ -189,8 +206,12 @@ __device__ __forceinline__ int tr_base(int lane, int mb) {
 // weights, in 3 slots two steps ahead; A issued first in each step so that the step's wait
 // leaves only B's latest loads in flight. The A row groups past a tile's last row with data
 // are then not loaded at all, and a wave skips the fragments that are all padding.
+// RS (rows mode, ST == 2): both operands go through registers instead, each lane storing its
+// 16-byte pieces of step k+1 at the places the direct loads fill while step k computes; the
+// weight fragments are then read with the transpose builtin (with direct loads in flight the
+// compiler drains them before every builtin read). Same padding skip as staggered.
 template <int BM, int BN, int WM, int WN, int MODE, int AK, int BKIND, int EPI, int ST,
-          bool DEEPA = false>
+          bool RS = false>
 __global__ __launch_bounds__(WM * WN * 64) void bwd_gemm_kernel(BwdArgs a) {
   constexpr int BK = 64, NW = WM * WN, NKS = BK / 16;
   constexpr int TM = BM / WM, TN = BN / WN, FM = TM / 32, FN = TN / 32;
@@ -198,11 +219,13 @@ __global__ __launch_bounds__(WM * WN * 64) void bwd_gemm_kernel(BwdArgs a) {
   constexpr bool STAG = ST == 0;
   constexpr int ASZ = BM * BK, BSZ = BN * BK;
   // ring slots of A and B (staggered: the deep operand has 3, the shallow one 2)
-  constexpr int NA = STAG ? (DEEPA ? 3 : 2) : ST, NB = STAG ? (DEEPA ? 2 : 3) : ST;
+  constexpr int NA = STAG ? 2 : ST, NB = STAG ? 3 : ST;   // RS: ST = 2
   constexpr int DMA_A = ASZ * 2 / 1024 / NW, DMA_B = BSZ * 2 / 1024 / NW;
   static_assert(DMA_A * 1024 * NW == ASZ * 2 && DMA_B * 1024 * NW == BSZ * 2, "even split");
   static_assert(FM >= 1 && FN >= 1 && FM <= 3, "wave tile covers whole fragments");
   static_assert(!STAG || (MODE == M_ROWS && !ATR), "staggered rings: rows mode only");
+  static_assert(!RS || (ST == 2 && MODE == M_ROWS && !ATR), "register staging: rows mode, 2 slots");
+  constexpr bool SKIPA = STAG || RS;   // A row groups past the data are skipped
   static_assert((NA * ASZ + NB * BSZ) * 2 <= 160 * 1024, "rings fit in LDS");
   static_assert(EPI != EPI_DDOWN || (NA * ASZ + NB * BSZ) * 2 >= (WN + 1) * BM * 4,
                 "the ring holds the epilogue's row sums");
@@ -303,7 +326,7 @@ __global__ __launch_bounds__(WM * WN * 64) void bwd_gemm_kernel(BwdArgs a) {
     for (int i = 0; i < DMA_A; ++i) {
       const bf16_t* src;
       if (!ATR) {
-        if (STAG && !DEEPA && (wave * DMA_A + i) * 8 >= rows_here) continue;   // wave-uniform
+        if (SKIPA && (wave * DMA_A + i) * 8 >= rows_here) continue;   // wave-uniform
         src = a.A + aoff[i] + kt * BK;
       } else {
         const int r = kt * BK + akrow[i];
@@ -333,28 +356,29 @@ __global__ __launch_bounds__(WM * WN * 64) void bwd_gemm_kernel(BwdArgs a) {
     bmat0 = shared_grp ? a.S0 : a.B0 + (size_t)g * msz;
     bmat1 = shared_grp ? a.S1 : a.B1 + (size_t)g * msz;
   }
+  // source of B load i of step kt
+  auto b_src = [&](int i, int kt) -> const bf16_t* {
+    const int r = kt * BK + bkrow[i];
+    if (BKIND == B_W2) {
+      return bmat0 + (uint32_t)r * (uint32_t)a.ldb + n0 + blch[i] * 8;
+    } else if (BKIND == B_W13) {
+      const int half = a.K / 2;
+      return r < half ? bmat0 + (uint32_t)r * (uint32_t)a.ldb + n0 + blch[i] * 8
+                      : bmat1 + (uint32_t)(r - half) * (uint32_t)a.ldb + n0 + blch[i] * 8;
+    } else if (BKIND == B_WGATE) {
+      return r < a.Kvalid ? a.B0 + (uint32_t)r * (uint32_t)a.ldb + n0 + blch[i] * 8
+                          : a.zero + blch[i] * 8;
+    } else {
+      return r < rows ? a.B0 + (uint32_t)(sbase + r) * (uint32_t)a.ldb + n0 + blch[i] * 8
+                      : a.zero + blch[i] * 8;
+    }
+  };
   auto issue_b = [&](int kt, int slot) {
     bf16_t* dst = Bs + slot * BSZ;
 #pragma unroll
-    for (int i = 0; i < DMA_B; ++i) {
-      const int r = kt * BK + bkrow[i];
-      const bf16_t* src;
-      if (BKIND == B_W2) {
-        src = bmat0 + (uint32_t)r * (uint32_t)a.ldb + n0 + blch[i] * 8;
-      } else if (BKIND == B_W13) {
-        const int half = a.K / 2;
-        src = r < half ? bmat0 + (uint32_t)r * (uint32_t)a.ldb + n0 + blch[i] * 8
-                       : bmat1 + (uint32_t)(r - half) * (uint32_t)a.ldb + n0 + blch[i] * 8;
-      } else if (BKIND == B_WGATE) {
-        src = r < a.Kvalid ? a.B0 + (uint32_t)r * (uint32_t)a.ldb + n0 + blch[i] * 8
-                           : a.zero + blch[i] * 8;
-      } else {
-        src = r < rows ? a.B0 + (uint32_t)(sbase + r) * (uint32_t)a.ldb + n0 + blch[i] * 8
-                       : a.zero + blch[i] * 8;
-      }
-      __builtin_amdgcn_global_load_lds((const void*)src,
+    for (int i = 0; i < DMA_B; ++i)
+      __builtin_amdgcn_global_load_lds((const void*)b_src(i, kt),
                                        (lds_ptr_t)(dst + (wave * DMA_B + i) * 512), 16, 0, 0);
-    }
   };
 
   // ---- fragment offsets
@@ -390,7 +414,8 @@ __global__ __launch_bounds__(WM * WN * 64) void bwd_gemm_kernel(BwdArgs a) {
 #pragma unroll
           for (int i = 0; i < NF; ++i) af[i] = *(const bf16x8*)&Ast[aoffs[ks] + i * WM * 32 * BK];
         }
-        tr_frags<BN, FN>(Bst, bbase, ks, bfv);
+        if constexpr (RS) tr_frags_bi<BN, FN>(Bst, bbase, ks, bfv);
+        else tr_frags<BN, FN>(Bst, bbase, ks, bfv);
 #pragma unroll
         for (int i = 0; i < NF; ++i)
 #pragma unroll
@@ -398,7 +423,42 @@ __global__ __launch_bounds__(WM * WN * 64) void bwd_gemm_kernel(BwdArgs a) {
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfv[j], acc[i][j], 0, 0, 0);
       }
     };
-    if constexpr (STAG && !DEEPA) {
+    if constexpr (RS) {
+      u32x4 ra[DMA_A], rb[DMA_B];
+      auto load_regs = [&](int kt) {
+#pragma unroll
+        for (int i = 0; i < DMA_A; ++i) {
+          if ((wave * DMA_A + i) * 8 >= rows_here) continue;   // wave-uniform
+          ra[i] = *(const u32x4*)(a.A + aoff[i] + kt * BK);
+        }
+#pragma unroll
+        for (int i = 0; i < DMA_B; ++i) rb[i] = *(const u32x4*)b_src(i, kt);
+      };
+      auto write_regs = [&](int slot) {
+#pragma unroll
+        for (int i = 0; i < DMA_A; ++i) {
+          if ((wave * DMA_A + i) * 8 >= rows_here) continue;
+          *(u32x4*)(As + slot * ASZ + (wave * DMA_A + i) * 512 + lane * 8) = ra[i];
+        }
+#pragma unroll
+        for (int i = 0; i < DMA_B; ++i)
+          *(u32x4*)(Bs + slot * BSZ + (wave * DMA_B + i) * 512 + lane * 8) = rb[i];
+      };
+      load_regs(0);
+      write_regs(0);
+      load_regs(KT > 1 ? 1 : 0);
+      __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's stores are in LDS
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      for (int kt = 0; kt < KT; ++kt) {
+        compute(As + (kt & 1) * ASZ, Bs + (kt & 1) * BSZ);
+        write_regs((kt + 1) & 1);            // step kt+1 (past the end: a copy nobody reads)
+        load_regs(kt + 2 < KT ? kt + 2 : KT - 1);
+        __builtin_amdgcn_s_waitcnt(0xC07F);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    } else if constexpr (STAG) {
       issue_a(0, 0);
       issue_b(0, 0);
       issue_b(KT > 1 ? 1 : 0, 1);
@@ -409,18 +469,6 @@ __global__ __launch_bounds__(WM * WN * 64) void bwd_gemm_kernel(BwdArgs a) {
         issue_a(kt + 1 < KT ? kt + 1 : KT - 1, (kt + 1) & 1);
         issue_b(kt + 2 < KT ? kt + 2 : KT - 1, (kt + 2) % 3);
         compute(As + (kt & 1) * ASZ, Bs + (kt % 3) * BSZ);
-      }
-    } else if constexpr (STAG) {          // rows deep, weights shallow
-      issue_b(0, 0);
-      issue_a(0, 0);
-      issue_a(KT > 1 ? 1 : 0, 1);
-      for (int kt = 0; kt < KT; ++kt) {
-        __builtin_amdgcn_s_waitcnt(wait_vm(DMA_A));
-        __builtin_amdgcn_s_barrier();
-        __builtin_amdgcn_sched_barrier(0);
-        issue_b(kt + 1 < KT ? kt + 1 : KT - 1, (kt + 1) & 1);
-        issue_a(kt + 2 < KT ? kt + 2 : KT - 1, (kt + 2) % 3);
-        compute(As + (kt % 3) * ASZ, Bs + (kt & 1) * BSZ);
       }
     } else {
 #pragma unroll
@@ -442,8 +490,7 @@ __global__ __launch_bounds__(WM * WN * 64) void bwd_gemm_kernel(BwdArgs a) {
   };
   if (KT > 0) {
     // wave-uniform count of this wave's row fragments that hold data (rows mode, staggered)
-    const int nf = STAG && !DEEPA ? min(FM, max(0, (rows_here - wm * 32 + WM * 32 - 1) / (WM * 32)))
-                                  : FM;
+    const int nf = SKIPA ? min(FM, max(0, (rows_here - wm * 32 + WM * 32 - 1) / (WM * 32))) : FM;
     if (nf >= FM) k_loop(std::integral_constant<int, FM>{});
     else if (nf == 2) k_loop(std::integral_constant<int, (FM > 2 ? 2 : 0)>{});
     else if (nf == 1) k_loop(std::integral_constant<int, (FM > 1 ? 1 : 0)>{});
@@ -475,12 +522,22 @@ __global__ __launch_bounds__(WM * WN * 64) void bwd_gemm_kernel(BwdArgs a) {
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
         const int col = n0 + wn * TN + j * 32 + fr;
+        const int fr0 = m_local * BM + (i * WM + wm) * 32;   // the fragment's first tile row
+        if (fr0 >= rows) continue;                           // all padding (wave-uniform)
+        // this lane's 16 values of u and v, in fragment order
+        f32x4 uq[4], vq[4];
+        const size_t o = uv_frag(sbase + fr0, col - fr, N, lane);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          uq[q] = *(const f32x4*)(a.U + o + 256 * q);
+          vq[q] = *(const f32x4*)(a.V + o + 256 * q);
+        }
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int lr = (i * WM + wm) * 32 + 8 * (r >> 2) + 4 * fkc + (r & 3);
           if (m_local * BM + lr < rows) {
             const size_t s = (size_t)(sbase + m_local * BM + lr);
-            const float u = a.U[s * N + col], v = a.V[s * N + col];
+            const float u = uq[r >> 2][r & 3], v = vq[r >> 2][r & 3];
             const float dh = acc[i][j][r];
             const float sig = __builtin_amdgcn_rcpf(1.0f + __expf(-u));
             const float sl = u * sig;                           // SiLU(u), as the forward
@@ -899,15 +956,16 @@ __global__ __launch_bounds__(256) void bwd_dx_kernel(const float* __restrict__ d
   }
 }
 
-// Row-tiled GEMMs (dgrads, router dgrad): 256 x BN tiles, 8 waves (4 x 2), staggered rings.
+// Row-tiled GEMMs (dgrads, router dgrad): 256 x BN tiles, 8 waves (4 x 2); the register-staged
+// ring when `staged`, else the staggered rings.
 template <int BN, int AK, int BKIND, int EPI>
-hipError_t launch_rows(const BwdArgs& a, int tiles, bool deep_rows, hipStream_t s) {
+hipError_t launch_rows(const BwdArgs& a, int tiles, bool staged, hipStream_t s) {
   if (tiles <= 0) return hipSuccess;
-  if (deep_rows)
-    hipLaunchKernelGGL((bwd_gemm_kernel<kRowsBM, BN, 4, 2, M_ROWS, AK, BKIND, EPI, 0, true>),
+  if (staged)
+    hipLaunchKernelGGL((bwd_gemm_kernel<kRowsBM, BN, 4, 2, M_ROWS, AK, BKIND, EPI, 2, true>),
                        dim3((tiles + 7) / 8 * 8), dim3(512), 0, s, a);
   else
-    hipLaunchKernelGGL((bwd_gemm_kernel<kRowsBM, BN, 4, 2, M_ROWS, AK, BKIND, EPI, 0, false>),
+    hipLaunchKernelGGL((bwd_gemm_kernel<kRowsBM, BN, 4, 2, M_ROWS, AK, BKIND, EPI, 0>),
                        dim3((tiles + 7) / 8 * 8), dim3(512), 0, s, a);
   return hipGetLastError();
 }
@@ -1094,8 +1152,9 @@ hipError_t launch_backward(const moe_problem& p, const BwdLayout& L, void* ws, c
   c.zero = zero;
   BwdArgs cr = c;                     // row-tiled GEMMs walk the row-tile schedule
   cr.sc = sr;
-  // rows in the deep ring when the weight tiles are shared in L2 by several m-tiles
-  const bool deep_rows = kDeepRowsFrom >= 0 && gemm_wide(p);
+  // register-staged ring when the weight tiles are shared in L2 by several m-tiles (the
+  // forward's wide class); the staggered rings otherwise
+  const bool staged = gemm_wide(p);
   // 3. dgrad-down + SwiGLU backward: d h' = dy_t W2, then du, dv, d g partials
   {
     BwdArgs a = cr;
@@ -1114,8 +1173,8 @@ hipError_t launch_backward(const moe_problem& p, const BwdLayout& L, void* ws, c
     a.dgate_part = dgate_part;
     a.NT = L.NT_down;
     const int tiles = L.max_mt_rows * L.NT_down;
-    err = (L.NT_down * 256 == p.d_ff) ? launch_rows<256, A_TOKEN, B_W2, EPI_DDOWN>(a, tiles, deep_rows, s)
-                                      : launch_rows<128, A_TOKEN, B_W2, EPI_DDOWN>(a, tiles, deep_rows, s);
+    err = (L.NT_down * 256 == p.d_ff) ? launch_rows<256, A_TOKEN, B_W2, EPI_DDOWN>(a, tiles, staged, s)
+                                      : launch_rows<128, A_TOKEN, B_W2, EPI_DDOWN>(a, tiles, staged, s);
     MOE_TRY(err);
   }
   MOE_TRY(mark());
@@ -1135,8 +1194,8 @@ hipError_t launch_backward(const moe_problem& p, const BwdLayout& L, void* ws, c
     a.out_shared = dx_shared;
     const int bn = bn_for(p.d);
     const int tiles = L.max_mt_rows * (p.d / bn);
-    err = (bn == 256) ? launch_rows<256, A_STORE, B_W13, EPI_ROWS>(a, tiles, deep_rows, s)
-                      : launch_rows<128, A_STORE, B_W13, EPI_ROWS>(a, tiles, deep_rows, s);
+    err = (bn == 256) ? launch_rows<256, A_STORE, B_W13, EPI_ROWS>(a, tiles, staged, s)
+                      : launch_rows<128, A_STORE, B_W13, EPI_ROWS>(a, tiles, staged, s);
     MOE_TRY(err);
   }
   MOE_TRY(mark());

@@ -76,7 +76,7 @@ struct GemmArgs {
   float* shared_out;    // down output, shared rows (token order)
   float* out_rows_b;    // down with K split in two: the second half's routed rows
   int ksplit;           // 1, or 2 for the down GEMM (routed groups only, no shared expert)
-  float* U;             // gate-up, or null: also store u and v (fp32, in H's row layout)
+  float* U;             // gate-up, or null: also store u and v (fp32 storage rows, fragment order)
   float* V;
 };
 
@@ -268,6 +268,11 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs args) 
 #pragma unroll
     for (int j = 0; j < FO; ++j) {
       const int col = tc.n0 + wn * (FEAT / WN) + j * 32 + fr;
+      if (GATEUP && args.U && tc.m_local * BM + wm * TM + i * 32 < tc.rows) {
+        const size_t o = uv_frag(tc.mt_global * BM + wm * TM + i * 32, col - fr, N, lane);
+        uv_store(args.U + o, acc[i][j]);
+        uv_store(args.V + o, acc[i][j + FN / 2]);
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int lr = wm * TM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
@@ -275,12 +280,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs args) 
           if (tc.m_local * BM + lr < tc.rows) {   // padding rows of H are never read
             const float u = acc[i][j][r];
             const float v = acc[i][j + FN / 2][r];
-            const size_t o = (size_t)(tc.mt_global * BM + lr) * N + col;
-            args.H[o] = f32_to_bf16(silu_f(u) * v);
-            if (args.U) {
-              args.U[o] = u;
-              args.V[o] = v;
-            }
+            args.H[(size_t)(tc.mt_global * BM + lr) * N + col] = f32_to_bf16(silu_f(u) * v);
           }
         } else {
           const int rg = tc.m_local * BM + lr;
@@ -499,6 +499,11 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_st_kernel(GemmArgs arg
 #pragma unroll
     for (int j = 0; j < FO; ++j) {
       const int col = tc.n0 + wn * (FEAT / WN) + j * 32 + fr;
+      if (GATEUP && args.U && (i * WM + wm) * 32 < rows_here) {
+        const size_t o = uv_frag(tc.mt_global * BM + (i * WM + wm) * 32, col - fr, N, lane);
+        uv_store(args.U + o, acc[i][j]);
+        uv_store(args.V + o, acc[i][j + FN / 2]);
+      }
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int lr = (i * WM + wm) * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
@@ -506,12 +511,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_st_kernel(GemmArgs arg
           if (lr < rows_here) {          // padding rows of H feed only padding rows of the down
             const float u = acc[i][j][r];
             const float v = acc[i][j + FN / 2][r];
-            const size_t o = (size_t)(tc.mt_global * BM + lr) * N + col;
-            args.H[o] = f32_to_bf16(silu_f(u) * v);
-            if (args.U) {
-              args.U[o] = u;
-              args.V[o] = v;
-            }
+            args.H[(size_t)(tc.mt_global * BM + lr) * N + col] = f32_to_bf16(silu_f(u) * v);
           }
         } else {
           const int rg = tc.m_local * BM + lr;
@@ -658,9 +658,10 @@ __global__ __launch_bounds__(256) void gemm_bf16_dec_kernel(GemmArgs args) {
         u += red[w][row * RS + col];
         v += red[w][row * RS + 32 + col];
       }
-      const size_t o = (size_t)(tc.mt_global * kDecBM + row) * N + tc.n0 + col;
-      args.H[o] = f32_to_bf16(silu_f(u) * v);
+      const int srow = tc.mt_global * kDecBM + row;
+      args.H[(size_t)srow * N + tc.n0 + col] = f32_to_bf16(silu_f(u) * v);
       if (args.U) {
+        const size_t o = uv_elem(srow, tc.n0 + col, N);
         args.U[o] = u;
         args.V[o] = v;
       }

@@ -20,6 +20,27 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf16_to_f32(bf16_t v) { return __uint_as_float((uint32_t)v << 16); }
 
+// u and v kept by the backward's gate-up recompute (fp32, storage rows x N columns, N a multiple
+// of 32) lie in MFMA fragment order: each 32 x 32 block of (storage row, column) is 1024
+// contiguous floats holding the 32x32 accumulator layout (lane c + 32h holds column c and rows
+// 8*(r/4) + 4h + r%4 at r = 0..15) as four quads, quad q = lanes' values r = 4q..4q+3, lane-major
+// inside the quad. A wave then writes or reads a fragment with four 16-byte accesses per lane,
+// each instruction covering 1 KB contiguous. Offset of lane `lane`'s first quad in the block at
+// (srow0, col0), both multiples of 32 (quad q at + 256 q):
+__device__ __forceinline__ size_t uv_frag(int srow0, int col0, int N, int lane) {
+  return ((size_t)(srow0 >> 5) * (size_t)(N >> 5) + (size_t)(col0 >> 5)) * 1024 + (size_t)lane * 4;
+}
+// offset of element (srow, col)
+__device__ __forceinline__ size_t uv_elem(int srow, int col, int N) {
+  const int rb = srow & 31, c = col & 31;
+  return uv_frag(srow & ~31, col & ~31, N, c + 32 * ((rb >> 2) & 1)) + 256 * (rb >> 3) + (rb & 3);
+}
+__device__ __forceinline__ void uv_store(float* dst, const f32x16& v) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    *(f32x4*)(dst + 256 * q) = f32x4{v[4 * q], v[4 * q + 1], v[4 * q + 2], v[4 * q + 3]};
+}
+
 // fp32 -> bf16, round to nearest even (NaN stays NaN).
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
   uint32_t u = __float_as_uint(f);
@@ -105,7 +126,7 @@ int down_ksplit(const moe_problem& p);
 // out_rows_b: [T*k, d] second-half partial rows, required when down_ksplit(p) == 2.
 // row_div: a routed row r gathers token sorted_assign[r] / row_div (0: k).
 // U, V (bf16 storage only): when given, only the gate-up GEMM runs, and it also stores u and v
-// in fp32 in H's row layout (the backward's recompute).
+// in fp32, in fragment order over H's storage rows (uv_frag; the backward's recompute).
 hipError_t launch_expert_ffn(const moe_problem& p, const void* x, const void* w1, const void* w3,
                              const void* w2, const void* ws1, const void* ws3, const void* ws2,
                              const int32_t* sorted_assign, const Schedule& sc, void* h,

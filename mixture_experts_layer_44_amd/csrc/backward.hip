@@ -25,8 +25,8 @@
 //   dgrad-down  [rows x d_ff] = dy_tok [rows x d] . W2_e [d x d_ff]   + SwiGLU backward epilogue
 //   dgrad-x     [rows x d]    = (du|dv) [rows x 2 d_ff] . (W1_e;W3_e) [2 d_ff x d]
 //   router      dx_r [T x d]  = d l [T x E] . W_gate [E x d]
-//     -- row-tiled (bwd_gemm_kernel): 256 x BN tiles, 8 waves of 64 x 128, staggered rings,
-//        ragged last tiles
+//     -- row-tiled (bwd_gemm_kernel): 256 x BN tiles, 8 waves of 64 x 128, staggered rings
+//        (the register-staged ring on the wide class), ragged last tiles
 //   wgrad-down  dW2_e [d x d_ff]     = (g dy)^T [d x rows] . h [rows x d_ff]
 //   wgrad-up    (dW1_e;dW3_e) [2 d_ff x d] = (du|dv)^T . x_gathered [rows x d]
 //     -- persistent (bwd_wgrad_kernel): 128 x 128 tiles streamed through a 2-slot ring
@@ -57,7 +57,7 @@ constexpr int BBM = 128;   // rows of a weight-gradient m-tile (rows of the weig
 // kernel (bwd_wgrad_kernel).
 constexpr int kWgradStages = 2;
 constexpr int kWgradBN = 128;
-constexpr int kRowsBM = 256;      // m-tile of the row-tiled GEMMs (ragged, staggered rings)
+constexpr int kRowsBM = 256;      // m-tile of the row-tiled GEMMs
 constexpr int ZERO_ELEMS = 256;
 
 enum AKind : int { A_TOKEN, A_STORE, A_IDENT, AT_STORE, AT_IDENT };

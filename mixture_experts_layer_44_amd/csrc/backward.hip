@@ -769,10 +769,11 @@ __global__ __launch_bounds__(512) void bwd_wgrad_kernel(BwdArgs a) {
     const int mm0 = second ? ct.m0 - a.Msplit : ct.m0;
     bf16_t* base = shared_grp ? (second ? a.SW1 : a.SW0)
                               : (second ? a.W1 : a.W0) + (size_t)ct.g * a.Msplit * a.N;
+    // non-temporal: the gradients are not read again here (DeepSeek-V3 shape: 22.6 GB of them)
     for (int idx = tid; idx < BM * BN / 8; idx += NW * 64) {
       const int row = idx / (BN / 8), ch = idx % (BN / 8);
-      *(u32x4*)(base + (size_t)(mm0 + row) * a.N + ct.n0 + ch * 8) =
-          *(const u32x4*)(outst + row * BN + ch * 8);
+      __builtin_nontemporal_store(*(const u32x4*)(outst + row * BN + ch * 8),
+                                  (u32x4*)(base + (size_t)(mm0 + row) * a.N + ct.n0 + ch * 8));
     }
     ckt = 0;
     cL += nwg;

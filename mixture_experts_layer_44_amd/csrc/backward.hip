@@ -787,6 +787,12 @@ __global__ __launch_bounds__(512) void bwd_wgrad_kernel(BwdArgs a) {
 // (group g, row r) -> assignment a = sorted_assign[off + r], token t = a / k, gate g_a:
 // DO[s] = bf16(g_a dy_t), XS[s] = x_t; shared rows: DO[s] = bf16(dy_r), XS[s] = x_r. Padding
 // rows are skipped. The first workgroup also clears the zero row.
+// four bf16 (round to nearest even) in one 8-byte word, element 0 lowest
+__device__ __forceinline__ uint2 pack_bf16x4(float a, float b, float c, float d) {
+  return uint2{(uint32_t)f32_to_bf16(a) | ((uint32_t)f32_to_bf16(b) << 16),
+               (uint32_t)f32_to_bf16(c) | ((uint32_t)f32_to_bf16(d) << 16)};
+}
+
 __global__ __launch_bounds__(256) void bwd_prep_kernel(const float* __restrict__ dy,
                                                        const bf16_t* __restrict__ x,
                                                        const int32_t* __restrict__ sorted_assign,
@@ -805,11 +811,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const float* __restrict__
       const f32x4* src = (const f32x4*)(dy + (size_t)item * d);
       for (int c = threadIdx.x; c < d4; c += 256) {
         const f32x4 v = src[c];
-        bf16_t* o = dyb + (size_t)item * d + 4 * c;
-        o[0] = f32_to_bf16(v[0]);
-        o[1] = f32_to_bf16(v[1]);
-        o[2] = f32_to_bf16(v[2]);
-        o[3] = f32_to_bf16(v[3]);
+        *(uint2*)(dyb + (size_t)item * d + 4 * c) = pack_bf16x4(v[0], v[1], v[2], v[3]);
       }
       continue;
     }
@@ -828,11 +830,8 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const float* __restrict__
     const uint2* xs = (const uint2*)(x + (size_t)t * d);
     for (int c = threadIdx.x; c < d4; c += 256) {
       const f32x4 v = src[c];
-      bf16_t* o = DO + (size_t)s * d + 4 * c;
-      o[0] = f32_to_bf16(gate * v[0]);
-      o[1] = f32_to_bf16(gate * v[1]);
-      o[2] = f32_to_bf16(gate * v[2]);
-      o[3] = f32_to_bf16(gate * v[3]);
+      *(uint2*)(DO + (size_t)s * d + 4 * c) =
+          pack_bf16x4(gate * v[0], gate * v[1], gate * v[2], gate * v[3]);
       ((uint2*)(XS + (size_t)s * d))[c] = xs[c];
     }
   }

@@ -30,7 +30,7 @@ namespace {
 constexpr int TM = 64;        // tokens per logits workgroup
 constexpr int EN = 64;        // experts per logits workgroup
 constexpr int UNROLL = 4;     // k-steps of loads in flight per wave
-constexpr int TOPK_TOK = 16;  // tokens per top-k workgroup (4 waves x 4)
+constexpr int TOPK_TOK = 4;   // tokens per top-k workgroup (one per wave)
 
 // partial logits of a 64-token x 64-expert block over the d slice blockIdx.z
 template <bool BF16>
@@ -255,8 +255,9 @@ size_t route_partial_bytes(const moe_problem& p) {
   return (size_t)route_ksplit(p) * p.T * E_pad * sizeof(float);
 }
 
-// small batches take one token per wave (4 per workgroup) so the top-k spreads over more CUs
-int route_topk_tokens(const moe_problem& p) { return small_routing(p) ? 4 : TOPK_TOK; }
+// One token per wave: each wave's logit loads then overlap other waves' top-k on the same CU (four
+// tokens per wave, one after the other, left one wave per SIMD waiting on its loads).
+int route_topk_tokens(const moe_problem&) { return TOPK_TOK; }
 int route_topk_blocks(const moe_problem& p) { return ceil_div(p.T, route_topk_tokens(p)); }
 
 hipError_t launch_route_topk(const moe_problem& p, const float* logits_part,
@@ -266,12 +267,8 @@ hipError_t launch_route_topk(const moe_problem& p, const float* logits_part,
   const int E_pad = ceil_div(p.E, 16) * 16;
   const int KS = route_ksplit(p);
   const int nblk = route_topk_blocks(p);
-  if (route_topk_tokens(p) == 4)
-    hipLaunchKernelGGL(route_topk_kernel<4>, dim3(nblk), dim3(256), 0, s, logits_part, KS, p.T,
-                       p.E, E_pad, p.k, logit_bias, sel_bias, ids, gates, psum_part);
-  else
-    hipLaunchKernelGGL(route_topk_kernel<TOPK_TOK>, dim3(nblk), dim3(256), 0, s, logits_part, KS,
-                       p.T, p.E, E_pad, p.k, logit_bias, sel_bias, ids, gates, psum_part);
+  hipLaunchKernelGGL(route_topk_kernel<TOPK_TOK>, dim3(nblk), dim3(256), 0, s, logits_part, KS, p.T,
+                     p.E, E_pad, p.k, logit_bias, sel_bias, ids, gates, psum_part);
   return hipGetLastError();
 }
 

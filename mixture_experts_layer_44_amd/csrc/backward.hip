@@ -845,7 +845,7 @@ __global__ __launch_bounds__(256) void bwd_prep_kernel(const float* __restrict__
 //        + p_e (w_e - sum_e' p_e' w_e'),  w_e = dL alpha E counts_pre[e] / (T k T)  (balance)
 // Writes d l in bf16 ([T, E_pad], zero past E) and per-workgroup column sums (fp32, tokens in
 // order within each wave, then the waves in order) for the logit offset's gradient.
-constexpr int RT_TOK = 4;
+constexpr int RT_TOK = 1;   // 4 in turn left one wave per SIMD waiting on its loads
 
 __global__ __launch_bounds__(256) void bwd_router_kernel(
     const float* __restrict__ part, int KS, int T, int E, int E16, int k,

@@ -36,6 +36,12 @@
  *   - Limits (else MOE_EUNSUPPORTED): 1 <= k <= E <= 256, k <= 32; T >= 0 and
  *     T*k < 2^31; n_shared in {0,1} with d_ff_shared == d_ff when 1; bf16:
  *     d and d_ff multiples of 128; fp32: d a multiple of 4.
+ *     Addressing: the kernels index each matrix with 32-bit element offsets, so
+ *     T*d, d*d_ff and (padded expert rows)*d_ff must each stay below 2^32. The
+ *     padded rows are T*k (or E*C for expert choice) plus at most one row tile
+ *     per expert and the shared expert's T rows; a Mixtral-shaped layer (d=4096,
+ *     d_ff=14336, k=2) accepts about 148k tokens per call. moe_backward also
+ *     needs (padded rows)*max(d, 2*d_ff) below 2^32.
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H

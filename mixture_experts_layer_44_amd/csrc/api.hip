@@ -97,6 +97,27 @@ int kernel_cap(const moe_problem& p) {
   return c >= (double)n ? (int)n : (int)c;
 }
 
+// The GEMM loaders address each matrix as a 64-bit base plus a 32-bit element offset
+// (row * row length + column), so every matrix they read must hold fewer than 2^32 elements:
+// x [T, d], each expert matrix [d_ff, d], and the padded row table h [m-tiles * BM, d_ff]
+// (for the expert-choice layout, its E*C bucket rows). With the backward, also its storage
+// rows times the widest row it addresses (2*d_ff for du|dv, d for the row copies).
+constexpr long long kAddr32 = 1ll << 32;
+
+bool forward_addr32_ok(const moe_problem& p, bool ec) {
+  if ((long long)p.T * p.d >= kAddr32 || (long long)p.d * p.d_ff >= kAddr32) return false;
+  const Layout L = layout(p, ec);
+  return (long long)L.max_mt * L.BM * p.d_ff < kAddr32;
+}
+
+bool backward_addr32_ok(const moe_problem& p) {
+  if (!forward_addr32_ok(p, false)) return false;
+  const BwdLayout L = backward_layout(p);
+  const long long rows = std::max((long long)L.max_mt * L.stor_bm, (long long)p.T);
+  const long long width = std::max({(long long)p.d, 2ll * p.d_ff, (long long)L.E_pad});
+  return rows * width < kAddr32;
+}
+
 moe_status check_ws(const moe_problem& p, const void* ws, size_t ws_bytes, bool ec = false) {
   const size_t need = layout(p, ec).total;
   if (ws_bytes < need) return MOE_EWORKSPACE;
@@ -132,9 +153,9 @@ MOE_API moe_status moe_validate(const moe_problem* p) {
   if (p->n_shared > 1) return MOE_EUNSUPPORTED;
   if (p->n_shared == 1 && p->d_ff_shared != p->d_ff) return MOE_EUNSUPPORTED;
   if ((long long)p->T * p->k >= (long long)INT_MAX - 4096) return MOE_EUNSUPPORTED;
-  if ((long long)p->T * p->d >= (1ll << 40)) return MOE_EUNSUPPORTED;
   if (p->dtype == MOE_BF16 && (p->d % 128 || p->d_ff % 128)) return MOE_EUNSUPPORTED;
   if (p->dtype == MOE_F32 && p->d % 4) return MOE_EUNSUPPORTED;
+  if (!forward_addr32_ok(*p, false)) return MOE_EUNSUPPORTED;
   return MOE_OK;
 }
 
@@ -171,6 +192,7 @@ MOE_API moe_status moe_expert_choice_workspace_bytes(const moe_problem* p, size_
   moe_status st = moe_validate(p);
   if (st != MOE_OK) return st;
   if (!bytes_out) return MOE_EINVAL;
+  if (!forward_addr32_ok(*p, true)) return MOE_EUNSUPPORTED;
   *bytes_out = layout(*p, true).total;
   return MOE_OK;
 }
@@ -187,6 +209,7 @@ MOE_API moe_status moe_forward_expert_choice(const moe_problem* p, const void* x
   const bool hasT = p->T > 0;
   if (!w_gate || !w1 || !w3 || !w2 || (hasT && (!x || !y))) return MOE_EINVAL;
   if (p->n_shared && (!ws1 || !ws3 || !ws2)) return MOE_EINVAL;
+  if (!forward_addr32_ok(*p, true)) return MOE_EUNSUPPORTED;
   if ((st = check_ws(*p, ws, ws_bytes, true)) != MOE_OK) return st;
   const Layout L = layout(*p, true);
   const int C = ec_capacity(*p);
@@ -300,7 +323,7 @@ MOE_API moe_status moe_backward_workspace_bytes(const moe_problem* p, size_t* by
   moe_status st = moe_validate(p);
   if (st != MOE_OK) return st;
   if (!bytes_out) return MOE_EINVAL;
-  if (p->dtype != MOE_BF16 || p->k > 16) return MOE_EUNSUPPORTED;
+  if (p->dtype != MOE_BF16 || p->k > 16 || !backward_addr32_ok(*p)) return MOE_EUNSUPPORTED;
   *bytes_out = backward_layout(*p).total;
   return MOE_OK;
 }
@@ -317,7 +340,7 @@ static moe_status backward_impl(const moe_problem* p, const void* x, const void*
                                 hipStream_t stream, hipEvent_t* ev) {
   moe_status st = moe_validate(p);
   if (st != MOE_OK) return st;
-  if (p->dtype != MOE_BF16 || p->k > 16) return MOE_EUNSUPPORTED;
+  if (p->dtype != MOE_BF16 || p->k > 16 || !backward_addr32_ok(*p)) return MOE_EUNSUPPORTED;
   const bool hasT = p->T > 0;
   if (!w_gate || !w1 || !w3 || !w2 || !counts_pre || !offsets || !dw_gate || !dw1 || !dw3 || !dw2)
     return MOE_EINVAL;

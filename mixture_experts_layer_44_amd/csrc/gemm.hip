@@ -345,8 +345,8 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_st_kernel(GemmArgs arg
   // A load i of this wave fills slot rows q*RPI.. (q = wave*DMA_A + i): lane l writes physical
   // 16-byte chunk l%CHUNKS of row q*RPI + l/CHUNKS and so fetches the logical chunk that the
   // swizzle puts there (the swizzle is an involution).
-  // (32-bit element offsets from the matrix base keep the register count down: every offset
-  // is below 2^31 for the sizes the entry points accept)
+  // (32-bit element offsets from the matrix base keep the register count down; the entry
+  // points reject every shape whose x, expert matrices or padded h rows reach 2^32 elements)
   uint32_t aoff[DMA_A];
 #pragma unroll
   for (int i = 0; i < DMA_A; ++i) {

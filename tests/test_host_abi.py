@@ -201,3 +201,33 @@ def test_backward_validation_returns_before_any_launch(moe):
     assert 0 < a < b
     with pytest.raises(moe.MoEError):
         moe.backward_workspace_bytes(moe.make_problem(16, 256, 8, 2, 256, dtype="f32"))
+
+
+def _padded_rows(T, E, k, bm):
+    """Rows of the padded row table: ceil(T*k / bm) tiles plus one spare tile per expert."""
+    return (-(-T * k // bm) + E) * bm
+
+
+@pytest.mark.parametrize("T,status", [(140000, 0), (148000, 0), (150000, 2)])
+def test_padded_rows_times_dff_must_fit_32bit_offsets(moe, T, status):
+    # Mixtral-shaped layer: the down GEMM addresses h [padded rows, d_ff] with 32-bit element
+    # offsets, so shapes whose table reaches 2^32 elements are refused before any launch
+    rows = _padded_rows(T, 8, 2, 256)
+    assert (rows * 14336 >= 2 ** 32) == (status != 0)
+    assert moe.validate(moe.make_problem(T, 4096, 8, 2, 14336)) == status
+
+
+@pytest.mark.parametrize("T,status", [(2 ** 19 - 1, 0), (2 ** 19, 2)])
+def test_x_elements_must_fit_32bit_offsets(moe, T, status):
+    # x [T, d] with d = 8192: T*d reaches 2^32 at T = 2^19
+    assert moe.validate(moe.make_problem(T, 8192, 256, 1, 128)) == status
+
+
+@pytest.mark.parametrize("T,status", [(70000, 0), (75000, 2)])
+def test_backward_rows_times_width_must_fit_32bit_offsets(moe, T, status):
+    # the backward also addresses du|dv [padded rows, 2*d_ff]
+    n = ctypes.c_size_t(0)
+    p = moe.make_problem(T, 4096, 8, 2, 14336)
+    assert moe.validate(p) == 0
+    assert moe.lib().moe_backward_workspace_bytes(ctypes.byref(p), ctypes.byref(n)) == status
+    assert (_padded_rows(T, 8, 2, 256) * 2 * 14336 >= 2 ** 32) == (status != 0)

@@ -9,7 +9,7 @@ already resident in HBM. W untimed warm-up steps, then exactly K steps
 between two device synchronisations. A second pass of K steps records HIP
 events on the launch stream between the stages, for the per-stage times and
 the dominant kernel's average launch duration (its roofline). A third, cold
-pass writes a 1 GiB buffer before each step, outside its events, so no step
+pass reads a 1 GiB buffer before each step, outside its events, so no step
 finds the last one's data in L2 or the Infinity Cache ("cold": medians). Prints ONE
 JSON line on stdout: tokens/s of the whole job, that roofline, and the fp64
 CPU oracle timed on a bounded sample of the same workload (1 core).
@@ -190,6 +190,19 @@ def calibration_copy(mib: int, dev, reps: int = 3):
 
 
 # ----------------------------------------------------------------------------- CPU baseline
+def cpu_model() -> str:
+    """The host CPU's model name as the kernel reports it (first processor), or 'unknown'."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.lower().startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
 def cpu_baseline(w, inp, sample_tokens: int):
     """The fp64 oracle, as it stands, on the first `sample_tokens` tokens of the
     workload (all of its experts' weights), on one host core."""
@@ -222,6 +235,7 @@ def cpu_baseline(w, inp, sample_tokens: int):
         torch.set_num_threads(torch_threads)
     assert np.isfinite(y).all()
     return {"value": S / dt, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+            "cpu_model": cpu_model(),
             "sample": f"first {S} of {w.T} tokens of {w.name}, every expert's full weights "
                       f"(fp64 up-cast included), route+align+experts+combine+balance; {dt:.1f} s",
             "seconds": dt}
@@ -423,6 +437,9 @@ def main(argv=None):
     ap.add_argument("--scrub", choices=("read", "write"), default="read",
                     help="how the cold pass evicts the caches before each step")
     ap.add_argument("--traffic-command", default="", help="command recorded with --write-traffic")
+    ap.add_argument("--configs", default="all",
+                    help="after the headline workload, also time these workloads (comma-separated "
+                         "names, 'all', or '' for none) and report them under `configs`")
     args = ap.parse_args(argv)
 
     if args.write_traffic:
@@ -466,6 +483,97 @@ def main(argv=None):
             return 2
         return bench_backward(args, w, p, g, kw, y, torch, moe)
 
+    del ws, y, kw
+    res = measure_forward(w, args, inp, dev, torch, moe)
+    torch.cuda.empty_cache()
+
+    configs = {}
+    if args.configs and not args.tokens:
+        names = (ALL_CONFIGS if args.configs == "all" else
+                 [n.strip() for n in args.configs.split(",") if n.strip()])
+        for name in names:
+            if name == w.name:
+                continue
+            wc = workloads.get(name)
+            log(f"[bench] --- config {wc}")
+            t0 = time.time()
+            inp_c = workloads.generate(wc, device=dev)
+            torch.cuda.synchronize()
+            log(f"[bench] inputs generated in {time.time() - t0:.1f} s")
+            rc = measure_forward(wc, args, inp_c, dev, torch, moe)
+            configs[wc.name] = config_entry(wc, rc)
+            del inp_c, rc
+            torch.cuda.empty_cache()
+        configs[w.name] = config_entry(w, res)
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        log(f"[bench] CPU oracle baseline on {args.cpu_sample} tokens ...")
+        cpu = cpu_baseline(w, inp, args.cpu_sample)
+        log(f"[bench] CPU oracle: {cpu['value']:.2f} tokens/s ({cpu['seconds']:.1f} s)")
+        cpu.pop("seconds")
+
+    bf16 = w.dtype == "bf16"
+    cfg = {"workload": w.name, "T": w.T, "d": w.d, "E": w.E, "k": w.k, "d_ff": w.d_ff,
+           "n_shared": w.n_shared, "capacity_factor": w.capacity_factor, "seed": w.seed,
+           "balance_stats": w.balance_alpha > 0}
+    line = {"metric": METRIC, "value": res["tokens_per_s"], "unit": "tokens/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": res["ms_per_step"],
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+            "dtype": "bf16" if bf16 else "f32", "data": "synthetic", "config": cfg,
+            "roofline": res["roofline"], "cpu_baseline": cpu, "layer": res["layer"],
+            "cold": res["cold"], "launch": "hip_graph" if args.graph else "eager"}
+    if configs:
+        line["configs"] = configs
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+# every config of the layer, timed in one default run (the headline is the first)
+ALL_CONFIGS = ("mixtral_prefill", "dsv3_fine", "skew_cap", "decode_T1", "decode_T8", "decode_T32",
+               "decode_T128", "tiny_fp32")
+
+
+def config_entry(w, r):
+    """The per-workload record of the `configs` object: warm and cold step times, tokens/s, the
+    layer's binding roofline (the larger of its MFMA and HBM times at peak) and its fraction, and
+    the dominant kernel with its average launch duration."""
+    lay = r["layer"]
+    bf16 = w.dtype == "bf16"
+    if not bf16:
+        bound, frac = "launch", None         # the fp32 layer is a parity case; no roofline claim
+    elif lay["flops"] / (PEAK_BF16_TFLOPS * 1e12) >= lay["bytes"] / (PEAK_HBM_GBS * 1e9):
+        bound, frac = "mfma", lay["mfma_frac"]
+    else:
+        bound, frac = "hbm", lay["hbm_frac"]
+    roof = r["roofline"]
+    cold_ms = r["cold"]["ms_per_step_median"]
+    return {"T": w.T, "d": w.d, "E": w.E, "k": w.k, "d_ff": w.d_ff, "n_shared": w.n_shared,
+            "capacity_factor": w.capacity_factor, "dtype": w.dtype, "seed": w.seed,
+            "ms_per_step": round(r["ms_per_step"], 5), "tokens_per_s": r["tokens_per_s"],
+            "cold_ms_per_step_median": round(cold_ms, 5),
+            "cold_ms_per_step_min": round(r["cold"]["ms_per_step_min"], 5),
+            "cold_tokens_per_s": w.T / (cold_ms * 1e-3) if cold_ms > 0 else None,
+            "layer_bound": bound, "layer_frac": frac,
+            "layer_mfma_frac": lay["mfma_frac"], "layer_hbm_frac": lay["hbm_frac"],
+            "layer_flops": lay["flops"], "layer_bytes": lay["bytes"],
+            "kept_rows": lay["kept_rows"], "touched_experts": lay["touched_experts"],
+            "stage_ms": lay["stage_ms"], "cold_stage_ms": r["cold"]["stage_ms_median"],
+            "dominant": {"stage": r["dominant"], "avg_launch_ms": round(roof["avg_launch_ms"], 5),
+                         "bound": roof["bound"], "achieved": roof["achieved"],
+                         "unit": roof["unit"], "frac": roof["frac"],
+                         "cold_frac": r["cold"]["dominant_frac"]}}
+
+
+def measure_forward(w, args, g, dev, torch, moe):
+    """Warm-up, then exactly K moe_forward steps between two device synchronisations (the
+    throughput), a staged pass of K steps (per-stage event times, the dominant kernel's average
+    launch duration) and a cold pass of K staged steps with the caches scrubbed before each."""
+    p = moe.problem_for(w)
+    ws = torch.empty(moe.workspace_bytes(p), dtype=torch.uint8, device=dev)
+    y = torch.empty((w.T, w.d), dtype=torch.float32, device=dev)
+    kw = dict(logit_bias=g["logit_bias"], sel_bias=g["sel_bias"], ws1=g["ws1"], ws3=g["ws3"],
+              ws2=g["ws2"], ws=ws)
     # routing of this batch (for the algorithmic work); identical in every step
     _, r = moe.forward(p, g["x"], g["w_gate"], g["w1"], g["w3"], g["w2"], return_routing=True, y=y,
                        **kw)
@@ -498,7 +606,7 @@ def main(argv=None):
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    log(f"[bench] warm-up done ({args.warmup} steps)")
+    log(f"[bench] {w.name}: warm-up done ({args.warmup} steps)")
 
     # the timed region: exactly K plain forward calls between two device synchronisations
     torch.cuda.synchronize()
@@ -522,13 +630,14 @@ def main(argv=None):
     for i, name in enumerate(moe.STAGES):
         vals = [events[s][i].elapsed_time(events[s][i + 1]) for s in range(args.steps)]
         stage_ms[name] = sum(vals) / len(vals)
-    log("[bench] stage ms: " + ", ".join(f"{k}={v:.4f}" for k, v in stage_ms.items()))
-    log(f"[bench] {ms_per_step:.4f} ms/step, {tokens_per_s:,.0f} tokens/s "
+    log(f"[bench] {w.name} stage ms: " + ", ".join(f"{k}={v:.4f}" for k, v in stage_ms.items()))
+    log(f"[bench] {w.name}: {ms_per_step:.4f} ms/step, {tokens_per_s:,.0f} tokens/s "
         f"(stage-event pass: {sum(stage_ms.values()):.4f} ms/step)")
 
-    # cold pass: before each step, outside its events, write a 1 GiB buffer (more than the 256 MB
-    # Infinity Cache plus the 8 x 4 MB of L2), so no step finds the previous step's weights or
-    # rows in a cache. Per-step and per-stage medians (the events add a few microseconds each).
+    # cold pass: before each step, outside its events, read a 1 GiB buffer (more than the 256 MB
+    # Infinity Cache plus the 8 x 4 MB of L2; --scrub write fills it instead), so no step finds the
+    # previous step's weights or rows in a cache. Per-step and per-stage medians (the events add a
+    # few microseconds each).
     scrub = torch.ones(1 << 28, dtype=torch.int32, device=dev)
     torch.cuda.synchronize()
     for s_ in range(args.steps):
@@ -543,7 +652,7 @@ def main(argv=None):
                                           for s in range(args.steps))
                   for i, name in enumerate(moe.STAGES)}
     cold_steps = [events[s][0].elapsed_time(events[s][len(moe.STAGES)]) for s in range(args.steps)]
-    log("[bench] cold stage ms (median): " + ", ".join(f"{k}={v:.4f}" for k, v in cold_stage.items()))
+    log(f"[bench] {w.name} cold stage ms (median): " + ", ".join(f"{k}={v:.4f}" for k, v in cold_stage.items()))
     log(f"[bench] cold step (caches scrubbed): median {statistics.median(cold_steps):.4f} ms, "
         f"min {min(cold_steps):.4f} ms")
 
@@ -586,24 +695,8 @@ def main(argv=None):
              "hbm_frac": lw["bytes"] / t_layer / (PEAK_HBM_GBS * 1e9),
              "stage_ms": {k: round(v, 5) for k, v in stage_ms.items()}}
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        log(f"[bench] CPU oracle baseline on {args.cpu_sample} tokens ...")
-        cpu = cpu_baseline(w, inp, args.cpu_sample)
-        log(f"[bench] CPU oracle: {cpu['value']:.2f} tokens/s ({cpu['seconds']:.1f} s)")
-        cpu.pop("seconds")
-
-    cfg = {"workload": w.name, "T": w.T, "d": w.d, "E": w.E, "k": w.k, "d_ff": w.d_ff,
-           "n_shared": w.n_shared, "capacity_factor": w.capacity_factor, "seed": w.seed,
-           "balance_stats": bal is not None}
-    line = {"metric": METRIC, "value": tokens_per_s, "unit": "tokens/s", "n_gpus": 1,
-            "steps": args.steps, "warmup": args.warmup, "ms_per_step": ms_per_step,
-            "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-            "dtype": "bf16" if bf16 else "f32", "data": "synthetic", "config": cfg,
-            "roofline": roof, "cpu_baseline": cpu, "layer": layer, "cold": cold,
-            "launch": "hip_graph" if args.graph else "eager"}
-    print(json.dumps(line), flush=True)
-    return 0
+    return {"ms_per_step": ms_per_step, "tokens_per_s": tokens_per_s, "roofline": roof,
+            "cold": cold, "layer": layer, "dominant": dom}
 
 
 if __name__ == "__main__":

@@ -1,8 +1,9 @@
 """HIP path vs the fp64 oracle, through the C ABI (needs an MI355X).
 
-Small problems are compared on every output row; the full-size workloads on
-every routing output (ids by the gap rule, grouping bit-exact) and on sampled
-rows of y, in the same launch configuration the benchmark times."""
+Every case, the full-size workloads included, is compared on every routing
+output (ids by the gap rule, grouping bit-exact, gates) and on every row of
+y; the full-size workloads run in the same launch configuration the
+benchmark times."""
 import dataclasses
 import sys
 
@@ -91,18 +92,20 @@ def test_decode_parity(w):
     assert rep.ok(w.dtype), str(rep)
 
 
-FULL = [("mixtral_prefill", 48), ("skew_cap", 48), ("dsv3_fine", 12)]
+FULL = ["mixtral_prefill", "skew_cap", "dsv3_fine"]
 
 
 @pytest.mark.slow
 @pytest.mark.timeout(900)
-@pytest.mark.parametrize("name,sample", FULL, ids=[f[0] for f in FULL])
-def test_full_size_parity(name, sample):
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_parity(name):
+    # every output row of the full-size layer, in the launch configuration the benchmark times;
+    # the oracle visits each expert once for all of its rows (host BLAS threads)
     w = workloads.get(name)
-    _say(f"[parity] full {w} sample={sample}")
-    rep = run_parity(w, gen_device="cuda", sample=sample)
+    _say(f"[parity] full {w}, every row")
+    rep = run_parity(w, gen_device="cuda", sample=None)
     _say(str(rep) + f" timings={ {k: round(v, 1) for k, v in rep.timings.items()} }")
-    assert rep.rows_checked >= sample
+    assert rep.rows_checked == w.T
     assert rep.ok(w.dtype), str(rep)
     if w.capacity_factor:
         assert rep.dropped > 0

@@ -212,6 +212,27 @@ moe_status moe_forward(const moe_problem* p, const void* x, const void* w_gate,
                        int32_t* sorted_assign, int32_t* assign_pos,
                        void* ws, size_t ws_bytes, hipStream_t stream);
 
+/* moe_forward without a workspace argument, for callers that cannot allocate device memory
+   (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc). It
+   allocates nothing: its scratch is one library-owned array of MOE_NOALLOC_SCRATCH_BYTES per
+   GPU, held from the first call on that GPU until the process ends. Same arguments, outputs
+   and errors as moe_forward, plus MOE_EWORKSPACE when the problem's moe_workspace_bytes()
+   exceeds MOE_NOALLOC_SCRATCH_BYTES (for example a decode-sized layer with d = 2048, E = 128,
+   k = 8, d_ff = 768 fits up to T = 256). Runs on the current device, which must be the
+   stream's. Every call on one GPU shares that GPU's array: calls that overlap in time on one
+   GPU (different streams, or threads) race and give wrong results; calls ordered on one stream
+   are safe. Nothing in the array needs to start at any value. */
+#define MOE_NOALLOC_SCRATCH_BYTES (32u << 20)
+moe_status moe_forward_noalloc(const moe_problem* p, const void* x, const void* w_gate,
+                               const float* logit_bias, const float* sel_bias,
+                               const void* w1, const void* w3, const void* w2,
+                               const void* ws1, const void* ws3, const void* ws2,
+                               float* y,
+                               int32_t* topk_ids, float* topk_w, float* prob_sum,
+                               int32_t* counts_pre, int32_t* counts, int32_t* offsets,
+                               int32_t* sorted_assign, int32_t* assign_pos,
+                               hipStream_t stream);
+
 /* Per-stage timing of moe_forward, for measurement tools. Same computation and
    kernels as moe_forward (routing outputs stay in ws), and additionally records
    caller-created HIP events on `stream`: stage_events[0] before the router,

@@ -24,8 +24,11 @@ __all__ = [
     "MOE_OK", "MOE_EINVAL", "MOE_EUNSUPPORTED", "MOE_EWORKSPACE", "MOE_EHIP", "forward_staged",
     "STAGES", "problem_for", "PreparedForward", "bias_update", "expert_choice_capacity",
     "expert_choice_workspace_bytes", "forward_expert_choice", "backward",
-    "backward_workspace_bytes", "BWD_STAGES",
+    "backward_workspace_bytes", "BWD_STAGES", "forward_noalloc", "NOALLOC_SCRATCH_BYTES",
 ]
+
+# size of the per-GPU scratch array of moe_forward_noalloc (MOE_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 32 << 20
 
 # stage names of moe_backward_staged, in event order (events 1..10 close these stages)
 BWD_STAGES = ("recompute", "prep", "dgrad_down", "dgrad_x", "wgrad_down", "wgrad_up", "router",
@@ -80,6 +83,8 @@ def _load() -> ctypes.CDLL:
     L.moe_forward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
                               vp, vp, vp, vp, sz, vp]
     L.moe_forward_staged.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp, vp]
+    L.moe_forward_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                      vp, vp, vp, vp, vp]
     L.moe_backward_workspace_bytes.argtypes = [P, ctypes.POINTER(sz)]
     L.moe_backward.argtypes = [P] + [vp] * 16 + [f32, f32] + [vp] * 10 + [sz, vp]
     L.moe_backward_staged.argtypes = [P] + [vp] * 16 + [f32, f32] + [vp] * 10 + [sz, vp, vp]
@@ -87,7 +92,7 @@ def _load() -> ctypes.CDLL:
                "moe_expert_ffn", "moe_combine", "moe_balance", "moe_forward", "moe_forward_staged",
                "moe_bias_update", "moe_expert_choice_capacity", "moe_expert_choice_workspace_bytes",
                "moe_forward_expert_choice", "moe_backward_workspace_bytes", "moe_backward",
-               "moe_backward_staged"):
+               "moe_backward_staged", "moe_forward_noalloc"):
         getattr(L, fn).restype = ctypes.c_int
     return L
 
@@ -306,6 +311,44 @@ def forward(p: Problem, x, w_gate, w1, w3, w2, logit_bias=None, sel_bias=None, w
     r["sorted_assign"] = r["sorted_assign"][:n]
     r["assign_pos"] = r["assign_pos"][:n]
     return y, r
+
+
+def forward_noalloc(p: Problem, x, w_gate, w1, w3, w2, y, routing=None, logit_bias=None,
+                    sel_bias=None, ws1=None, ws3=None, ws2=None):
+    """moe_forward_noalloc: the whole layer without a workspace (the library's per-GPU scratch
+    array), for callers that cannot allocate. y [T,d] fp32 and every tensor in `routing`
+    (topk_ids, topk_w, prob_sum, counts_pre, counts, offsets, sorted_assign, assign_pos; any
+    subset) are preallocated by the caller; this function allocates nothing. Returns y."""
+    dev, dt = x.device, _dt(p)
+    _need(x, "x", (p.T, p.d), dt, dev)
+    _need(w_gate, "w_gate", (p.E, p.d), dt, dev)
+    _need(w1, "w1", (p.E, p.d_ff, p.d), dt, dev)
+    _need(w3, "w3", (p.E, p.d_ff, p.d), dt, dev)
+    _need(w2, "w2", (p.E, p.d, p.d_ff), dt, dev)
+    _need(logit_bias, "logit_bias", (p.E,), torch.float32, dev, optional=True)
+    _need(sel_bias, "sel_bias", (p.E,), torch.float32, dev, optional=True)
+    _need(y, "y", (p.T, p.d), torch.float32, dev)
+    if p.n_shared:
+        _need(ws1, "ws1", (1, p.d_ff_shared, p.d), dt, dev)
+        _need(ws3, "ws3", (1, p.d_ff_shared, p.d), dt, dev)
+        _need(ws2, "ws2", (1, p.d, p.d_ff_shared), dt, dev)
+    r = dict(routing or {})
+    n = p.T * p.k
+    shapes = dict(topk_ids=(n, torch.int32), topk_w=(n, torch.float32),
+                  prob_sum=(p.E, torch.float32), counts_pre=(p.E, torch.int32),
+                  counts=(p.E, torch.int32), offsets=(p.E + 1, torch.int32),
+                  sorted_assign=(n, torch.int32), assign_pos=(n, torch.int32))
+    for key, t in r.items():
+        size, dtype = shapes[key]
+        if t.device != dev or t.dtype != dtype or not t.is_contiguous() or t.numel() < size:
+            raise ValueError(f"{key} must be a contiguous {dtype} tensor of >= {size} entries on {dev}")
+    g = r.get
+    _check("moe_forward_noalloc", _lib.moe_forward_noalloc(
+        ctypes.byref(p), _ptr(x), _ptr(w_gate), _ptr(logit_bias), _ptr(sel_bias), _ptr(w1),
+        _ptr(w3), _ptr(w2), _ptr(ws1), _ptr(ws3), _ptr(ws2), _ptr(y), _ptr(g("topk_ids")),
+        _ptr(g("topk_w")), _ptr(g("prob_sum")), _ptr(g("counts_pre")), _ptr(g("counts")),
+        _ptr(g("offsets")), _ptr(g("sorted_assign")), _ptr(g("assign_pos")), _stream(dev)))
+    return y
 
 
 def bias_update(p: Problem, counts_pre, sel_bias, gamma: float):

@@ -2,12 +2,19 @@
 // launch sequence route -> align -> schedule -> gate-up GEMM -> down GEMM -> combine.
 // Validation never touches the GPU, so invalid calls return before anything is enqueued.
 #include <algorithm>
+#include <atomic>
 #include <climits>
 #include <cmath>
+#include <mutex>
 
 #include "moe_internal.h"
 
 #define MOE_API extern "C" __attribute__((visibility("default")))
+
+// Workspace of moe_forward_noalloc: one copy per GPU, held until the process ends. Host code
+// never passes this name to a kernel (on the host it is only a stand-in for the symbol); it uses
+// the device address that hipGetSymbolAddress returns for the current device.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
 
 namespace moe {
 namespace {
@@ -248,6 +255,10 @@ MOE_API moe_status moe_route(const moe_problem* p, const void* x, const void* w_
   if (!w_gate || (hasT && (!x || !topk_ids || !topk_w))) return MOE_EINVAL;
   if ((st = check_ws(*p, ws, ws_bytes)) != MOE_OK) return st;
   const Layout L = layout(*p);
+  if (small_route_fused(*p))   // the same kernel (and bits) as moe_forward at these sizes
+    return hip_status(launch_route_small(*p, -1, x, w_gate, logit_bias, sel_bias, topk_ids,
+                                         topk_w, prob_sum, false, nullptr, nullptr, nullptr,
+                                         nullptr, nullptr, schedule_in(*p, L, ws), stream));
   return hip_status(launch_route(*p, x, w_gate, logit_bias, sel_bias, topk_ids, topk_w, prob_sum,
                                  at<float>(ws, L.logits_part), at<float>(ws, L.psum_part), stream));
 }
@@ -419,8 +430,14 @@ moe_status forward_impl(const moe_problem* p, const void* x, const void* w_gate,
   if (mark(0) != hipSuccess) return MOE_EHIP;
   const Schedule sc = schedule_in(*p, L, ws);
   hipError_t e;
-  if (small_routing(*p)) {
-    // decode-sized: logits, then top-k + grouping + schedule in one launch
+  if (small_route_fused(*p)) {
+    // decode-sized bf16: the whole router, grouping and schedule in one launch
+    e = launch_route_small(*p, kernel_cap(*p), x, w_gate, logit_bias, sel_bias, ids, gates,
+                           prob_sum, true, cpre, cnt, offs, sa, ap, sc, stream);
+    if (e != hipSuccess || mark(1) != hipSuccess || mark(2) != hipSuccess || mark(3) != hipSuccess)
+      return MOE_EHIP;
+  } else if (small_routing(*p)) {
+    // small fp32 batches: logits, then top-k + grouping + schedule in one launch
     e = launch_route_logits(*p, x, w_gate, at<float>(ws, L.logits_part), stream);
     if (e != hipSuccess || mark(1) != hipSuccess) return MOE_EHIP;
     e = launch_route_align_small(*p, kernel_cap(*p), at<float>(ws, L.logits_part), logit_bias,
@@ -457,6 +474,51 @@ MOE_API moe_status moe_forward(const moe_problem* p, const void* x, const void* 
   return forward_impl(p, x, w_gate, logit_bias, sel_bias, w1, w3, w2, ws1, ws3, ws2, y, topk_ids,
                       topk_w, prob_sum, counts_pre, counts, offsets, sorted_assign, assign_pos, ws,
                       ws_bytes, stream, nullptr);
+}
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// Device address of `scratch` on the current device, looked up once per device (with that device
+// current, as the lookup requires) and kept for the rest of the process.
+moe_status scratch_ptr(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return MOE_EHIP;
+  if (dev < 0 || dev >= kMaxDevices) return MOE_EUNSUPPORTED;
+  void* ptr = g_scratch[dev].load(std::memory_order_acquire);
+  if (!ptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    ptr = g_scratch[dev].load(std::memory_order_relaxed);
+    if (!ptr) {
+      if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return MOE_EHIP;
+      g_scratch[dev].store(ptr, std::memory_order_release);
+    }
+  }
+  *out = ptr;
+  return MOE_OK;
+}
+
+}  // namespace
+
+MOE_API moe_status moe_forward_noalloc(const moe_problem* p, const void* x, const void* w_gate,
+                                       const float* logit_bias, const float* sel_bias,
+                                       const void* w1, const void* w3, const void* w2,
+                                       const void* ws1, const void* ws3, const void* ws2, float* y,
+                                       int32_t* topk_ids, float* topk_w, float* prob_sum,
+                                       int32_t* counts_pre, int32_t* counts, int32_t* offsets,
+                                       int32_t* sorted_assign, int32_t* assign_pos,
+                                       hipStream_t stream) {
+  moe_status st = moe_validate(p);
+  if (st != MOE_OK) return st;
+  if (layout(*p).total > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_EWORKSPACE;
+  void* ws = nullptr;
+  if ((st = scratch_ptr(&ws)) != MOE_OK) return st;
+  return forward_impl(p, x, w_gate, logit_bias, sel_bias, w1, w3, w2, ws1, ws3, ws2, y, topk_ids,
+                      topk_w, prob_sum, counts_pre, counts, offsets, sorted_assign, assign_pos, ws,
+                      (size_t)MOE_NOALLOC_SCRATCH_BYTES, stream, nullptr);
 }
 
 MOE_API moe_status moe_forward_staged(const moe_problem* p, const void* x, const void* w_gate,

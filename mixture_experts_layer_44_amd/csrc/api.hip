@@ -255,10 +255,14 @@ MOE_API moe_status moe_route(const moe_problem* p, const void* x, const void* w_
   if (!w_gate || (hasT && (!x || !topk_ids || !topk_w))) return MOE_EINVAL;
   if ((st = check_ws(*p, ws, ws_bytes)) != MOE_OK) return st;
   const Layout L = layout(*p);
-  if (small_route_fused(*p))   // the same kernel (and bits) as moe_forward at these sizes
-    return hip_status(launch_route_small(*p, -1, x, w_gate, logit_bias, sel_bias, topk_ids,
-                                         topk_w, prob_sum, false, nullptr, nullptr, nullptr,
-                                         nullptr, nullptr, schedule_in(*p, L, ws), stream));
+  if (small_topk_fused(*p)) {   // the same kernels (and bits) as moe_forward at these sizes
+    hipError_t e = launch_route_logits(*p, x, w_gate, at<float>(ws, L.logits_part), stream);
+    if (e == hipSuccess)
+      e = launch_topk_align_small(*p, -1, at<float>(ws, L.logits_part), logit_bias, sel_bias,
+                                  topk_ids, topk_w, prob_sum, false, nullptr, nullptr, nullptr,
+                                  nullptr, nullptr, schedule_in(*p, L, ws), stream);
+    return hip_status(e);
+  }
   return hip_status(launch_route(*p, x, w_gate, logit_bias, sel_bias, topk_ids, topk_w, prob_sum,
                                  at<float>(ws, L.logits_part), at<float>(ws, L.psum_part), stream));
 }
@@ -430,14 +434,16 @@ moe_status forward_impl(const moe_problem* p, const void* x, const void* w_gate,
   if (mark(0) != hipSuccess) return MOE_EHIP;
   const Schedule sc = schedule_in(*p, L, ws);
   hipError_t e;
-  if (small_route_fused(*p)) {
-    // decode-sized bf16: the whole router, grouping and schedule in one launch
-    e = launch_route_small(*p, kernel_cap(*p), x, w_gate, logit_bias, sel_bias, ids, gates,
-                           prob_sum, true, cpre, cnt, offs, sa, ap, sc, stream);
-    if (e != hipSuccess || mark(1) != hipSuccess || mark(2) != hipSuccess || mark(3) != hipSuccess)
-      return MOE_EHIP;
+  if (small_topk_fused(*p)) {
+    // decode-sized: the logits, then top-k, grouping and schedule in one launch
+    e = launch_route_logits(*p, x, w_gate, at<float>(ws, L.logits_part), stream);
+    if (e != hipSuccess || mark(1) != hipSuccess) return MOE_EHIP;
+    e = launch_topk_align_small(*p, kernel_cap(*p), at<float>(ws, L.logits_part), logit_bias,
+                                sel_bias, ids, gates, prob_sum, true, cpre, cnt, offs, sa, ap, sc,
+                                stream);
+    if (e != hipSuccess || mark(2) != hipSuccess || mark(3) != hipSuccess) return MOE_EHIP;
   } else if (small_routing(*p)) {
-    // small fp32 batches: logits, then top-k + grouping + schedule in one launch
+    // small batches: logits, top-k, then grouping + schedule in one launch
     e = launch_route_logits(*p, x, w_gate, at<float>(ws, L.logits_part), stream);
     if (e != hipSuccess || mark(1) != hipSuccess) return MOE_EHIP;
     e = launch_route_align_small(*p, kernel_cap(*p), at<float>(ws, L.logits_part), logit_bias,

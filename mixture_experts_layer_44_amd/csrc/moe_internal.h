@@ -101,14 +101,15 @@ hipError_t launch_route_align_small(const moe_problem& p, int cap, const float* 
                                     int32_t* sorted_assign, int32_t* assign_pos, const Schedule& sc,
                                     hipStream_t s);
 
-// the fused one-workgroup router (logits in LDS, softmax / top-k, and with do_align the grouping
-// and GEMM schedule too): bf16, T <= 128, T*k <= 1024
-bool small_route_fused(const moe_problem& p);
-hipError_t launch_route_small(const moe_problem& p, int cap, const void* x, const void* w_gate,
-                              const float* logit_bias, const float* sel_bias, int32_t* ids,
-                              float* gates, float* prob_sum, bool do_align, int32_t* counts_pre,
-                              int32_t* counts, int32_t* offsets, int32_t* sorted_assign,
-                              int32_t* assign_pos, const Schedule& sc, hipStream_t s);
+// top-k + grouping + GEMM schedule in one workgroup after the logits kernel (T <= 16,
+// T*k <= 1024); without do_align only the top-k (ids, gates, prob_sum)
+bool small_topk_fused(const moe_problem& p);
+hipError_t launch_topk_align_small(const moe_problem& p, int cap, const float* logits_part,
+                                   const float* logit_bias, const float* sel_bias, int32_t* ids,
+                                   float* gates, float* prob_sum, bool do_align,
+                                   int32_t* counts_pre, int32_t* counts, int32_t* offsets,
+                                   int32_t* sorted_assign, int32_t* assign_pos, const Schedule& sc,
+                                   hipStream_t s);
 
 // top-k of every token from the logits partials; per-workgroup probability sums to psum_part
 // (when not null)

@@ -5,10 +5,10 @@
 // Computation" and "Weighted Sum Output") and align.hip (histogram, prefix sum, stable order by
 // expert, first-come capacity dropping: "Mixture of experts (MoE)" handbook, "Implementation";
 // "MoE Architecture" §2 "Expert capacity and token dropping"):
-//   - route_small_kernel (bf16, T <= 128): the fused router, one launch: logits kept in LDS,
-//     softmax / top-k with wave reductions, then grouping and the GEMM schedule.
-//   - align_small_kernel: after the multi-launch logits and top-k (fp32 storage, or batches the
-//     fused kernel does not take), probability sums + grouping + schedule in one workgroup.
+//   - topk_align_small_kernel (T <= 16): after the logits kernel, softmax / top-k with wave
+//     reductions, then grouping and the GEMM schedule, in one launch.
+//   - align_small_kernel: after the logits and the multi-workgroup top-k (larger small
+//     batches), probability sums + grouping + schedule in one workgroup.
 // The grouping is bit-identical to the multi-launch align kernels. At decode sizes each of
 // those steps is a few microseconds of launch latency and almost no work, so a single
 // 1024-thread workgroup does them back to back out of LDS.
@@ -158,105 +158,33 @@ __global__ __launch_bounds__(1024) void align_small_kernel(
                      n_shared, sc);
 }
 
-// ------------------------------------------------------------------ fused decode router
-// The whole router of a small batch in one workgroup, the logits never leaving the CU:
-//   1. logits [T][E_pad] = x . w_gate^T with v_mfma_f32_16x16x32_bf16 (fp32 accumulate). Wave w
-//      takes expert tile w % tiles (16 experts) over K slice w / tiles (d / S columns); its
-//      16-byte operand loads go straight to registers, U steps of 32 ahead. The S slices' partial
-//      logits are added into LDS in slice order (deterministic).
-//   2. one token per wave at a time: offset, softmax, top-k and renormalised gates with the DPP
-//      wave reductions of topk.h; each wave keeps its own running probability sums, added in wave
-//      order at the end (prob_sum).
-//   3. grouping by expert with the capacity limit and the grouped-GEMM schedule, out of LDS.
-// At decode sizes the multi-launch router spends most of its time in launch latency and global
-// round trips between its three kernels; here one CU streams w_gate once (512 KB for E = 128,
-// d = 2048) and everything after stays on chip.
-constexpr int kSmallLogits = 16384;   // T * E_pad logits kept in LDS (64 KB)
+// ------------------------------------------------------------------ fused top-k + grouping
+// After the router's logits kernel (split-K fp32 partials, many workgroups), one workgroup of 16
+// waves does the rest of the routing of a small batch (T <= 16, T*k <= 1024) in one launch:
+//   1. one token per wave at a time: the K-split partials added in slice order, the offset,
+//      softmax, top-k and renormalised gates with the DPP wave reductions of topk.h -- the same
+//      per-token code as route_topk_kernel, so ids and gates are the same bits; each wave keeps
+//      running probability sums, added in wave order at the end (prob_sum);
+//   2. grouping by expert with the capacity limit, and the grouped-GEMM schedule, out of LDS.
+// At decode sizes each launch costs a few microseconds of fixed latency for almost no work; this
+// replaces the top-k launch and the grouping launch with one. (Computing the logits in this
+// workgroup too was measured slower: one CU streams w_gate at a fraction of the rate that the
+// logits kernel's workgroups reach together.)
+constexpr int kSmallTopkTokens = 16;   // one token per wave
 
-template <int NF>
-__global__ __launch_bounds__(1024) void route_small_kernel(
-    const bf16_t* __restrict__ x, const bf16_t* __restrict__ w, int T, int d, int E, int E_pad,
-    int k, int S, const float* __restrict__ logit_bias, const float* __restrict__ sel_bias,
-    int32_t* __restrict__ ids, float* __restrict__ gates, float* __restrict__ prob_sum,
-    int do_align, int cap, int32_t* __restrict__ counts_pre, int32_t* __restrict__ counts,
+__global__ __launch_bounds__(1024) void topk_align_small_kernel(
+    const float* __restrict__ part, int KS, int T, int E, int E_pad, int k,
+    const float* __restrict__ logit_bias, const float* __restrict__ sel_bias,
+    int32_t* __restrict__ ids, float* __restrict__ gates, float* __restrict__ prob_sum, int do_align,
+    int cap, int32_t* __restrict__ counts_pre, int32_t* __restrict__ counts,
     int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_assign,
     int32_t* __restrict__ assign_pos, int n_shared, Schedule sc) {
-  __shared__ float lg[kSmallLogits];
   __shared__ float pw[NWAVE][256];
   __shared__ AlignLds L;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int tiles = E_pad / 16;
-  const bool gemm_wave = wave < tiles * S;
-  const int tile = wave % tiles, slice = wave / tiles;
-  const int r = lane & 15, kq = (lane >> 4) * 8;
-  const int e_b = tile * 16 + r;
 
-  // ---- 1. logits
-  f32x4 acc[NF];
-#pragma unroll
-  for (int f = 0; f < NF; ++f) acc[f] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (gemm_wave) {
-    const int klen = d / S, kb0 = slice * klen;
-    const bool b_ok = e_b < E;
-    const bf16_t* bp = w + (size_t)(b_ok ? e_b : 0) * d + kb0 + kq;
-    const bf16_t* ap[NF];
-    bool a_ok[NF];
-#pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      const int t = 16 * f + r;
-      a_ok[f] = t < T;
-      ap[f] = x + (size_t)(a_ok[f] ? t : 0) * d + kb0 + kq;   // rows past T read row 0, zeroed
-    }
-    const bf16x8 z8 = {};
-    constexpr int U = NF == 1 ? 8 : (NF == 2 ? 4 : (NF == 4 ? 2 : 1));
-    const int nsteps = klen / 32;
-    int st = 0;
-    for (; st + U <= nsteps; st += U) {
-      bf16x8 a[U][NF], b[U];
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        b[u] = *(const bf16x8*)(bp + (st + u) * 32);
-#pragma unroll
-        for (int f = 0; f < NF; ++f) a[u][f] = *(const bf16x8*)(ap[f] + (st + u) * 32);
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int u = 0; u < U; ++u)
-#pragma unroll
-        for (int f = 0; f < NF; ++f)
-          acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_ok[f] ? a[u][f] : z8,
-                                                           b_ok ? b[u] : z8, acc[f], 0, 0, 0);
-    }
-    for (; st < nsteps; ++st) {
-      const bf16x8 b = *(const bf16x8*)(bp + st * 32);
-#pragma unroll
-      for (int f = 0; f < NF; ++f) {
-        const bf16x8 a = *(const bf16x8*)(ap[f] + st * 32);
-        acc[f] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_ok[f] ? a : z8, b_ok ? b : z8, acc[f],
-                                                         0, 0, 0);
-      }
-    }
-  }
-  // C layout (16x16): lane holds column (expert) lane%16, rows (tokens) 4*(lane/16)+i. The
-  // slices are added in slice order: slice 0 writes, then each later slice adds its part.
-  for (int sl = 0; sl < S; ++sl) {
-    if (gemm_wave && slice == sl) {
-#pragma unroll
-      for (int f = 0; f < NF; ++f)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int t = 16 * f + 4 * (lane >> 4) + i;
-          if (t < T) {
-            float* dst = &lg[t * E_pad + e_b];
-            *dst = sl == 0 ? acc[f][i] : *dst + acc[f][i];
-          }
-        }
-    }
-    __syncthreads();
-  }
-
-  // ---- 2. softmax, top-k, gates; per-wave probability sums
+  // ---- 1. softmax, top-k, gates; per-wave probability sums
   float pacc[4] = {0.f, 0.f, 0.f, 0.f};
   for (int t = wave; t < T; t += NWAVE) {
     float lgv[4], pr[4];
@@ -265,7 +193,8 @@ __global__ __launch_bounds__(1024) void route_small_kernel(
     for (int i = 0; i < 4; ++i) {
       const int e = lane + 64 * i;
       live[i] = e < E;
-      lgv[i] = live[i] ? lg[t * E_pad + e] + (logit_bias ? logit_bias[e] : 0.f) : -INFINITY;
+      lgv[i] = live[i] ? sum_partials(part, KS, T, E_pad, t, e) + (logit_bias ? logit_bias[e] : 0.f)
+                       : -INFINITY;
     }
     int my_e;
     float my_g;
@@ -289,7 +218,7 @@ __global__ __launch_bounds__(1024) void route_small_kernel(
   }
   if (!do_align) return;   // uniform
 
-  // ---- 3. grouping + schedule
+  // ---- 2. grouping + schedule
   align_schedule_lds(L, T * k, T, E, cap, counts_pre, counts, offsets, sorted_assign, assign_pos,
                      n_shared, sc);
 }
@@ -298,32 +227,23 @@ __global__ __launch_bounds__(1024) void route_small_kernel(
 
 bool small_routing(const moe_problem& p) { return (long long)p.T * p.k <= 1024; }
 
-// the fused one-workgroup router: bf16, T*k <= 1024, at most 128 tokens (8 row fragments) and
-// their logits fit the LDS table
-bool small_route_fused(const moe_problem& p) {
-  const int E_pad = ceil_div(p.E, 16) * 16;
-  return p.dtype == MOE_BF16 && p.T >= 1 && p.T <= 128 && small_routing(p) &&
-         (long long)p.T * E_pad <= kSmallLogits;
+// top-k and grouping in one workgroup after the logits: at most 4 tokens per wave
+bool small_topk_fused(const moe_problem& p) {
+  return p.T >= 1 && p.T <= kSmallTopkTokens && small_routing(p);
 }
 
-hipError_t launch_route_small(const moe_problem& p, int cap, const void* x, const void* w_gate,
-                              const float* logit_bias, const float* sel_bias, int32_t* ids,
-                              float* gates, float* prob_sum, bool do_align, int32_t* counts_pre,
-                              int32_t* counts, int32_t* offsets, int32_t* sorted_assign,
-                              int32_t* assign_pos, const Schedule& sc, hipStream_t s) {
-  if (!small_route_fused(p)) return hipErrorInvalidValue;
+hipError_t launch_topk_align_small(const moe_problem& p, int cap, const float* logits_part,
+                                   const float* logit_bias, const float* sel_bias, int32_t* ids,
+                                   float* gates, float* prob_sum, bool do_align,
+                                   int32_t* counts_pre, int32_t* counts, int32_t* offsets,
+                                   int32_t* sorted_assign, int32_t* assign_pos, const Schedule& sc,
+                                   hipStream_t s) {
+  if (!small_topk_fused(p)) return hipErrorInvalidValue;
   const int E_pad = ceil_div(p.E, 16) * 16;
-  const int tiles = E_pad / 16;
-  // K slices: as many as the 16 waves allow, each a whole number of 32-column steps
-  int S = NWAVE / tiles;
-  while (S > 1 && p.d % (32 * S)) --S;
-  auto kern = p.T <= 16 ? route_small_kernel<1>
-            : p.T <= 32 ? route_small_kernel<2>
-            : p.T <= 64 ? route_small_kernel<4> : route_small_kernel<8>;
-  hipLaunchKernelGGL(kern, dim3(1), dim3(1024), 0, s, (const bf16_t*)x, (const bf16_t*)w_gate, p.T,
-                     p.d, p.E, E_pad, p.k, S, logit_bias, sel_bias, ids, gates, prob_sum,
-                     do_align ? 1 : 0, cap, counts_pre, counts, offsets, sorted_assign, assign_pos,
-                     p.n_shared, sc);
+  hipLaunchKernelGGL(topk_align_small_kernel, dim3(1), dim3(1024), 0, s, logits_part,
+                     route_ksplit(p), p.T, p.E, E_pad, p.k, logit_bias, sel_bias, ids, gates,
+                     prob_sum, do_align ? 1 : 0, cap, counts_pre, counts, offsets, sorted_assign,
+                     assign_pos, p.n_shared, sc);
   return hipGetLastError();
 }
 

@@ -562,7 +562,8 @@ def config_entry(w, r):
             "dominant": {"stage": r["dominant"], "avg_launch_ms": round(roof["avg_launch_ms"], 5),
                          "bound": roof["bound"], "achieved": roof["achieved"],
                          "unit": roof["unit"], "frac": roof["frac"],
-                         "cold_frac": r["cold"]["dominant_frac"]}}
+                         "cold_frac": r["cold"]["dominant_frac"], "traffic": roof["traffic"],
+                         "algorithmic_per_launch": roof["algorithmic_per_launch"]}}
 
 
 def measure_forward(w, args, g, dev, torch, moe):

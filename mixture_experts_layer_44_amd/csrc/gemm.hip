@@ -80,7 +80,8 @@ struct GemmArgs {
   float* V;
 };
 
-template <int BM, int BNB, int WM, int WN, int BK, int STAGES, bool GATEUP, bool RS = false>
+// RS: register staging depth (0: direct global->LDS ring; 1 or 2 register sets of loads in flight)
+template <int BM, int BNB, int WM, int WN, int BK, int STAGES, bool GATEUP, int RS = 0>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs args) {
   constexpr int NW = WM * WN;
   constexpr int CHUNKS = BK / 8;                   // 16-byte chunks per row per stage
@@ -113,6 +114,16 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs args) 
   // physical slot l%CHUNKS, so it fetches the logical chunk that the swizzle puts there.
   const bf16_t* src_base[DMA_WAVE];
   uint32_t src_off[DMA_WAVE];
+  // The assignment ids of this lane's gathered rows are loaded together, before the first wait
+  // (loaded one by one, each behind the branch on its load's matrix, they were serial round
+  // trips at the start of every tile). Loads of B rows read a valid entry and discard it.
+  int sa[DMA_WAVE];
+#pragma unroll
+  for (int i = 0; i < DMA_WAVE; ++i) {
+    const int r = tc.m_local * BM + (wave * DMA_WAVE + i) * RPI + lane / CHUNKS;
+    const bool gathered = !shared_grp && (wave * DMA_WAVE + i) * RPI < BM;
+    sa[i] = GATEUP ? args.sorted_assign[tc.off + (gathered && r < tc.rows ? r : 0)] : 0;
+  }
 #pragma unroll
   for (int i = 0; i < DMA_WAVE; ++i) {
     const int q = wave * DMA_WAVE + i;
@@ -123,7 +134,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs args) 
       if (GATEUP) {
         const int r = tc.m_local * BM + row;
         const int rr = r < tc.rows ? r : 0;             // padding rows repeat the first row
-        int tok = shared_grp ? rr : args.sorted_assign[tc.off + rr] / args.k;
+        int tok = shared_grp ? rr : sa[i] / args.k;
         srow = (unsigned)tok < (unsigned)args.T ? tok : 0;
       } else {
         srow = tc.mt_global * BM + row;
@@ -187,6 +198,24 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs args) 
   auto compute = [&](const bf16_t* buf) {
     constexpr int NKS = BK / 16;
     __builtin_amdgcn_iglp_opt(1);
+    if constexpr (RS == 2) {
+      // two register sets leave no room for a second set of fragments; the other wave on the
+      // SIMD covers this wave's fragment reads
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        bf16x8 af1[FM], bf1[FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) af1[i] = *(const bf16x8*)&buf[swz<BK>(arow[i], 2 * ks + fkc)];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) bf1[j] = *(const bf16x8*)&buf[swz<BK>(brow[j], 2 * ks + fkc)];
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af1[i], bf1[j], acc[i][j], 0, 0, 0);
+      }
+      return;
+    }
     bf16x8 af[2][FM], bfr[2][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i) af[0][i] = *(const bf16x8*)&buf[swz<BK>(arow[i], fkc)];
@@ -212,7 +241,53 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs args) 
     }
   };
 
-  if constexpr (RS) {
+  if constexpr (RS == 2) {
+    // Two register sets: each lane loads its 16-byte pieces of step kt+3 while step kt computes
+    // out of one LDS stage; after the MFMAs it stores step kt+1 (loaded two steps earlier) into
+    // the other stage. A load has two compute steps to land, where one step covers an L2 hit
+    // but not a line that has to come from the Infinity Cache or HBM. Steps go in pairs so the
+    // two register sets are fixed at compile time (the launcher checks that KT is even);
+    // vector-memory loads retire in order, so the wait before a store leaves the newer set's
+    // loads in flight.
+    static_assert(STAGES == 2, "two stages: compute one while the other is written");
+    u32x4 stg0[DMA_WAVE], stg1[DMA_WAVE];
+    const int last = KT - 1;
+    auto load_into = [&](u32x4 (&r)[DMA_WAVE], int kt) {
+#pragma unroll
+      for (int i = 0; i < DMA_WAVE; ++i)
+        r[i] = *(const u32x4*)(src_base[i] + src_off[i] + k0 + kt * BK);
+    };
+    auto write_from = [&](const u32x4 (&r)[DMA_WAVE], int st) {
+      bf16_t* dst = smem + st * STAGE;
+#pragma unroll
+      for (int i = 0; i < DMA_WAVE; ++i)
+        *(u32x4*)(dst + (wave * DMA_WAVE + i) * RPI * BK + lane * 8) = r[i];
+    };
+    load_into(stg0, 0);
+    load_into(stg1, min(1, last));
+    write_from(stg0, 0);
+    load_into(stg0, min(2, last));
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's stores are in LDS
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    for (int kt = 0; kt < KT; kt += 2) {
+      // stage 0 holds step kt, stg1 step kt+1, stg0 step kt+2
+      compute(smem);
+      write_from(stg1, 1);
+      load_into(stg1, min(kt + 3, last));
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      // stage 1 holds step kt+1, stg0 step kt+2, stg1 step kt+3 (past the end: copies of the
+      // last step, stored into a stage nobody reads again)
+      compute(smem + STAGE);
+      write_from(stg0, 0);
+      load_into(stg0, min(kt + 4, last));
+      __builtin_amdgcn_s_waitcnt(0xC07F);
+      __builtin_amdgcn_s_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  } else if constexpr (RS == 1) {
     // Register-staged: each lane loads its 16-byte pieces of step kt+1 into registers while
     // step kt computes, then stores them (ds_write_b128, the same places the direct loads
     // fill) into the other stage; one barrier per step.
@@ -347,6 +422,13 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_st_kernel(GemmArgs arg
   // swizzle puts there (the swizzle is an involution).
   // (32-bit element offsets from the matrix base keep the register count down; the entry
   // points reject every shape whose x, expert matrices or padded h rows reach 2^32 elements)
+  // (the assignment ids of the gathered rows are loaded together, before the first wait)
+  int sa[DMA_A];
+#pragma unroll
+  for (int i = 0; i < DMA_A; ++i) {
+    const int r = tc.m_local * BM + (wave * DMA_A + i) * RPI + lane / CHUNKS;
+    sa[i] = GATEUP ? args.sorted_assign[tc.off + (!shared_grp && r < tc.rows ? r : 0)] : 0;
+  }
   uint32_t aoff[DMA_A];
 #pragma unroll
   for (int i = 0; i < DMA_A; ++i) {
@@ -357,7 +439,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_st_kernel(GemmArgs arg
     if (GATEUP) {
       const int r = tc.m_local * BM + row;
       const int rr = r < tc.rows ? r : 0;             // padding rows repeat the first row
-      const int tok = shared_grp ? rr : args.sorted_assign[tc.off + rr] / args.k;
+      const int tok = shared_grp ? rr : sa[i] / args.k;
       srow = (unsigned)tok < (unsigned)args.T ? tok : 0;
     } else {
       srow = tc.mt_global * BM + row;
@@ -586,6 +668,13 @@ __global__ __launch_bounds__(256) void gemm_bf16_dec_kernel(GemmArgs args) {
     const int row = tc.n0 + (GATEUP ? (b & 1) : b) * 16 + r16;
     bp[b] = mat + (size_t)row * K + kbase;
   }
+  // (the assignment ids of the gathered rows are loaded together, before the first wait)
+  int sa[kDecBM / 16];
+#pragma unroll
+  for (int f = 0; f < kDecBM / 16; ++f) {
+    const int r = tc.m_local * kDecBM + f * 16 + r16;
+    sa[f] = GATEUP ? args.sorted_assign[tc.off + (!shared_grp && r < tc.rows ? r : 0)] : 0;
+  }
   const bf16_t* ap[kDecBM / 16];
 #pragma unroll
   for (int f = 0; f < kDecBM / 16; ++f) {
@@ -593,7 +682,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_dec_kernel(GemmArgs args) {
     if (GATEUP) {
       const int r = tc.m_local * kDecBM + f * 16 + r16;
       const int rr = r < tc.rows ? r : 0;             // padding rows repeat the first row
-      const int tok = shared_grp ? rr : args.sorted_assign[tc.off + rr] / args.k;
+      const int tok = shared_grp ? rr : sa[f] / args.k;
       srow = (unsigned)tok < (unsigned)args.T ? tok : 0;
     } else {
       srow = tc.mt_global * kDecBM + f * 16 + r16;     // padding rows: results not stored
@@ -867,7 +956,7 @@ hipError_t launch_dec(const moe_problem& p, const GemmArgs& a, const GemmArgs& b
 }
 
 template <int BM, int BNB_UP, int WM_UP, int WN_UP, int BNB_DN, int WM_DN, int WN_DN, int BK, int ST,
-          bool RS = false>
+          int RS = 0>
 hipError_t launch_bf16(const moe_problem& p, const GemmArgs& a, const GemmArgs& b, hipStream_t s,
                        hipEvent_t between, bool up_only) {
   if (p.d_ff % (BNB_UP / 2) || p.d % BNB_DN) return hipErrorInvalidValue;   // n-tiles cover N

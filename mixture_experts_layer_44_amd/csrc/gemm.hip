@@ -80,7 +80,7 @@ struct GemmArgs {
   float* V;
 };
 
-// RS: register staging depth (0: direct global->LDS ring; 1 or 2 register sets of loads in flight)
+// RS: 1 = register-staged (2 stages), 0 = direct global->LDS ring
 template <int BM, int BNB, int WM, int WN, int BK, int STAGES, bool GATEUP, int RS = 0>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs args) {
   constexpr int NW = WM * WN;
@@ -198,24 +198,6 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs args) 
   auto compute = [&](const bf16_t* buf) {
     constexpr int NKS = BK / 16;
     __builtin_amdgcn_iglp_opt(1);
-    if constexpr (RS == 2) {
-      // two register sets leave no room for a second set of fragments; the other wave on the
-      // SIMD covers this wave's fragment reads
-#pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        bf16x8 af1[FM], bf1[FN];
-#pragma unroll
-        for (int i = 0; i < FM; ++i) af1[i] = *(const bf16x8*)&buf[swz<BK>(arow[i], 2 * ks + fkc)];
-#pragma unroll
-        for (int j = 0; j < FN; ++j) bf1[j] = *(const bf16x8*)&buf[swz<BK>(brow[j], 2 * ks + fkc)];
-#pragma unroll
-        for (int i = 0; i < FM; ++i)
-#pragma unroll
-          for (int j = 0; j < FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af1[i], bf1[j], acc[i][j], 0, 0, 0);
-      }
-      return;
-    }
     bf16x8 af[2][FM], bfr[2][FN];
 #pragma unroll
     for (int i = 0; i < FM; ++i) af[0][i] = *(const bf16x8*)&buf[swz<BK>(arow[i], fkc)];
@@ -241,53 +223,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs args) 
     }
   };
 
-  if constexpr (RS == 2) {
-    // Two register sets: each lane loads its 16-byte pieces of step kt+3 while step kt computes
-    // out of one LDS stage; after the MFMAs it stores step kt+1 (loaded two steps earlier) into
-    // the other stage. A load has two compute steps to land, where one step covers an L2 hit
-    // but not a line that has to come from the Infinity Cache or HBM. Steps go in pairs so the
-    // two register sets are fixed at compile time (the launcher checks that KT is even);
-    // vector-memory loads retire in order, so the wait before a store leaves the newer set's
-    // loads in flight.
-    static_assert(STAGES == 2, "two stages: compute one while the other is written");
-    u32x4 stg0[DMA_WAVE], stg1[DMA_WAVE];
-    const int last = KT - 1;
-    auto load_into = [&](u32x4 (&r)[DMA_WAVE], int kt) {
-#pragma unroll
-      for (int i = 0; i < DMA_WAVE; ++i)
-        r[i] = *(const u32x4*)(src_base[i] + src_off[i] + k0 + kt * BK);
-    };
-    auto write_from = [&](const u32x4 (&r)[DMA_WAVE], int st) {
-      bf16_t* dst = smem + st * STAGE;
-#pragma unroll
-      for (int i = 0; i < DMA_WAVE; ++i)
-        *(u32x4*)(dst + (wave * DMA_WAVE + i) * RPI * BK + lane * 8) = r[i];
-    };
-    load_into(stg0, 0);
-    load_into(stg1, min(1, last));
-    write_from(stg0, 0);
-    load_into(stg0, min(2, last));
-    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's stores are in LDS
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    for (int kt = 0; kt < KT; kt += 2) {
-      // stage 0 holds step kt, stg1 step kt+1, stg0 step kt+2
-      compute(smem);
-      write_from(stg1, 1);
-      load_into(stg1, min(kt + 3, last));
-      __builtin_amdgcn_s_waitcnt(0xC07F);
-      __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-      // stage 1 holds step kt+1, stg0 step kt+2, stg1 step kt+3 (past the end: copies of the
-      // last step, stored into a stage nobody reads again)
-      compute(smem + STAGE);
-      write_from(stg0, 0);
-      load_into(stg0, min(kt + 4, last));
-      __builtin_amdgcn_s_waitcnt(0xC07F);
-      __builtin_amdgcn_s_barrier();
-      __builtin_amdgcn_sched_barrier(0);
-    }
-  } else if constexpr (RS == 1) {
+  if constexpr (RS == 1) {
     // Register-staged: each lane loads its 16-byte pieces of step kt+1 into registers while
     // step kt computes, then stores them (ds_write_b128, the same places the direct loads
     // fill) into the other stage; one barrier per step.
@@ -1030,7 +966,7 @@ hipError_t launch_expert_ffn(const moe_problem& p, const void* x, const void* w1
     b.out_rows_b = out_rows_b;
     if (!up_only && b.ksplit == 2 && !out_rows_b) return hipErrorInvalidValue;
     if (sc.BM == 256 && gemm_wide(p))
-      return launch_bf16<256, 256, 4, 2, 256, 4, 2, 64, 2, true>(p, a, b, s, between, up_only);
+      return launch_bf16<256, 256, 4, 2, 256, 4, 2, 64, 2, 1>(p, a, b, s, between, up_only);
     if (sc.BM == 256) return launch_bf16_st<256, 256, 4, 2, 256, 4, 2>(p, a, b, s, between, up_only);
     if (sc.BM == 192) return launch_bf16_st<192, 256, 2, 4, 256, 2, 4>(p, a, b, s, between, up_only);
     if (sc.BM == kDecBM && gemm_dec(p)) return launch_dec(p, a, b, s, between, up_only);

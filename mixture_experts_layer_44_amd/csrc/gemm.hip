@@ -797,9 +797,9 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs32 args) {
 
 }  // namespace
 
-int grid_for(int mtiles, int nt) {
-  long long g = (long long)mtiles * nt;
-  return (int)((g + 7) / 8 * 8);
+int grid_for(int mtiles, int nt, int xcd_chunk) {
+  const long long g = (long long)mtiles * nt, q = xcd_chunk ? 8 * kXcdChunk : 8;
+  return (int)((g + q - 1) / q * q);
 }
 
 // expected kept rows per expert: T*k/E, or the capacity if that is smaller
@@ -883,11 +883,11 @@ void launch_dec_k(int steps, dim3 grid, hipStream_t s, const GemmArgs& a) {
 hipError_t launch_dec(const moe_problem& p, const GemmArgs& a, const GemmArgs& b, hipStream_t s,
                       hipEvent_t between, bool up_only) {
   if (!gemm_dec(p) || a.sc.BM != kDecBM) return hipErrorInvalidValue;
-  launch_dec_k<true>(p.d / 256, dim3(grid_for(a.sc.max_mtiles, p.d_ff / dec_feat(true))), s, a);
+  launch_dec_k<true>(p.d / 256, dim3(grid_for(a.sc.max_mtiles, p.d_ff / dec_feat(true), a.sc.xcd_chunk)), s, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || up_only) return err;
   if (between && (err = hipEventRecord(between, s)) != hipSuccess) return err;
-  launch_dec_k<false>(p.d_ff / 256, dim3(grid_for(b.sc.max_mtiles, p.d / dec_feat(false))), s, b);
+  launch_dec_k<false>(p.d_ff / 256, dim3(grid_for(b.sc.max_mtiles, p.d / dec_feat(false), b.sc.xcd_chunk)), s, b);
   return hipGetLastError();
 }
 
@@ -897,13 +897,13 @@ hipError_t launch_bf16(const moe_problem& p, const GemmArgs& a, const GemmArgs& 
                        hipEvent_t between, bool up_only) {
   if (p.d_ff % (BNB_UP / 2) || p.d % BNB_DN) return hipErrorInvalidValue;   // n-tiles cover N
   hipLaunchKernelGGL((gemm_bf16_kernel<BM, BNB_UP, WM_UP, WN_UP, BK, ST, true, RS>),
-                     dim3(grid_for(a.sc.max_mtiles, p.d_ff / (BNB_UP / 2))), dim3(WM_UP * WN_UP * 64),
+                     dim3(grid_for(a.sc.max_mtiles, p.d_ff / (BNB_UP / 2), a.sc.xcd_chunk)), dim3(WM_UP * WN_UP * 64),
                      0, s, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || up_only) return err;
   if (between && (err = hipEventRecord(between, s)) != hipSuccess) return err;
   hipLaunchKernelGGL((gemm_bf16_kernel<BM, BNB_DN, WM_DN, WN_DN, BK, ST, false, RS>),
-                     dim3(grid_for(b.sc.max_mtiles * b.ksplit, p.d / BNB_DN)),
+                     dim3(grid_for(b.sc.max_mtiles * b.ksplit, p.d / BNB_DN, b.sc.xcd_chunk)),
                      dim3(WM_DN * WN_DN * 64), 0, s, b);
   return hipGetLastError();
 }
@@ -913,13 +913,13 @@ hipError_t launch_bf16_st(const moe_problem& p, const GemmArgs& a, const GemmArg
                           hipStream_t s, hipEvent_t between, bool up_only) {
   if (p.d_ff % (BNB_UP / 2) || p.d % BNB_DN) return hipErrorInvalidValue;   // n-tiles cover N
   hipLaunchKernelGGL((gemm_bf16_st_kernel<BM, BNB_UP, WM_UP, WN_UP, true>),
-                     dim3(grid_for(a.sc.max_mtiles, p.d_ff / (BNB_UP / 2))), dim3(WM_UP * WN_UP * 64),
+                     dim3(grid_for(a.sc.max_mtiles, p.d_ff / (BNB_UP / 2), a.sc.xcd_chunk)), dim3(WM_UP * WN_UP * 64),
                      0, s, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || up_only) return err;
   if (between && (err = hipEventRecord(between, s)) != hipSuccess) return err;
   hipLaunchKernelGGL((gemm_bf16_st_kernel<BM, BNB_DN, WM_DN, WN_DN, false>),
-                     dim3(grid_for(b.sc.max_mtiles * b.ksplit, p.d / BNB_DN)),
+                     dim3(grid_for(b.sc.max_mtiles * b.ksplit, p.d / BNB_DN, b.sc.xcd_chunk)),
                      dim3(WM_DN * WN_DN * 64), 0, s, b);
   return hipGetLastError();
 }
@@ -990,7 +990,7 @@ hipError_t launch_expert_ffn(const moe_problem& p, const void* x, const void* w1
   a.sorted_assign = sorted_assign;
   a.sc = sc;
   a.H = (float*)h;
-  hipLaunchKernelGGL(gemm_f32_kernel<true>, dim3(grid_for(sc.max_mtiles, ceil_div(p.d_ff, BN32))),
+  hipLaunchKernelGGL(gemm_f32_kernel<true>, dim3(grid_for(sc.max_mtiles, ceil_div(p.d_ff, BN32), sc.xcd_chunk)),
                      dim3(256), 0, s, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
@@ -1008,7 +1008,7 @@ hipError_t launch_expert_ffn(const moe_problem& p, const void* x, const void* w1
   b.sc = sc;
   b.out_rows = out_rows;
   b.shared_out = shared_out;
-  hipLaunchKernelGGL(gemm_f32_kernel<false>, dim3(grid_for(sc.max_mtiles, ceil_div(p.d, BN32))),
+  hipLaunchKernelGGL(gemm_f32_kernel<false>, dim3(grid_for(sc.max_mtiles, ceil_div(p.d, BN32), sc.xcd_chunk)),
                      dim3(256), 0, s, b);
   return hipGetLastError();
 }

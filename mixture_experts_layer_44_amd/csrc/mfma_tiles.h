@@ -19,14 +19,27 @@ struct TileCoord {
 };
 
 // Tile for this workgroup, or false if it has none. Uniform across the workgroup.
+// Workgroups are dealt round-robin to the 8 XCDs (xcd = b % 8). By default each XCD walks one
+// contiguous range of the tile list. With sc.xcd_chunk, the list is dealt to the XCDs in chunks
+// of kXcdChunk consecutive tiles instead, so that the tiles of the few segments at a capacity
+// limit (L2-bound: their m-tiles share each weight tile) spread over every XCD's L2 rather than
+// landing on the first few XCDs; a chunk keeps an n-tile's m-tiles together. The grid then has
+// whole multiples of 8 * kXcdChunk workgroups (grid_for).
 __device__ __forceinline__ bool tile_coord(const Schedule& sc, int NT, int bn, TileCoord& tc,
                                            int S = 1, int* half = nullptr) {
   const int total = sc.mt_start[sc.G] * NT;
   const int bid = blockIdx.x;
   const int xcd = bid & 7, slot = bid >> 3;
-  const int per = (total * S + 7) >> 3;
-  if (slot >= per) return false;
-  int L = xcd * per + slot;
+  int L;
+  if (sc.xcd_chunk) {
+    const int per = (total * S + 8 * kXcdChunk - 1) / (8 * kXcdChunk) * kXcdChunk;
+    if (slot >= per) return false;
+    L = ((slot / kXcdChunk) * 8 + xcd) * kXcdChunk + slot % kXcdChunk;
+  } else {
+    const int per = (total * S + 7) >> 3;
+    if (slot >= per) return false;
+    L = xcd * per + slot;
+  }
   if (L >= total * S) return false;
   if (half) *half = L / total;   // work unit L = half * total + tile
   L %= total;

@@ -68,7 +68,9 @@ struct Schedule {
   int max_mtiles;
   int G;
   int BM;
+  int xcd_chunk = 0;   // 1: tiles dealt to the XCDs in chunks of kXcdChunk (capacity-limited routing)
 };
+constexpr int kXcdChunk = 16;
 
 // m-tiles that n_rows routed rows (in E segments) plus the shared expert's T rows can need
 int max_mtiles(long long n_rows, int T, int E, int n_shared, int BM);
@@ -79,7 +81,8 @@ bool gemm_small(const moe_problem& p);
 bool gemm_dec(const moe_problem& p);     // small class on the decode kernel (32-row m-tiles)
 int gemm_bm(const moe_problem& p);
 int gemm_bm_exact(const moe_problem& p, int C);   // all segments of exactly C rows
-int grid_for(int mtiles, int nt);
+// workgroups for up to mtiles * nt tiles (a whole number of XCD chunks when chunked)
+int grid_for(int mtiles, int nt, int xcd_chunk = 0);
 
 // ---------------------------------------------------------------- launchers
 // router: d-slices of the logits GEMM, scratch bytes for its fp32 partial logits, and the

@@ -237,7 +237,110 @@ __global__ __launch_bounds__(1024) void psum_reduce_kernel(const float* __restri
   }
 }
 
+// ------------------------------------------------------------------ fused router
+// When w_gate is small (E <= 16 experts: 128 KB at d = 4096), one workgroup of 16 waves owns a
+// block of 16 tokens against every expert over the whole of d, so the logits never leave the CU:
+//   1. wave w takes the 16 tokens and the w-th sixteenth of d, all E_pad/16 expert fragments
+//      (v_mfma_f32_16x16x32_bf16, fp32 accumulate), loads four 32-column steps ahead; the
+//      sixteen partial blocks are added through LDS in wave order (deterministic);
+//   2. softmax, top-k and renormalised gates from LDS with the DPP wave reductions of topk.h,
+//      one token per wave; the workgroup's probability sums (tokens in wave order) go to its
+//      row of psum_part.
+// Each block reads w_gate once, from L2, and its 16 x rows once; the split-K path instead writes
+// fp32 partial logits for a second launch to add up. With more experts, w_gate re-read per
+// 16-token block costs more L2 traffic than the partial logits (measured slower at E = 64).
+constexpr int FTB = 16;                 // tokens per fused-router workgroup (one per wave)
+constexpr int FMAX_E = 16;              // one expert fragment
+
+__global__ __launch_bounds__(1024) void route_fused_kernel(
+    const bf16_t* __restrict__ x, const bf16_t* __restrict__ w, int T, int d, int E, int k,
+    const float* __restrict__ logit_bias, const float* __restrict__ sel_bias,
+    int32_t* __restrict__ ids, float* __restrict__ gates, float* __restrict__ psum_part) {
+  constexpr int RS = 16 + 4;            // padded logits row
+  __shared__ float part[16][FTB * RS];
+  __shared__ float pw[16][FMAX_E];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int tok0 = blockIdx.x * FTB;
+  const int r = lane & 15, kq = (lane >> 4) * 8;
+  const int klen = d / 16, kb0 = wave * klen;
+  const int t_a = tok0 + r;
+  const bool a_ok = t_a < T, b_ok = r < E;
+  const bf16_t* ap = x + (size_t)(a_ok ? t_a : 0) * d + kb0 + kq;   // rows past T read row 0
+  const bf16_t* bp = w + (size_t)(b_ok ? r : 0) * d + kb0 + kq;
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  const bf16x8 z8 = {};
+  constexpr int U = 4;
+  const int nsteps = klen / 32;         // d % 512 == 0
+  int st = 0;
+  for (; st + U <= nsteps; st += U) {
+    bf16x8 a[U], b[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      a[u] = *(const bf16x8*)(ap + (st + u) * 32);
+      b[u] = *(const bf16x8*)(bp + (st + u) * 32);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_ok ? a[u] : z8, b_ok ? b[u] : z8, acc, 0, 0,
+                                                    0);
+  }
+  for (; st < nsteps; ++st) {
+    const bf16x8 a = *(const bf16x8*)(ap + st * 32);
+    const bf16x8 b = *(const bf16x8*)(bp + st * 32);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_ok ? a : z8, b_ok ? b : z8, acc, 0, 0, 0);
+  }
+  // C layout (16x16): lane holds column (expert) lane%16, rows (tokens) 4*(lane/16)+i
+#pragma unroll
+  for (int i = 0; i < 4; ++i) part[wave][(4 * (lane >> 4) + i) * RS + r] = acc[i];
+  __syncthreads();
+
+  // ---- softmax / top-k, one token per wave; logits = the sixteen parts added in wave order
+  const int t = tok0 + wave;
+  float pr0 = 0.f;
+  if (t < T) {   // uniform
+    float lg[4], pr[4];
+    bool live[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = lane + 64 * i;
+      live[i] = e < E;
+      float v = -INFINITY;
+      if (live[i]) {
+        v = 0.f;
+        for (int wv = 0; wv < 16; ++wv) v += part[wv][wave * RS + e];
+        v += logit_bias ? logit_bias[e] : 0.f;
+      }
+      lg[i] = v;
+    }
+    int my_e;
+    float my_g;
+    token_topk(lg, live, sel_bias, k, lane, pr, my_e, my_g);
+    pr0 = pr[0];
+    if (lane < k) {
+      ids[(size_t)t * k + lane] = my_e;
+      gates[(size_t)t * k + lane] = my_g;
+    }
+  }
+  if (psum_part) {
+    if (lane < FMAX_E) pw[wave][lane] = pr0;
+    __syncthreads();
+    if (tid < E) {
+      float s = 0.f;
+      for (int wv = 0; wv < 16; ++wv) s += pw[wv][tid];
+      psum_part[(size_t)blockIdx.x * E + tid] = s;
+    }
+  }
+}
+
 }  // namespace
+
+// the fused router: bf16, at most 64 experts, and a batch past the small-batch routing (which
+// has its own one-workgroup top-k and grouping)
+bool route_fused(const moe_problem& p) {
+  return p.dtype == MOE_BF16 && p.E <= FMAX_E && p.d % 512 == 0 && !small_routing(p);
+}
 
 int route_ksplit(const moe_problem& p) {
   const int E_pad = ceil_div(p.E, 16) * 16;
@@ -297,6 +400,18 @@ hipError_t launch_route(const moe_problem& p, const void* x, const void* w_gate,
                         const float* logit_bias, const float* sel_bias, int32_t* ids,
                         float* gates, float* prob_sum, float* logits_part, float* psum_part,
                         hipStream_t s) {
+  if (route_fused(p)) {
+    if (p.T == 0) return hipSuccess;
+    const int nblk = ceil_div(p.T, FTB);
+    hipLaunchKernelGGL(route_fused_kernel, dim3(nblk), dim3(1024), 0, s, (const bf16_t*)x,
+                       (const bf16_t*)w_gate, p.T, p.d, p.E, p.k, logit_bias, sel_bias, ids, gates,
+                       prob_sum ? psum_part : nullptr);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess || !prob_sum) return err;
+    hipLaunchKernelGGL(psum_reduce_kernel, dim3(1), dim3(1024), 0, s, psum_part, nblk, p.E,
+                       prob_sum);
+    return hipGetLastError();
+  }
   const int nblk = route_topk_blocks(p);
   hipError_t err = launch_route_logits(p, x, w_gate, logits_part, s);
   if (err != hipSuccess) return err;

@@ -208,7 +208,7 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
 // out[e] = sum over the nblk rows of a [nblk][E] table of per-workgroup partial sums (the top-k
 // workgroups' probability sums, or the backward's logit-bias gradient). A fixed tree, so the
 // result is identical from run to run: thread (c, e) adds the rows of chunk c of C = 1024/E
-// in order, eight loads in flight; then thread e adds the C chunk sums in order.
+// in order, 32 loads in flight; then thread e adds the C chunk sums in order.
 __global__ __launch_bounds__(1024) void psum_reduce_kernel(const float* __restrict__ part, int nblk,
                                                            int E, float* __restrict__ out) {
   __shared__ float csum[1024];
@@ -219,12 +219,12 @@ __global__ __launch_bounds__(1024) void psum_reduce_kernel(const float* __restri
     const int b0 = (int)((long long)nblk * c / C), b1 = (int)((long long)nblk * (c + 1) / C);
     float s = 0.f;
     int b = b0;
-    for (; b + 8 <= b1; b += 8) {
-      float v[8];
+    for (; b + 32 <= b1; b += 32) {   // 32 loads in flight, added in block order
+      float v[32];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = part[(size_t)(b + u) * E + e];
+      for (int u = 0; u < 32; ++u) v[u] = part[(size_t)(b + u) * E + e];
 #pragma unroll
-      for (int u = 0; u < 8; ++u) s += v[u];
+      for (int u = 0; u < 32; ++u) s += v[u];
     }
     for (; b < b1; ++b) s += part[(size_t)b * E + e];
     csum[tid] = s;   // = csum[c * E + e]

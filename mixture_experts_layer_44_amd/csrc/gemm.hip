@@ -416,17 +416,28 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_st_kernel(GemmArgs arg
                                        (lds_ptr_t)(dst + (wave * DMA_A + i) * RPI * BK), 16, 0, 0);
     }
   };
-  // The gate-up's weight tiles are read once, from HBM; they go in with the non-temporal hint so
-  // they do not push the gathered x rows out of L2 before the expert's other n-tiles reuse them
-  // (DeepSeek-V3-shaped gate-up 3.41 -> 3.21 ms; on the down GEMM the hint measured no better).
-  constexpr int B_CPOL = GATEUP ? 2 : 0;   // 2: nt
+  // A weight tile that only one m-tile of its group reads is streamed from HBM once: it goes in
+  // with the non-temporal hint, so it does not push out of L2 the lines that are reused -- the
+  // gathered x rows, shared by the expert's n-tiles, and the weight tiles of groups with several
+  // m-tiles (a capped expert, the shared expert), shared by those m-tiles. DeepSeek-V3-shaped
+  // gate-up 3.41 -> 3.08 ms and down 1.93 -> 1.82 ms; skewed gate-up 0.45 -> 0.42 ms. (The hint on
+  // every weight tile: gate-up 3.21 ms.)
+  const bool b_stream = tc.mtg == 1;   // uniform
   auto issue_b = [&](int kt, int slot) {
     bf16_t* dst = Bs + slot * BSLOT;
+    if (b_stream) {
 #pragma unroll
-    for (int i = 0; i < DMA_B; ++i)
-      __builtin_amdgcn_global_load_lds((const void*)(bmat[i] + boff[i] + k0 + kt * BK),
-                                       (lds_ptr_t)(dst + (wave * DMA_B + i) * RPI * BK), 16, 0,
-                                       B_CPOL);
+      for (int i = 0; i < DMA_B; ++i)
+        __builtin_amdgcn_global_load_lds((const void*)(bmat[i] + boff[i] + k0 + kt * BK),
+                                         (lds_ptr_t)(dst + (wave * DMA_B + i) * RPI * BK), 16, 0,
+                                         2 /* nt */);
+    } else {
+#pragma unroll
+      for (int i = 0; i < DMA_B; ++i)
+        __builtin_amdgcn_global_load_lds((const void*)(bmat[i] + boff[i] + k0 + kt * BK),
+                                         (lds_ptr_t)(dst + (wave * DMA_B + i) * RPI * BK), 16, 0,
+                                         0);
+    }
   };
 
   const int wm = wave / WN, wn = wave % WN;

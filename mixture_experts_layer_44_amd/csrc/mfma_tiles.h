@@ -16,6 +16,7 @@ constexpr int wait_vm(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0F70; }
 
 struct TileCoord {
   int g, m_local, n0, mt_global, rows, off;
+  int mtg;   // m-tiles of group g
 };
 
 // Tile for this workgroup, or false if it has none. Uniform across the workgroup.
@@ -49,6 +50,7 @@ __device__ __forceinline__ bool tile_coord(const Schedule& sc, int NT, int bn, T
   const int lp = L - ms * NT;
   const int n_tile = lp / mtg;
   tc.g = g;
+  tc.mtg = mtg;
   tc.m_local = lp - n_tile * mtg;
   tc.n0 = n_tile * bn;
   tc.mt_global = ms + tc.m_local;

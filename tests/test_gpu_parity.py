@@ -70,6 +70,14 @@ SMALL = [
     W("bf16_dec_k5", T=24, d=1280, E=16, k=2, d_ff=1024, seed=122, n_shared=1, d_ff_shared=1024),
     W("bf16_dec_k6", T=40, d=1536, E=16, k=4, d_ff=1792, seed=123),
     W("bf16_dec_k7", T=40, d=1792, E=16, k=4, d_ff=1280, seed=124, capacity_factor=1.0),
+    # the fused router (E <= 16, d % 512 == 0, T*k > 1024): E not a multiple of 16, T not a
+    # multiple of 16, logit offset, selection bias and a capacity limit
+    W("bf16_fused_router", T=1101, d=512, E=12, k=3, d_ff=256, seed=125, sel_bias=True,
+      zipf_s=1.1, capacity_factor=1.25),
+    # top-k, grouping and schedule in one workgroup (T <= 16) with a capacity limit, a selection
+    # bias and a shared expert
+    W("bf16_small16_cap", T=16, d=256, E=32, k=4, d_ff=256, seed=126, capacity_factor=0.5,
+      sel_bias=True, n_shared=1, d_ff_shared=256),
 ]
 
 
@@ -193,6 +201,9 @@ COMPOSE = [
       sel_bias=True, capacity_factor=1.1),
     # wide tiles, down GEMM split in K: expert_ffn sums the halves itself, forward in the combine
     W("compose_ksplit", T=2048, d=1024, E=4, k=2, d_ff=1024, seed=202, capacity_factor=0.9),
+    # T <= 16: top-k, grouping and schedule in one workgroup after the logits
+    W("compose_small16", T=12, d=256, E=16, k=4, d_ff=256, seed=203, sel_bias=True,
+      capacity_factor=0.8),
 ]
 
 

@@ -122,7 +122,7 @@ __global__ __launch_bounds__(256) void align_scatter_kernel(
     uint64_t active = __ballot(valid);
     while (active) {
       const int leader = __ffsll((unsigned long long)active) - 1;
-      const int le = __shfl(e, leader);
+      const int le = __builtin_amdgcn_readlane(e, leader);   // leader is wave-uniform
       const uint64_t m = __ballot(valid && e == le);
       if (valid && e == le) {
         my_rank = __popcll(m & lt_mask);

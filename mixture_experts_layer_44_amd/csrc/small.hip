@@ -21,16 +21,11 @@ namespace {
 constexpr int NWAVE = 16;
 
 // exclusive scan of v over the first 320 threads (5 waves; the values live in threads < 257,
-// the others pass 0); all 1024 threads call it. Each wave scans its 64 values with shuffles,
+// the others pass 0); all 1024 threads call it. Each wave scans its 64 values with DPP steps,
 // then adds the totals of the waves before it.
 __device__ int scan320(int v, int* wsum, int* total) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
+  const int x = wave_incl_scan(v);
   if (lane == 63 && wave < 5) wsum[wave] = x;
   __syncthreads();
   int base = 0;
@@ -68,7 +63,7 @@ __device__ void align_schedule_lds(AlignLds& L, int n, int T, int E, int cap,
   uint64_t active = __ballot(valid);
   while (active) {
     const int leader = __ffsll((unsigned long long)active) - 1;
-    const int le = __shfl(e, leader);
+    const int le = __builtin_amdgcn_readlane(e, leader);   // leader is wave-uniform
     const uint64_t msk = __ballot(valid && e == le);
     if (valid && e == le) {
       my_rank = __popcll(msk & lt_mask);

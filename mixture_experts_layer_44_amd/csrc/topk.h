@@ -33,6 +33,18 @@ __device__ __forceinline__ int wave_reduce_bits(int v, int identity, Op op) {
   return __builtin_amdgcn_readlane(v, 63);
 }
 
+// Inclusive prefix sum over the lanes: the steps of wave_reduce_bits leave in lane l the sum of
+// lanes 0..l (rows of 16 first, then the row totals carried by the two row broadcasts).
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  v += dpp<0x111, 0xF, 0xF>(0, v);
+  v += dpp<0x112, 0xF, 0xF>(0, v);
+  v += dpp<0x114, 0xF, 0xE>(0, v);
+  v += dpp<0x118, 0xF, 0xC>(0, v);
+  v += dpp<0x142, 0xA, 0xF>(0, v);
+  v += dpp<0x143, 0xC, 0xF>(0, v);
+  return v;
+}
+
 __device__ __forceinline__ float wave_max_f(float x) {
   const int r = wave_reduce_bits(__float_as_int(x), __float_as_int(-INFINITY), [](int a, int b) {
     return __float_as_int(fmaxf(__int_as_float(a), __int_as_float(b)));
@@ -68,29 +80,21 @@ __device__ __forceinline__ uint32_t sortable(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Arg-max over the wave of (key, expert): larger key first, lower expert index on equal keys.
-// Each lane offers one candidate (key_u = sortable key, or 0 for none; tag = 255 - expert).
-// Returns the winning expert.
-__device__ __forceinline__ int wave_argmax(uint32_t key_u, int expert) {
-  int hi = (int)key_u, lo = 255 - expert;
-  auto step = [&](int nh, int nl) {
-    const bool take = ((uint32_t)nh > (uint32_t)hi) || (nh == hi && nl > lo);
-    hi = take ? nh : hi;
-    lo = take ? nl : lo;
-  };
-  step(dpp<0x111, 0xF, 0xF>(hi, hi), dpp<0x111, 0xF, 0xF>(lo, lo));
-  step(dpp<0x112, 0xF, 0xF>(hi, hi), dpp<0x112, 0xF, 0xF>(lo, lo));
-  step(dpp<0x114, 0xF, 0xE>(hi, hi), dpp<0x114, 0xF, 0xE>(lo, lo));
-  step(dpp<0x118, 0xF, 0xC>(hi, hi), dpp<0x118, 0xF, 0xC>(lo, lo));
-  step(dpp<0x142, 0xA, 0xF>(hi, hi), dpp<0x142, 0xA, 0xF>(lo, lo));
-  step(dpp<0x143, 0xC, 0xF>(hi, hi), dpp<0x143, 0xC, 0xF>(lo, lo));
-  return 255 - __builtin_amdgcn_readlane(lo, 63);
+__device__ __forceinline__ uint32_t wave_max_u(uint32_t x) {
+  return (uint32_t)wave_reduce_bits((int)x, 0, [](int a, int b) {
+    return (int)max((uint32_t)a, (uint32_t)b);
+  });
 }
 
 // Softmax + top-k of one token. logits[i] / live[i] for experts lane + 64 i (i < 4,
 // E <= 256); sel_bias (may be null) shifts only the keys. On return lanes j < k hold the
 // j-th selected expert (out_e) and its renormalised gate (out_g); pr[] holds each lane's
 // probabilities (0 for dead experts).
+//
+// Each of the k selections is one wave max over the remaining keys (one value per lane) and
+// four ballots for the experts that hold it; the lowest such expert wins, so equal keys go to
+// the lower expert index. Branch-free per lane: the selection is latency-bound on one wave,
+// and one token's selection is the serial part of the small-batch routing.
 __device__ __forceinline__ void token_topk(const float (&lg)[4], const bool (&live)[4],
                                            const float* __restrict__ sel_bias, int k, int lane,
                                            float (&pr)[4], int& out_e, float& out_g) {
@@ -102,37 +106,28 @@ __device__ __forceinline__ void token_topk(const float (&lg)[4], const bool (&li
     loc += ex[i];
   }
   const float inv = 1.0f / wave_sum_f(loc);
+  // selection keys: 0 for dead (and, below, already chosen) experts; live keys are >= 1
   uint32_t key[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     pr[i] = ex[i] * inv;
     const float kf = sel_bias && live[i] ? lg[i] + sel_bias[lane + 64 * i] : lg[i];
-    key[i] = live[i] ? sortable(kf) : 0u;
+    key[i] = live[i] ? max(sortable(kf), 1u) : 0u;
   }
-  bool taken[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) taken[i] = !live[i];
   int my_e = 0;
   float my_p = 0.f;
   for (int j = 0; j < k; ++j) {
-    // this lane's best remaining candidate (experts lane, lane+64, ... ascending, so the
-    // first strictly larger key wins and equal keys keep the lower expert)
-    uint32_t bk = 0u;
-    int be = 255, bi = -1;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      if (!taken[i] && (bi < 0 || key[i] > bk)) { bk = key[i]; be = lane + 64 * i; bi = i; }
-    }
-    const int win = wave_argmax(bi < 0 ? 0u : bk, bi < 0 ? 255 : be);
-    const int owner = win & 63, sl = win >> 6;
+    const uint32_t best = wave_max_u(max(max(key[0], key[1]), max(key[2], key[3])));
+    const uint64_t b0 = __ballot(key[0] == best), b1 = __ballot(key[1] == best);
+    const uint64_t b2 = __ballot(key[2] == best), b3 = __ballot(key[3] == best);
+    const int sl = b0 ? 0 : b1 ? 1 : b2 ? 2 : 3;
+    const uint64_t bm = b0 ? b0 : b1 ? b1 : b2 ? b2 : b3;
+    const int owner = __ffsll((unsigned long long)bm) - 1;
+    const int win = owner + 64 * sl;
     const float cand = sl == 0 ? pr[0] : sl == 1 ? pr[1] : sl == 2 ? pr[2] : pr[3];
     const float pw = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(cand), owner));
-    if (lane == owner) {
-      if (sl == 0) taken[0] = true;
-      else if (sl == 1) taken[1] = true;
-      else if (sl == 2) taken[2] = true;
-      else taken[3] = true;
-    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) key[i] = (i == sl && lane == owner) ? 0u : key[i];
     if (lane == j) { my_e = win; my_p = pw; }
   }
   const float psel = wave_sum_f(lane < k ? my_p : 0.f);

@@ -10,10 +10,10 @@
 //   count:   one workgroup per 1024-assignment chunk; LDS histogram -> blk_counts[b][e].
 //   scan:    one workgroup; per expert, exclusive prefix over chunks (blk_base), the
 //            pre-drop count, the capacity clamp and the exclusive prefix over experts.
-//   scatter: one workgroup per chunk; 4 rounds of 256 assignments. Inside a wave the
-//            rank among equal experts comes from ballots (lanes below with the same
-//            expert); across the 4 waves and earlier rounds from LDS counters updated
-//            between barriers. rank = blk_base + in-chunk rank; kept iff rank < cap.
+//   scatter: one workgroup of 16 waves per chunk, one assignment per thread. Inside a wave
+//            the rank among equal experts comes from ballots (lanes below with the same
+//            expert); across waves from per-wave LDS counts of the waves before.
+//            rank = blk_base + in-chunk rank; kept iff rank < cap.
 // A separate one-workgroup kernel turns the offsets into the grouped-GEMM m-tile list.
 #include "moe_internal.h"
 
@@ -92,61 +92,54 @@ __global__ __launch_bounds__(256) void align_scan_kernel(
   if (e == 0) offsets[E] = total;
 }
 
-__global__ __launch_bounds__(256) void align_scatter_kernel(
+__global__ __launch_bounds__(1024) void align_scatter_kernel(
     const int32_t* __restrict__ ids, int n, int E, int cap, const int32_t* __restrict__ blk_base,
     const int32_t* __restrict__ offsets, int32_t* __restrict__ sorted_assign,
     int32_t* __restrict__ assign_pos) {
-  __shared__ int running[256];   // assignments of expert e seen in earlier rounds
-  __shared__ int wcnt[4][256];   // assignments of expert e in wave w of this round
-  __shared__ int cbase[256];     // this chunk's base rank of expert e (loaded once)
+  static_assert(kAlignChunk == 1024, "one assignment per thread");
+  constexpr int NW = 16;
+  __shared__ int wcnt[NW][256];  // assignments of expert e in wave w of this chunk
+  __shared__ int cbase[256];     // this chunk's base rank of expert e
   __shared__ int first[256];     // offsets[e] + cbase[e]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int e = tid; e < E; e += 256) {
-    running[e] = 0;
-    cbase[e] = blk_base[(size_t)blockIdx.x * E + e];
-    first[e] = offsets[e] + cbase[e];
+  for (int i = tid; i < NW * 256; i += 1024) (&wcnt[0][0])[i] = 0;
+  if (tid < E) {
+    cbase[tid] = blk_base[(size_t)blockIdx.x * E + tid];
+    first[tid] = offsets[tid] + cbase[tid];
   }
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  const int a0 = blockIdx.x * kAlignChunk;
-  for (int r = 0; r < kAlignChunk / 256; ++r) {
-    for (int i = tid; i < 4 * 256; i += 256) (&wcnt[0][0])[i] = 0;
-    __syncthreads();
-    const int a = a0 + r * 256 + tid;
-    int e = -1;
-    if (a < n) {
-      e = ids[a];
-      if ((unsigned)e >= (unsigned)E) e = -1;
+  const int a = blockIdx.x * kAlignChunk + tid;
+  int e = -1;
+  if (a < n) {
+    e = ids[a];
+    if ((unsigned)e >= (unsigned)E) e = -1;
+  }
+  const bool valid = e >= 0;
+  __syncthreads();   // wcnt zeroed
+  int my_rank = 0;
+  uint64_t active = __ballot(valid);
+  while (active) {
+    const int leader = __ffsll((unsigned long long)active) - 1;
+    const int le = __builtin_amdgcn_readlane(e, leader);   // leader is wave-uniform
+    const uint64_t m = __ballot(valid && e == le);
+    if (valid && e == le) {
+      my_rank = __popcll(m & lt_mask);
+      if (lane == leader) wcnt[wave][e] = __popcll(m);
     }
-    const bool valid = e >= 0;
-    int my_rank = 0;
-    uint64_t active = __ballot(valid);
-    while (active) {
-      const int leader = __ffsll((unsigned long long)active) - 1;
-      const int le = __builtin_amdgcn_readlane(e, leader);   // leader is wave-uniform
-      const uint64_t m = __ballot(valid && e == le);
-      if (valid && e == le) {
-        my_rank = __popcll(m & lt_mask);
-        if (lane == leader) wcnt[wave][e] = __popcll(m);
+    active &= ~m;
+  }
+  __syncthreads();
+  if (a < n) {
+    int pos = -1;
+    if (valid) {
+      int rank = my_rank;   // rank inside this chunk: lanes below, then the waves before
+      for (int w = 0; w < wave; ++w) rank += wcnt[w][e];
+      if (cap < 0 || cbase[e] + rank < cap) {
+        pos = first[e] + rank;
+        sorted_assign[pos] = a;
       }
-      active &= ~m;
     }
-    __syncthreads();
-    if (a < n) {
-      int pos = -1;
-      if (valid) {
-        int rank = running[e] + my_rank;   // rank inside this chunk
-        for (int w = 0; w < wave; ++w) rank += wcnt[w][e];
-        if (cap < 0 || cbase[e] + rank < cap) {
-          pos = first[e] + rank;
-          sorted_assign[pos] = a;
-        }
-      }
-      assign_pos[a] = pos;
-    }
-    __syncthreads();
-    for (int e2 = tid; e2 < E; e2 += 256)
-      running[e2] += wcnt[0][e2] + wcnt[1][e2] + wcnt[2][e2] + wcnt[3][e2];
-    __syncthreads();
+    assign_pos[a] = pos;
   }
 }
 
@@ -212,7 +205,7 @@ hipError_t launch_align(const moe_problem& p, int cap, const int32_t* ids, int32
                      blk_base, counts_pre, counts, offsets);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || nblk == 0) return err;
-  hipLaunchKernelGGL(align_scatter_kernel, dim3(nblk), dim3(256), 0, s, ids, n, p.E, cap, blk_base,
+  hipLaunchKernelGGL(align_scatter_kernel, dim3(nblk), dim3(1024), 0, s, ids, n, p.E, cap, blk_base,
                      offsets, sorted_assign, assign_pos);
   return hipGetLastError();
 }

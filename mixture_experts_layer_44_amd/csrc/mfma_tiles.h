@@ -25,7 +25,10 @@ struct TileCoord {
 // of kXcdChunk consecutive tiles instead, so that the tiles of the few segments at a capacity
 // limit (L2-bound: their m-tiles share each weight tile) spread over every XCD's L2 rather than
 // landing on the first few XCDs; a chunk keeps an n-tile's m-tiles together. The grid then has
-// whole multiples of 8 * kXcdChunk workgroups (grid_for).
+// whole multiples of 8 * kXcdChunk workgroups (grid_for). The chunks are taken alternately
+// from the front and the back of the tile list, so tiles of the heavily loaded segments and of
+// the lightly loaded ones (weight-streaming, HBM-bound) run side by side rather than one after
+// the other (skewed layer with a capacity limit: 0.87 -> 0.86 ms).
 __device__ __forceinline__ bool tile_coord(const Schedule& sc, int NT, int bn, TileCoord& tc,
                                            int S = 1, int* half = nullptr) {
   const int total = sc.mt_start[sc.G] * NT;
@@ -35,7 +38,10 @@ __device__ __forceinline__ bool tile_coord(const Schedule& sc, int NT, int bn, T
   if (sc.xcd_chunk) {
     const int per = (total * S + 8 * kXcdChunk - 1) / (8 * kXcdChunk) * kXcdChunk;
     if (slot >= per) return false;
-    L = ((slot / kXcdChunk) * 8 + xcd) * kXcdChunk + slot % kXcdChunk;
+    int q = (slot / kXcdChunk) * 8 + xcd;
+    const int Q = (total * S + kXcdChunk - 1) / kXcdChunk;
+    if (q < Q) q = (q & 1) ? Q - 1 - (q >> 1) : (q >> 1);
+    L = q * kXcdChunk + slot % kXcdChunk;
   } else {
     const int per = (total * S + 7) >> 3;
     if (slot >= per) return false;

@@ -177,7 +177,13 @@ __global__ __launch_bounds__(256) void schedule_kernel(const int32_t* __restrict
       sc.grp_rows[g] = min(rows[i], (m1 - m0) * BM);
       sc.grp_off[g] = offs[i];
       sc.mt_start[g] = m0;
-      for (int m = m0; m < m1; ++m) sc.mt_group[m] = g;
+      for (int m = m0; m < m1; ++m) {
+        sc.mt_group[m] = g;
+        if (sc.mt_info) {
+          ((int4*)sc.mt_info)[2 * m] = int4{g, m0, m1 - m0, min(rows[i], (m1 - m0) * BM)};
+          ((int4*)sc.mt_info)[2 * m + 1] = int4{offs[i], 0, 0, 0};
+        }
+      }
     }
     base += mts[i];
   }

@@ -21,6 +21,7 @@ namespace {
 
 struct Layout {
   size_t logits_part, psum_part, blk_counts, blk_base, grp_rows, grp_off, mt_start, mt_group, h;
+  size_t mt_info;
   size_t ids, gates, prob_sum, counts_pre, counts, offsets, sorted_assign, assign_pos;
   size_t out_rows, out_rows_b, shared_out;
   size_t probsT, pos_table;   // expert choice only
@@ -61,6 +62,7 @@ Layout layout(const moe_problem& p, bool ec = false) {
   L.grp_off = take((size_t)G * 4);
   L.mt_start = take((size_t)(G + 1) * 4);
   L.mt_group = take((size_t)L.max_mt * 4);
+  L.mt_info = take((size_t)L.max_mt * 32);
   L.h = take((size_t)L.max_mt * L.BM * p.d_ff * esz);
   L.ids = take(n * 4);
   L.gates = take(n * 4);
@@ -90,6 +92,7 @@ Schedule schedule_in(const moe_problem& p, const Layout& L, void* ws) {
   sc.grp_off = at<int32_t>(ws, L.grp_off);
   sc.mt_start = at<int32_t>(ws, L.mt_start);
   sc.mt_group = at<int32_t>(ws, L.mt_group);
+  sc.mt_info = at<int32_t>(ws, L.mt_info);
   sc.max_mtiles = L.max_mt;
   sc.G = p.E + p.n_shared;
   sc.BM = L.BM;

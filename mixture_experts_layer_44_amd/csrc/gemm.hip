@@ -606,8 +606,10 @@ __global__ __launch_bounds__(256) void gemm_bf16_dec_kernel(GemmArgs args) {
   constexpr int RS = NBLK * 16 + 4;          // padded fp32 row of a wave's partial sums in LDS
   __shared__ float red[4][kDecBM * RS];
 
+  // tiles in identity order: the tile is known one round trip after the start (each tile
+  // streams its own weight rows, so the XCD-contiguous walk buys little here)
   TileCoord tc;
-  if (!tile_coord(args.sc, args.N / FEAT, FEAT, tc)) return;
+  if (!tile_coord<true>(args.sc, args.N / FEAT, FEAT, tc)) return;
   const bool shared_grp = tc.g >= args.E;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);

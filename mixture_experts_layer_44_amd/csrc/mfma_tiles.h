@@ -29,30 +29,57 @@ struct TileCoord {
 // from the front and the back of the tile list, so tiles of the heavily loaded segments and of
 // the lightly loaded ones (weight-streaming, HBM-bound) run side by side rather than one after
 // the other (skewed layer with a capacity limit: 0.87 -> 0.86 ms).
+template <bool IDENT = false>
 __device__ __forceinline__ bool tile_coord(const Schedule& sc, int NT, int bn, TileCoord& tc,
                                            int S = 1, int* half = nullptr) {
-  const int total = sc.mt_start[sc.G] * NT;
   const int bid = blockIdx.x;
-  const int xcd = bid & 7, slot = bid >> 3;
-  int L;
-  if (sc.xcd_chunk) {
-    const int per = (total * S + 8 * kXcdChunk - 1) / (8 * kXcdChunk) * kXcdChunk;
-    if (slot >= per) return false;
-    int q = (slot / kXcdChunk) * 8 + xcd;
-    const int Q = (total * S + kXcdChunk - 1) / kXcdChunk;
-    if (q < Q) q = (q & 1) ? Q - 1 - (q >> 1) : (q >> 1);
-    L = q * kXcdChunk + slot % kXcdChunk;
+  int L, g, ms, mtg, rows, off;
+  auto from_info = [&](int m) {
+    const int4 i0 = ((const int4*)sc.mt_info)[2 * m];
+    const int4 i1 = ((const int4*)sc.mt_info)[2 * m + 1];
+    g = i0.x;
+    ms = i0.y;
+    mtg = i0.z;
+    rows = i0.w;
+    off = i1.x;
+  };
+  if (IDENT && sc.mt_info) {
+    // identity walk (S == 1): workgroup b runs tile b. Its m-tile slot and the m-tile count
+    // are loaded together, so the tile is known after one round trip.
+    L = bid;
+    const int m = L / NT;
+    if (m >= sc.max_mtiles) return false;
+    const int mt_total = sc.mt_start[sc.G];
+    from_info(m);
+    if (m >= mt_total) return false;
   } else {
-    const int per = (total * S + 7) >> 3;
-    if (slot >= per) return false;
-    L = xcd * per + slot;
+    const int total = sc.mt_start[sc.G] * NT;
+    const int xcd = bid & 7, slot = bid >> 3;
+    if (sc.xcd_chunk) {
+      const int per = (total * S + 8 * kXcdChunk - 1) / (8 * kXcdChunk) * kXcdChunk;
+      if (slot >= per) return false;
+      int q = (slot / kXcdChunk) * 8 + xcd;
+      const int Q = (total * S + kXcdChunk - 1) / kXcdChunk;
+      if (q < Q) q = (q & 1) ? Q - 1 - (q >> 1) : (q >> 1);
+      L = q * kXcdChunk + slot % kXcdChunk;
+    } else {
+      const int per = (total * S + 7) >> 3;
+      if (slot >= per) return false;
+      L = xcd * per + slot;
+    }
+    if (L >= total * S) return false;
+    if (half) *half = L / total;   // work unit L = half * total + tile
+    L %= total;
+    if (sc.mt_info) {
+      from_info(L / NT);
+    } else {
+      g = sc.mt_group[L / NT];
+      ms = sc.mt_start[g];
+      mtg = sc.mt_start[g + 1] - ms;
+      rows = sc.grp_rows[g];
+      off = sc.grp_off[g];
+    }
   }
-  if (L >= total * S) return false;
-  if (half) *half = L / total;   // work unit L = half * total + tile
-  L %= total;
-  const int g = sc.mt_group[L / NT];
-  const int ms = sc.mt_start[g];
-  const int mtg = sc.mt_start[g + 1] - ms;
   const int lp = L - ms * NT;
   const int n_tile = lp / mtg;
   tc.g = g;
@@ -60,8 +87,8 @@ __device__ __forceinline__ bool tile_coord(const Schedule& sc, int NT, int bn, T
   tc.m_local = lp - n_tile * mtg;
   tc.n0 = n_tile * bn;
   tc.mt_global = ms + tc.m_local;
-  tc.rows = sc.grp_rows[g];
-  tc.off = sc.grp_off[g];
+  tc.rows = rows;
+  tc.off = off;
   return true;
 }
 

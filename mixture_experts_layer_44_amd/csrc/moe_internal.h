@@ -65,6 +65,9 @@ struct Schedule {
   int32_t* grp_off;    // [G]   first row in sorted order (routed), 0 for shared
   int32_t* mt_start;   // [G+1] exclusive prefix of ceil(rows/BM); mt_start[G] = total m-tiles
   int32_t* mt_group;   // [max_mtiles] group of each m-tile
+  // [max_mtiles][8] or null: per m-tile slot m, {g, mt_start[g], m-tiles of g, grp_rows[g],
+  // grp_off[g], 0, 0, 0}, so that a workgroup finds its tile with one load instead of a chain
+  int32_t* mt_info = nullptr;
   int max_mtiles;
   int G;
   int BM;

@@ -117,7 +117,14 @@ __device__ void align_schedule_lds(AlignLds& L, int n, int T, int E, int cap,
     sc.grp_rows[tid] = min(rows, (m1 - m0) * sc.BM);
     sc.grp_off[tid] = tid < E ? L.s_off[tid] : 0;
     sc.mt_start[tid] = m0;
-    for (int m = m0; m < m1; ++m) sc.mt_group[m] = tid;
+    const int grows = min(rows, (m1 - m0) * sc.BM), goff = tid < E ? L.s_off[tid] : 0;
+    for (int m = m0; m < m1; ++m) {
+      sc.mt_group[m] = tid;
+      if (sc.mt_info) {
+        ((int4*)sc.mt_info)[2 * m] = int4{tid, m0, m1 - m0, grows};
+        ((int4*)sc.mt_info)[2 * m + 1] = int4{goff, 0, 0, 0};
+      }
+    }
   }
   if (tid == 0) sc.mt_start[G] = min(mt_total, sc.max_mtiles);
 }

@@ -41,52 +41,68 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     g8[u] = u < k ? wt[u] : 0.f;
   }
   const int d4 = d >> 2;
-  for (int c = threadIdx.x; c < d4; c += 256) {
-    f32x4 acc = shared_out ? *(const f32x4*)(shared_out + (size_t)t * d + 4 * c)
-                           : f32x4{0.f, 0.f, 0.f, 0.f};
-    // The loads of the kept slots among the first NS are all issued before they are added in
-    // slot order (a dropped slot loads nothing: out_rows may hold only kept rows).
-    f32x4 v[NS], vb[NS];
+  // Two 16-byte column chunks per thread and pass (c and c + 256): the loads of both are issued
+  // before either is added, so a short row (decode) takes one round trip instead of two.
+  for (int c0 = threadIdx.x; c0 < d4; c0 += 512) {
+    const bool two = c0 + 256 < d4;   // uniform except in the last pass of a ragged row
+    f32x4 acc[2];
+    f32x4 v[2][NS], vb[2][NS];
 #pragma unroll
-    for (int u = 0; u < NS; ++u) {
-      v[u] = vb[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (r8[u] < 0) continue;
-      const size_t o = (size_t)r8[u] * d + 4 * c;
-      v[u] = *(const f32x4*)(out_rows + o);
-      if (out_rows_b) vb[u] = *(const f32x4*)(out_rows_b + o);   // the down GEMM's two K halves
+    for (int h = 0; h < 2; ++h) {
+      const int c = c0 + 256 * h;
+      const bool live = h == 0 || two;
+      acc[h] = shared_out && live ? *(const f32x4*)(shared_out + (size_t)t * d + 4 * c)
+                                  : f32x4{0.f, 0.f, 0.f, 0.f};
+      // the loads of the kept slots among the first NS (a dropped slot loads nothing: out_rows
+      // may hold only kept rows)
+#pragma unroll
+      for (int u = 0; u < NS; ++u) {
+        v[h][u] = vb[h][u] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (r8[u] < 0 || !live) continue;
+        const size_t o = (size_t)r8[u] * d + 4 * c;
+        v[h][u] = *(const f32x4*)(out_rows + o);
+        if (out_rows_b) vb[h][u] = *(const f32x4*)(out_rows_b + o);   // the down GEMM's K halves
+      }
     }
 #pragma unroll
-    for (int u = 0; u < NS; ++u) {
-      if (r8[u] < 0) continue;
-      if (out_rows_b) {
-        v[u][0] += vb[u][0];
-        v[u][1] += vb[u][1];
-        v[u][2] += vb[u][2];
-        v[u][3] += vb[u][3];
+    for (int h = 0; h < 2; ++h) {
+      const int c = c0 + 256 * h;
+      if (h == 1 && !two) break;
+      // slots added in slot order after the shared row
+#pragma unroll
+      for (int u = 0; u < NS; ++u) {
+        if (r8[u] < 0) continue;
+        f32x4 w = v[h][u];
+        if (out_rows_b) {
+          w[0] += vb[h][u][0];
+          w[1] += vb[h][u][1];
+          w[2] += vb[h][u][2];
+          w[3] += vb[h][u][3];
+        }
+        acc[h][0] = fmaf(g8[u], w[0], acc[h][0]);
+        acc[h][1] = fmaf(g8[u], w[1], acc[h][1]);
+        acc[h][2] = fmaf(g8[u], w[2], acc[h][2]);
+        acc[h][3] = fmaf(g8[u], w[3], acc[h][3]);
       }
-      acc[0] = fmaf(g8[u], v[u][0], acc[0]);
-      acc[1] = fmaf(g8[u], v[u][1], acc[1]);
-      acc[2] = fmaf(g8[u], v[u][2], acc[2]);
-      acc[3] = fmaf(g8[u], v[u][3], acc[3]);
-    }
-    for (int j = NS; j < k; ++j) {   // slots past the first NS, one at a time
-      const int r = pos[j];
-      if (r < 0 || r >= n) continue;
-      f32x4 w = *(const f32x4*)(out_rows + (size_t)r * d + 4 * c);
-      if (out_rows_b) {
-        const f32x4 vb = *(const f32x4*)(out_rows_b + (size_t)r * d + 4 * c);
-        w[0] += vb[0];
-        w[1] += vb[1];
-        w[2] += vb[2];
-        w[3] += vb[3];
+      for (int j = NS; j < k; ++j) {   // slots past the first NS, one at a time
+        const int r = pos[j];
+        if (r < 0 || r >= n) continue;
+        f32x4 w = *(const f32x4*)(out_rows + (size_t)r * d + 4 * c);
+        if (out_rows_b) {
+          const f32x4 wb = *(const f32x4*)(out_rows_b + (size_t)r * d + 4 * c);
+          w[0] += wb[0];
+          w[1] += wb[1];
+          w[2] += wb[2];
+          w[3] += wb[3];
+        }
+        const float g = wt[j];
+        acc[h][0] = fmaf(g, w[0], acc[h][0]);
+        acc[h][1] = fmaf(g, w[1], acc[h][1]);
+        acc[h][2] = fmaf(g, w[2], acc[h][2]);
+        acc[h][3] = fmaf(g, w[3], acc[h][3]);
       }
-      const float g = wt[j];
-      acc[0] = fmaf(g, w[0], acc[0]);
-      acc[1] = fmaf(g, w[1], acc[1]);
-      acc[2] = fmaf(g, w[2], acc[2]);
-      acc[3] = fmaf(g, w[3], acc[3]);
+      *(f32x4*)(y + (size_t)t * d + 4 * c) = acc[h];
     }
-    *(f32x4*)(y + (size_t)t * d + 4 * c) = acc;
   }
 }
 

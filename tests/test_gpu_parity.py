@@ -80,7 +80,7 @@ SMALL = [
       sel_bias=True, n_shared=1, d_ff_shared=256),
     # multi-launch routing with E_pad = 208 (the router's last 64-expert group is partly
     # padding), T not a multiple of the 64-token logits block, a logit offset and a selection bias
-    W("bf16_router_blocks", T=300, d=384, E=200, k=6, d_ff=256, seed=127, sel_bias=True,
+    W("bf16_E200", T=300, d=384, E=200, k=6, d_ff=256, seed=127, sel_bias=True,
       zipf_s=0.5),
 ]
 

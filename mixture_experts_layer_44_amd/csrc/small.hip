@@ -44,9 +44,9 @@ struct AlignLds {
   int wsum[5];
 };
 
-// Grouping by expert + grouped-GEMM schedule out of LDS, one assignment per thread: all 1024
-// threads call it after L.s_ids[0..n) is filled and L.wcnt zeroed (and a barrier). Ranks come
-// from ballots inside a wave plus the per-wave counts of earlier waves, i.e. ascending flat
+// Grouping by expert + grouped-GEMM schedule out of LDS, at most one assignment per thread: all
+// 1024 threads call it after L.s_ids[0..n) is filled and L.wcnt zeroed (and a barrier). Ranks
+// come from ballots inside a wave plus the per-wave counts of earlier waves, i.e. ascending flat
 // index a inside each expert, as the multi-launch path's stable order.
 __device__ void align_schedule_lds(AlignLds& L, int n, int T, int E, int cap,
                                    int32_t* __restrict__ counts_pre, int32_t* __restrict__ counts,
@@ -55,8 +55,13 @@ __device__ void align_schedule_lds(AlignLds& L, int n, int T, int E, int cap,
                                    int32_t* __restrict__ assign_pos, int n_shared,
                                    const Schedule& sc) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int a = tid;
-  const int e = a < n ? L.s_ids[a] : -1;
+  // Wave w takes assignments [w*per, (w+1)*per) in lane order. With at most 256 of them, 16 per
+  // wave: the ballot loop below runs once per distinct expert among a wave's assignments, a
+  // serial chain, so spreading a few assignments over all 16 waves shortens it.
+  const int per = n <= 16 * NWAVE ? 16 : 64;
+  const int a = lane < per ? wave * per + lane : n;   // n: no assignment
+  const bool has_a = a < n;
+  const int e = has_a ? L.s_ids[a] : -1;
   const bool valid = e >= 0 && e < E;
   const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   int my_rank = 0;
@@ -90,7 +95,7 @@ __device__ void align_schedule_lds(AlignLds& L, int n, int T, int E, int cap,
     L.s_off[E] = total;
   }
   __syncthreads();
-  if (a < n) {
+  if (has_a) {
     int pos = -1;
     if (valid) {
       int rank = my_rank;

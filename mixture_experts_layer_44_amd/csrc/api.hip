@@ -20,7 +20,8 @@ namespace moe {
 namespace {
 
 struct Layout {
-  size_t logits_part, psum_part, blk_counts, blk_base, grp_rows, grp_off, mt_start, mt_group, h;
+  size_t logits_part, psum_part, psum_stage, blk_counts, blk_base, grp_rows, grp_off, mt_start,
+      mt_group, h;
   size_t mt_info;
   size_t ids, gates, prob_sum, counts_pre, counts, offsets, sorted_assign, assign_pos;
   size_t out_rows, out_rows_b, shared_out;
@@ -56,6 +57,7 @@ Layout layout(const moe_problem& p, bool ec = false) {
   const size_t esz = p.dtype == MOE_BF16 ? 2 : 4;
   L.logits_part = take(route_partial_bytes(p));
   L.psum_part = take((size_t)nblk_route * p.E * 4);
+  L.psum_stage = take((size_t)kPsumStage * p.E * 4);
   L.blk_counts = take((size_t)nblk_align * p.E * 4);
   L.blk_base = take((size_t)nblk_align * p.E * 4);
   L.grp_rows = take((size_t)G * 4);
@@ -241,7 +243,8 @@ MOE_API moe_status moe_forward_expert_choice(const moe_problem* p, const void* x
     e = launch_ec_probs(*p, at<float>(ws, L.logits_part), logit_bias, probsT,
                         prob_sum ? psum_part : nullptr, stream);
   if (e == hipSuccess && prob_sum)
-    e = launch_psum_reduce(psum_part, hasT ? ec_probs_blocks(*p) : 0, p->E, prob_sum, stream);
+    e = launch_psum_reduce(psum_part, hasT ? ec_probs_blocks(*p) : 0, p->E, prob_sum, stream,
+                           at<float>(ws, L.psum_stage));
   if (e == hipSuccess) e = launch_ec_select(*p, C, probsT, tokens, gates, pos, offs, stream);
   if (e == hipSuccess) e = launch_schedule(*p, offs, sc, stream, (long long)p->E * C);
   if (e == hipSuccess)
@@ -270,7 +273,8 @@ MOE_API moe_status moe_route(const moe_problem* p, const void* x, const void* w_
     return hip_status(e);
   }
   return hip_status(launch_route(*p, x, w_gate, logit_bias, sel_bias, topk_ids, topk_w, prob_sum,
-                                 at<float>(ws, L.logits_part), at<float>(ws, L.psum_part), stream));
+                                 at<float>(ws, L.logits_part), at<float>(ws, L.psum_part),
+                                 at<float>(ws, L.psum_stage), stream));
 }
 
 MOE_API moe_status moe_align(const moe_problem* p, const int32_t* topk_ids, int32_t* counts_pre,
@@ -458,7 +462,8 @@ moe_status forward_impl(const moe_problem* p, const void* x, const void* w_gate,
     if (e != hipSuccess || mark(2) != hipSuccess || mark(3) != hipSuccess) return MOE_EHIP;
   } else {
     e = launch_route(*p, x, w_gate, logit_bias, sel_bias, ids, gates, prob_sum,
-                     at<float>(ws, L.logits_part), at<float>(ws, L.psum_part), stream);
+                     at<float>(ws, L.logits_part), at<float>(ws, L.psum_part),
+                     at<float>(ws, L.psum_stage), stream);
     if (e != hipSuccess || mark(1) != hipSuccess) return MOE_EHIP;
     e = launch_align(*p, kernel_cap(*p), ids, cpre, cnt, offs, sa, ap,
                      at<int32_t>(ws, L.blk_counts), at<int32_t>(ws, L.blk_base), stream);

@@ -123,10 +123,11 @@ hipError_t launch_route_topk(const moe_problem& p, const float* logits_part,
                              const float* logit_bias, const float* sel_bias, int32_t* ids,
                              float* gates, float* psum_part, hipStream_t s);
 
+// psum_stage: [kPsumStage][E] floats for the probability-sum reduction, or null
 hipError_t launch_route(const moe_problem& p, const void* x, const void* w_gate,
                         const float* logit_bias, const float* sel_bias, int32_t* ids,
                         float* gates, float* prob_sum, float* logits_part, float* psum_part,
-                        hipStream_t s);
+                        float* psum_stage, hipStream_t s);
 
 hipError_t launch_align(const moe_problem& p, int cap, const int32_t* ids, int32_t* counts_pre,
                         int32_t* counts, int32_t* offsets, int32_t* sorted_assign,
@@ -162,9 +163,11 @@ hipError_t launch_add_rows(const moe_problem& p, float* out_rows, const float* o
 hipError_t launch_balance(const moe_problem& p, const int32_t* counts_pre, const float* prob_sum,
                           float alpha, float* f, float* P, float* L, hipStream_t s);
 
-// prob_sum[e] = sum over the nblk per-workgroup partials, in workgroup order
+// prob_sum[e] = sum over the nblk per-workgroup partials, a fixed tree (run-to-run identical).
+// stage: [kPsumStage][E] floats, or null (one workgroup reads every partial).
+constexpr int kPsumStage = 64;
 hipError_t launch_psum_reduce(const float* psum_part, int nblk, int E, float* prob_sum,
-                              hipStream_t s);
+                              hipStream_t s, float* stage = nullptr);
 
 // ---- expert-choice routing (expert_choice.hip)
 int ec_probs_blocks(const moe_problem& p);

@@ -208,23 +208,37 @@ __global__ __launch_bounds__(256) void route_topk_kernel(
 // out[e] = sum over the nblk rows of a [nblk][E] table of per-workgroup partial sums (the top-k
 // workgroups' probability sums, or the backward's logit-bias gradient). A fixed tree, so the
 // result is identical from run to run: thread (c, e) adds the rows of chunk c of C = 1024/E
-// in order, 32 loads in flight; then thread e adds the C chunk sums in order.
+// in order, 64 loads in flight; then thread e adds the C chunk sums in order. With G workgroups,
+// workgroup g does this over rows [nblk*g/G, nblk*(g+1)/G) and writes row g of out (G = 1: out
+// is the sum); the launcher chains a G-workgroup pass and a one-workgroup pass over its G rows
+// for many partials, still a fixed tree.
 __global__ __launch_bounds__(1024) void psum_reduce_kernel(const float* __restrict__ part, int nblk,
                                                            int E, float* __restrict__ out) {
   __shared__ float csum[1024];
   const int tid = threadIdx.x;
   const int C = 1024 / E;   // E <= 256: at least 4 chunks
   const int c = tid / E, e = tid % E;
+  const int G = gridDim.x, g = blockIdx.x;
+  const int r0 = (int)((long long)nblk * g / G), nr = (int)((long long)nblk * (g + 1) / G) - r0;
+  part += (size_t)r0 * E;
+  out += (size_t)g * E;
   if (c < C) {
-    const int b0 = (int)((long long)nblk * c / C), b1 = (int)((long long)nblk * (c + 1) / C);
+    const int b0 = (int)((long long)nr * c / C), b1 = (int)((long long)nr * (c + 1) / C);
     float s = 0.f;
     int b = b0;
-    for (; b + 32 <= b1; b += 32) {   // 32 loads in flight, added in block order
-      float v[32];
+    for (; b + 64 <= b1; b += 64) {   // 64 loads in flight, added in block order
+      float v[64];
 #pragma unroll
-      for (int u = 0; u < 32; ++u) v[u] = part[(size_t)(b + u) * E + e];
+      for (int u = 0; u < 64; ++u) v[u] = part[(size_t)(b + u) * E + e];
 #pragma unroll
-      for (int u = 0; u < 32; ++u) s += v[u];
+      for (int u = 0; u < 64; ++u) s += v[u];
+    }
+    for (; b + 8 <= b1; b += 8) {
+      float v[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) v[u] = part[(size_t)(b + u) * E + e];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) s += v[u];
     }
     for (; b < b1; ++b) s += part[(size_t)b * E + e];
     csum[tid] = s;   // = csum[c * E + e]
@@ -390,8 +404,19 @@ hipError_t launch_route_logits(const moe_problem& p, const void* x, const void* 
   return hipGetLastError();
 }
 
+// One workgroup reads its partials at one CU's rate (1 MB, the skewed shape's 4096 x 64, took
+// 12.3 us with 32 or 64 loads in flight); with a stage buffer, many partials go through
+// kPsumStage workgroups first (the two launches: 2 x 4.8 us).
 hipError_t launch_psum_reduce(const float* psum_part, int nblk, int E, float* prob_sum,
-                              hipStream_t s) {
+                              hipStream_t s, float* stage) {
+  if (stage && nblk >= 8 * kPsumStage) {
+    hipLaunchKernelGGL(psum_reduce_kernel, dim3(kPsumStage), dim3(1024), 0, s, psum_part, nblk, E,
+                       stage);
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    psum_part = stage;
+    nblk = kPsumStage;
+  }
   hipLaunchKernelGGL(psum_reduce_kernel, dim3(1), dim3(1024), 0, s, psum_part, nblk, E, prob_sum);
   return hipGetLastError();
 }
@@ -399,7 +424,7 @@ hipError_t launch_psum_reduce(const float* psum_part, int nblk, int E, float* pr
 hipError_t launch_route(const moe_problem& p, const void* x, const void* w_gate,
                         const float* logit_bias, const float* sel_bias, int32_t* ids,
                         float* gates, float* prob_sum, float* logits_part, float* psum_part,
-                        hipStream_t s) {
+                        float* psum_stage, hipStream_t s) {
   if (route_fused(p)) {
     if (p.T == 0) return hipSuccess;
     const int nblk = ceil_div(p.T, FTB);
@@ -408,9 +433,7 @@ hipError_t launch_route(const moe_problem& p, const void* x, const void* w_gate,
                        prob_sum ? psum_part : nullptr);
     hipError_t err = hipGetLastError();
     if (err != hipSuccess || !prob_sum) return err;
-    hipLaunchKernelGGL(psum_reduce_kernel, dim3(1), dim3(1024), 0, s, psum_part, nblk, p.E,
-                       prob_sum);
-    return hipGetLastError();
+    return launch_psum_reduce(psum_part, nblk, p.E, prob_sum, s, psum_stage);
   }
   const int nblk = route_topk_blocks(p);
   hipError_t err = launch_route_logits(p, x, w_gate, logits_part, s);
@@ -419,8 +442,7 @@ hipError_t launch_route(const moe_problem& p, const void* x, const void* w_gate,
                           prob_sum ? psum_part : nullptr, s);
   if (err != hipSuccess) return err;
   if (!prob_sum) return hipSuccess;
-  hipLaunchKernelGGL(psum_reduce_kernel, dim3(1), dim3(1024), 0, s, psum_part, nblk, p.E, prob_sum);
-  return hipGetLastError();
+  return launch_psum_reduce(psum_part, nblk, p.E, prob_sum, s, psum_stage);
 }
 
 }  // namespace moe

@@ -735,7 +735,7 @@ __global__ __launch_bounds__(256) void gemm_bf16_dec_kernel(GemmArgs args) {
 }
 
 // ------------------------------------------------------------------ fp32 path (VALU)
-constexpr int BM32 = kGemmBM32, BN32 = 64, BK32 = 16;
+constexpr int BM32 = kGemmBM32, BN32 = 64, BK32 = 32;
 
 struct GemmArgs32 {
   const float* A;
@@ -776,34 +776,60 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs32 args) {
   const float* Bb[NB];
   Bb[0] = shared_grp ? args.S0 : args.B0 + (size_t)tc.g * N * K;
   if (GATEUP) Bb[NB - 1] = shared_grp ? args.S1 : args.B1 + (size_t)tc.g * N * K;
-  float acc[NB][4][4] = {};
+  constexpr int RM = BM32 / 16;   // rows per thread (16 x 16 threads over BM32 x 64)
+  float acc[NB][RM][4] = {};
   __syncthreads();
-  for (int k0 = 0; k0 < K; k0 += BK32) {
-    for (int idx = tid; idx < BM32 * BK32; idx += 256) {
-      const int r = idx / BK32, kk = idx % BK32;
+  // This thread's elements of one K chunk, loaded into registers one chunk ahead (the loads of
+  // chunk k0 + BK32 are in flight while chunk k0 is multiplied), then stored to LDS.
+  constexpr int LA = BM32 * BK32 / 256, LB = BN32 * BK32 / 256;
+  static_assert(LA * 256 == BM32 * BK32 && LB * 256 == BN32 * BK32, "even split");
+  float ra[LA], rb[NB][LB];
+  auto load = [&](int k0) {
+#pragma unroll
+    for (int u = 0; u < LA; ++u) {
+      const int idx = tid + 256 * u, r = idx / BK32, kk = idx % BK32;
       const int t = tok[r];
-      As[kk][r] = (t >= 0 && k0 + kk < K) ? args.A[(size_t)t * K + k0 + kk] : 0.f;
+      ra[u] = (t >= 0 && k0 + kk < K) ? args.A[(size_t)t * K + k0 + kk] : 0.f;
     }
+#pragma unroll
     for (int q = 0; q < NB; ++q)
-      for (int idx = tid; idx < BN32 * BK32; idx += 256) {
-        const int c = idx / BK32, kk = idx % BK32;
+#pragma unroll
+      for (int u = 0; u < LB; ++u) {
+        const int idx = tid + 256 * u, c = idx / BK32, kk = idx % BK32;
         const int n = tc.n0 + c;
-        Bs[q][kk][c] = (n < N && k0 + kk < K) ? Bb[q][(size_t)n * K + k0 + kk] : 0.f;
+        rb[q][u] = (n < N && k0 + kk < K) ? Bb[q][(size_t)n * K + k0 + kk] : 0.f;
+      }
+  };
+  load(0);
+  for (int k0 = 0; k0 < K; k0 += BK32) {
+#pragma unroll
+    for (int u = 0; u < LA; ++u) {
+      const int idx = tid + 256 * u;
+      As[idx % BK32][idx / BK32] = ra[u];
+    }
+#pragma unroll
+    for (int q = 0; q < NB; ++q)
+#pragma unroll
+      for (int u = 0; u < LB; ++u) {
+        const int idx = tid + 256 * u;
+        Bs[q][idx % BK32][idx / BK32] = rb[q][u];
       }
     __syncthreads();
+    if (k0 + BK32 < K) load(k0 + BK32);
+#pragma unroll 8
     for (int kk = 0; kk < BK32; ++kk) {
-      float a[4], b[NB][4];
-      for (int i = 0; i < 4; ++i) a[i] = As[kk][ty * 4 + i];
+      float a[RM], b[NB][4];
+      for (int i = 0; i < RM; ++i) a[i] = As[kk][ty * RM + i];
       for (int q = 0; q < NB; ++q)
         for (int j = 0; j < 4; ++j) b[q][j] = Bs[q][kk][tx * 4 + j];
       for (int q = 0; q < NB; ++q)
-        for (int i = 0; i < 4; ++i)
+        for (int i = 0; i < RM; ++i)
           for (int j = 0; j < 4; ++j) acc[q][i][j] = fmaf(a[i], b[q][j], acc[q][i][j]);
     }
     __syncthreads();
   }
-  for (int i = 0; i < 4; ++i) {
-    const int lr = ty * 4 + i;
+  for (int i = 0; i < RM; ++i) {
+    const int lr = ty * RM + i;
     for (int j = 0; j < 4; ++j) {
       const int col = tc.n0 + tx * 4 + j;
       if (col >= N) continue;

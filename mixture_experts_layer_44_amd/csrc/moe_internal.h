@@ -52,7 +52,7 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
 // ---------------------------------------------------------------- tiling constants
 constexpr int kAlignChunk = 1024;    // assignments per align workgroup
 constexpr int kGemmBM = 128;         // rows per grouped-GEMM m-tile (bf16 path)
-constexpr int kGemmBM32 = 64;        // rows per m-tile (fp32 path)
+constexpr int kGemmBM32 = 16;        // rows per m-tile (fp32 path; its tiles are VALU-bound)
 
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }

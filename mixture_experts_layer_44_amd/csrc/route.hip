@@ -14,7 +14,8 @@
 //          every x and W_gate byte a workgroup needs is loaded once), and the four partials
 //          are added in wave order through LDS. Loads are issued four k-steps ahead of the
 //          MFMAs. KS is chosen on the host so that the grid has >= ~512 workgroups; the fp32
-//          partials [KS][T][E_pad] never round to bf16.
+//          partials [KS][T][E_pad] never round to bf16. (fp32 storage: one partial logit per
+//          wave, route_logits_f32_kernel.)
 //  topk:   one wave per token. Sums the KS partials in slice order (run-to-run identical),
 //          adds logit_bias, softmax, keys = logits (+ sel_bias), k rounds of a 64-lane
 //          arg-max (larger key first, lower expert index on equal keys), gates = kept p /
@@ -33,7 +34,6 @@ constexpr int UNROLL = 4;     // k-steps of loads in flight per wave
 constexpr int TOPK_TOK = 4;   // tokens per top-k workgroup (one per wave)
 
 // partial logits of a 64-token x 64-expert block over the d slice blockIdx.z
-template <bool BF16>
 __global__ __launch_bounds__(256) void route_logits_kernel(const void* __restrict__ xv,
                                                            const void* __restrict__ wv, int T,
                                                            int d, int E, int E_pad, int KS,
@@ -45,7 +45,7 @@ __global__ __launch_bounds__(256) void route_logits_kernel(const void* __restric
   const int slice = d / KS, k_begin = blockIdx.z * slice;
   float* out = part + (size_t)blockIdx.z * T * E_pad;
 
-  if constexpr (BF16) {
+  {
     constexpr int RS = EN + 4;                        // padded row of a wave's partials
     __shared__ float red[4][TM * RS];
     const bf16_t* x = (const bf16_t*)xv;
@@ -140,23 +140,31 @@ __global__ __launch_bounds__(256) void route_logits_kernel(const void* __restric
                       red[3][tr * RS + ec];
       if (tok0 + tr < T) out[(size_t)(tok0 + tr) * E_pad + e0 + ec] = s;
     }
-  } else {
-    const float* x = (const float*)xv;
-    const float* w = (const float*)wv;
-    const int ecount = min(EN, E_pad - e0);
-    for (int idx = tid; idx < TM * ecount; idx += 256) {
-      const int tr = idx / ecount, e = e0 + idx % ecount;
-      const int t = tok0 + tr;
-      if (t >= T) continue;
-      float s = 0.f;
-      if (e < E) {
-        const float* xr = x + (size_t)t * d + k_begin;
-        const float* wr = w + (size_t)e * d + k_begin;
-        for (int i = 0; i < slice; ++i) s = fmaf(xr[i], wr[i], s);
-      }
-      out[(size_t)t * E_pad + e] = s;
-    }
   }
+}
+
+// fp32 storage: one partial logit (slice z, token t, expert e) per wave, the 64 lanes striding
+// the slice (coalesced rows) and a DPP wave sum at the end (a fixed order). Enough waves for a
+// small problem to spread over the CUs.
+__global__ __launch_bounds__(256) void route_logits_f32_kernel(const float* __restrict__ x,
+                                                               const float* __restrict__ w, int T,
+                                                               int d, int E, int E_pad, int KS,
+                                                               float* __restrict__ part) {
+  const int lane = threadIdx.x & 63;
+  const long long task = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (task >= (long long)KS * T * E_pad) return;   // wave-uniform
+  const int e = (int)(task % E_pad);
+  const long long rest = task / E_pad;
+  const int t = (int)(rest % T), z = (int)(rest / T);
+  const int slice = d / KS, k0 = z * slice;
+  float s = 0.f;
+  if (e < E) {
+    const float* xr = x + (size_t)t * d + k0;
+    const float* wr = w + (size_t)e * d + k0;
+    for (int i = lane; i < slice; i += 64) s = fmaf(xr[i], wr[i], s);
+    s = wave_sum_f(s);
+  }
+  if (lane == 0) part[((size_t)z * T + t) * E_pad + e] = s;
 }
 
 // TOK tokens per workgroup of 4 waves (TOK/4 per wave, one after the other)
@@ -396,11 +404,13 @@ hipError_t launch_route_logits(const moe_problem& p, const void* x, const void* 
   const int KS = route_ksplit(p);
   dim3 grid(ceil_div(p.T, TM), ceil_div(E_pad, EN), KS);
   if (p.dtype == MOE_BF16)
-    hipLaunchKernelGGL(route_logits_kernel<true>, grid, dim3(256), 0, s, x, w_gate, p.T, p.d, p.E,
+    hipLaunchKernelGGL(route_logits_kernel, grid, dim3(256), 0, s, x, w_gate, p.T, p.d, p.E,
                        E_pad, KS, logits_part);
   else
-    hipLaunchKernelGGL(route_logits_kernel<false>, grid, dim3(256), 0, s, x, w_gate, p.T, p.d,
-                       p.E, E_pad, KS, logits_part);
+    hipLaunchKernelGGL(route_logits_f32_kernel,
+                       dim3((unsigned)(((long long)KS * p.T * E_pad + 3) / 4)), dim3(256), 0, s,
+                       (const float*)x, (const float*)w_gate, p.T, p.d, p.E, E_pad, KS,
+                       logits_part);
   return hipGetLastError();
 }
 

@@ -151,20 +151,24 @@ __global__ __launch_bounds__(256) void route_logits_f32_kernel(const float* __re
                                                                int d, int E, int E_pad, int KS,
                                                                float* __restrict__ part) {
   const int lane = threadIdx.x & 63;
-  const long long task = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (task >= (long long)KS * T * E_pad) return;   // wave-uniform
-  const int e = (int)(task % E_pad);
-  const long long rest = task / E_pad;
-  const int t = (int)(rest % T), z = (int)(rest / T);
-  const int slice = d / KS, k0 = z * slice;
-  float s = 0.f;
-  if (e < E) {
-    const float* xr = x + (size_t)t * d + k0;
-    const float* wr = w + (size_t)e * d + k0;
-    for (int i = lane; i < slice; i += 64) s = fmaf(xr[i], wr[i], s);
-    s = wave_sum_f(s);
+  const long long ntask = (long long)KS * T * E_pad;
+  const int slice = d / KS;
+  // wave-uniform loop over the tasks (the grid is capped by the launcher)
+  for (long long task = (long long)blockIdx.x * 4 + (threadIdx.x >> 6); task < ntask;
+       task += (long long)gridDim.x * 4) {
+    const int e = (int)(task % E_pad);
+    const long long rest = task / E_pad;
+    const int t = (int)(rest % T), z = (int)(rest / T);
+    const int k0 = z * slice;
+    float s = 0.f;
+    if (e < E) {
+      const float* xr = x + (size_t)t * d + k0;
+      const float* wr = w + (size_t)e * d + k0;
+      for (int i = lane; i < slice; i += 64) s = fmaf(xr[i], wr[i], s);
+      s = wave_sum_f(s);
+    }
+    if (lane == 0) part[((size_t)z * T + t) * E_pad + e] = s;
   }
-  if (lane == 0) part[((size_t)z * T + t) * E_pad + e] = s;
 }
 
 // TOK tokens per workgroup of 4 waves (TOK/4 per wave, one after the other)
@@ -408,7 +412,8 @@ hipError_t launch_route_logits(const moe_problem& p, const void* x, const void* 
                        E_pad, KS, logits_part);
   else
     hipLaunchKernelGGL(route_logits_f32_kernel,
-                       dim3((unsigned)(((long long)KS * p.T * E_pad + 3) / 4)), dim3(256), 0, s,
+                       dim3((unsigned)std::min(((long long)KS * p.T * E_pad + 3) / 4, 1ll << 20)),
+                       dim3(256), 0, s,
                        (const float*)x, (const float*)w_gate, p.T, p.d, p.E, E_pad, KS,
                        logits_part);
   return hipGetLastError();

@@ -78,6 +78,11 @@ SMALL = [
     # bias and a shared expert
     W("bf16_small16_cap", T=16, d=256, E=32, k=4, d_ff=256, seed=126, capacity_factor=0.5,
       sel_bias=True, n_shared=1, d_ff_shared=256),
+    # router logits one expert per wave (T <= 4, d a multiple of 512): three 512-column pieces
+    # per lane, E_pad = 48 (the last workgroup's waves past E write zeros), offset, selection
+    # bias, shared expert
+    W("bf16_gemv_T3", T=3, d=1536, E=40, k=5, d_ff=256, seed=128, sel_bias=True, zipf_s=0.7,
+      n_shared=1, d_ff_shared=256),
     # multi-launch routing with E_pad = 208 (the router's last 64-expert group is partly
     # padding), T not a multiple of the 64-token logits block, a logit offset and a selection bias
     W("bf16_E200", T=300, d=384, E=200, k=6, d_ff=256, seed=127, sel_bias=True,

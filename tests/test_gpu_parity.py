@@ -83,6 +83,8 @@ SMALL = [
     # bias, shared expert
     W("bf16_gemv_T3", T=3, d=1536, E=40, k=5, d_ff=256, seed=128, sel_bias=True, zipf_s=0.7,
       n_shared=1, d_ff_shared=256),
+    # the same with the widest row it takes (d = 4096: eight pieces per lane) and T = 4
+    W("bf16_gemv_T4", T=4, d=4096, E=24, k=3, d_ff=512, seed=129, capacity_factor=1.0),
     # multi-launch routing with E_pad = 208 (the router's last 64-expert group is partly
     # padding), T not a multiple of the 64-token logits block, a logit offset and a selection bias
     W("bf16_E200", T=300, d=384, E=200, k=6, d_ff=256, seed=127, sel_bias=True,

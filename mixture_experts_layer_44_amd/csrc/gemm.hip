@@ -20,11 +20,13 @@
 //   ragged  (48 < r < 768) gemm_bf16_st_kernel, BM=128 / 192 (8 waves, 2x4) or 256 (4x2),
 //                         BNB=256, BK=64; B in the deep ring, A in the shallow one; the rows of
 //                         a tile past its segment's end are neither loaded nor multiplied.
-//   wide    (r >= 768)    gemm_bf16_kernel, BM=256, BNB=256, 8 waves (4x2), 2 stages with
-//                         register staging (the weight tiles are shared in L2 by several
-//                         m-tiles; the loads run faster through registers than straight to LDS).
+//   wide    (r >= 768)    gemm_bf16_w4_kernel, BM=256, BNB=256, 4 waves of 128 x 128 (one per
+//                         SIMD), 2 LDS stages filled from two register sets (the weight tiles
+//                         are shared in L2 by several m-tiles; the loads run faster through
+//                         registers than straight to LDS). Shapes whose x or h reach 2 GiB take
+//                         gemm_bf16_kernel with 8 waves (4x2) and one register set.
 //   d % 256 != 0          gemm_bf16_kernel, BM=128, BNB=256 / 128, BK=64, 3-stage ring.
-// Except in the decode class, each wave owns a block of 32x32 MFMA tiles
+// Except in the decode and wide classes, each wave owns a block of 32x32 MFMA tiles
 // (v_mfma_f32_32x32x16_bf16, fp32 accumulators), two waves per SIMD: while one waits for its
 // LDS fragments the other issues MFMAs.
 // BNB counts B rows: the gate-up B tile holds the W1 rows and then the W3 rows of the same
@@ -45,10 +47,12 @@
 //
 // In gemm_bf16_kernel, rows of an m-tile past the end of its segment are loaded from the
 // segment's first row; their results land only in padding rows of H (gate-up) or are not
-// stored (down). The wide class keeps loading them on purpose: with every tile the same length,
-// the m-tiles that share a weight tile stay in step and meet in L2 (skipping the padding loads of
-// a segment's last tile doubled FETCH_SIZE at unchanged time); it skips only the LDS reads and
-// MFMAs of row fragments that are all padding.
+// stored (down). The eight-wave wide variant keeps loading them on purpose: with every tile the
+// same length, the m-tiles that share a weight tile stay in step and meet in L2 (skipping the
+// padding loads of a segment's last tile doubled FETCH_SIZE at unchanged time); it skips only the
+// LDS reads and MFMAs of row fragments that are all padding. The four-wave wide kernel does the
+// same, except that its padding rows' loads fall outside the buffer range and return zeros
+// without a memory access (the loads and barriers still run, so the pace is unchanged).
 //
 // Work order: tiles are numbered group-major, then n-tile, then m-tile, so neighbouring
 // tiles share a weight tile (B) or a row block (A). Workgroups are dealt round-robin to
@@ -303,6 +307,277 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_kernel(GemmArgs args) 
         const int lr = wm * TM + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
         if (GATEUP) {
           if (tc.m_local * BM + lr < tc.rows) {   // padding rows of H are never read
+            const float u = acc[i][j][r];
+            const float v = acc[i][j + FN / 2][r];
+            args.H[(size_t)(tc.mt_global * BM + lr) * N + col] = f32_to_bf16(silu_f(u) * v);
+          }
+        } else {
+          const int rg = tc.m_local * BM + lr;
+          if (rg < tc.rows) {
+            float* dst = shared_grp ? args.shared_out + (size_t)rg * N
+                                    : (half ? args.out_rows_b : args.out_rows) +
+                                          (size_t)(tc.off + rg) * N;
+            dst[col] = acc[i][j][r];
+          }
+        }
+      }
+    }
+}
+
+// ------------------------------------------------------------------ wide class, four waves
+// 256 x 256 tiles (gate-up: 128 features of W1 and of W3), four waves of 128 x 128, one wave
+// per SIMD with its 16 accumulator fragments (256 registers) in the accumulation registers.
+// Against eight waves of 64 x 128, a K step reads a third fewer LDS bytes (8 fragment reads
+// per 16 MFMAs instead of 6 per 8).
+// Both operands go through registers in two sets: set s holds the steps of parity s. During
+// step kt, piece p of the set holding step kt+1 is written to LDS and then reloaded with step
+// kt+3, so every load has about two steps to land before its write. The writes, the loads and
+// the fragment reads of the next sub-step are interleaved with the MFMAs
+// (sched_group_barrier): with one wave per SIMD, no other wave covers them.
+// Each thread moves 16 pieces of 16 bytes per step: piece p is stage row p*32 + tid/8 (rows
+// 0..255 A, 256..511 B), physical slot tid%8, so one wave's write of a piece is 1 KB contiguous
+// and its load of a piece covers 8 whole 128-byte row segments. In a [rows][64] stage the
+// swizzle of row r depends on (r/2)%8 only, so all 16 pieces of a thread fetch one logical chunk.
+template <bool GATEUP>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void gemm_bf16_w4_kernel(GemmArgs args) {
+  constexpr int BM = 256, BNB = 256, BK = 64, WN = 2;
+  constexpr int STAGE = (BM + BNB) * BK;            // bf16 elements per stage
+  constexpr int FM = 4, FN = 4, NKS = BK / 16;
+  constexpr int FEAT = GATEUP ? BNB / 2 : BNB;
+  __shared__ __attribute__((aligned(1024))) bf16_t smem[2 * STAGE];
+
+  const int S = GATEUP ? 1 : args.ksplit;
+  TileCoord tc;
+  int half = 0;
+  if (!tile_coord(args.sc, args.N / FEAT, FEAT, tc, S, &half)) return;
+  const bool shared_grp = tc.g >= args.E;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int K = args.K, N = args.N;
+  const int KT = K / BK / S;
+  const int k0 = half * KT * BK;
+
+  const int prow = tid >> 3, slot = tid & 7;
+  const int lchunk = slot ^ ((prow >> 1) & 7);
+  // A pieces: gathered rows, byte offsets from x (gate-up) or h (down) in 32 bits (the launch
+  // takes this kernel only when x and the padded h rows stay below 2 GiB). Padding rows (past
+  // the segment's end) get an offset past the buffer's 2 GiB range, so their loads return zeros
+  // without a memory access; their results are never stored.
+  int sa[8];
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const int r = tc.m_local * BM + p * 32 + prow;
+    sa[p] = GATEUP ? args.sorted_assign[tc.off + (!shared_grp && r < tc.rows ? r : 0)] : 0;
+  }
+  constexpr uint32_t kARange = 0x80000000u;
+  uint32_t aoff[8];
+#pragma unroll
+  for (int p = 0; p < 8; ++p) {
+    const int r = tc.m_local * BM + p * 32 + prow;
+    int srow;
+    if (GATEUP) {
+      const int tok = shared_grp ? r : sa[p] / args.k;
+      srow = (unsigned)tok < (unsigned)args.T ? tok : 0;
+    } else {
+      srow = tc.mt_global * BM + p * 32 + prow;
+    }
+    aoff[p] = r < tc.rows ? ((uint32_t)srow * (uint32_t)K + lchunk * 8) * 2 : kARange;
+  }
+  // B pieces: weight rows n0 + q*32 + tid/8 (gate-up: W1 for q < 4, W3 for q >= 4; down: W2
+  // rows n0 + q*32 + tid/8), one lane offset for all eight, the row block in the scalar offset
+  const bf16_t* bm0;
+  const bf16_t* bm1;
+  if (GATEUP) {
+    bm0 = shared_grp ? args.S0 : args.B0 + (size_t)tc.g * N * K;
+    bm1 = shared_grp ? args.S1 : args.B1 + (size_t)tc.g * N * K;
+  } else {
+    bm0 = shared_grp ? args.S0 : args.B0 + (size_t)tc.g * N * K;
+    bm1 = bm0 + (size_t)128 * K;
+  }
+  bm0 += (size_t)tc.n0 * K;
+  bm1 += (size_t)tc.n0 * K;
+  const __amdgpu_buffer_rsrc_t ra =
+      __builtin_amdgcn_make_buffer_rsrc((void*)args.A, (short)0, (int)kARange, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb0 = __builtin_amdgcn_make_buffer_rsrc((void*)bm0, (short)0, -1, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb1 = __builtin_amdgcn_make_buffer_rsrc((void*)bm1, (short)0, -1, 0x00020000);
+  const uint32_t boff = ((uint32_t)prow * (uint32_t)K + lchunk * 8) * 2;
+
+  auto gload = [&](u32x4* st, int p, int kt) {
+    const int kb = (k0 + kt * BK) * 2;
+    if (p < 8) {
+      st[p] = __builtin_amdgcn_raw_buffer_load_b128(ra, aoff[p], kb, 0);
+    } else {
+      const int q = p - 8;
+      st[p] = __builtin_amdgcn_raw_buffer_load_b128(q < 4 ? rb0 : rb1, boff, (q & 3) * 64 * K + kb, 0);
+    }
+  };
+  // LDS (bytes): A of stage s at s*32K, B of stage s at 64K + s*32K, each [256 rows][128 B]
+  // swizzled; piece p of this thread lands at tid*16 + (p%8)*4K in its matrix's region, so
+  // every LDS access below is one of a few base registers plus an immediate offset.
+  typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+  typedef __attribute__((address_space(3))) bf16x8 lds_bf16x8;
+  typedef __attribute__((address_space(3))) char lds_char;
+  lds_char* const lds = (lds_char*)smem;
+  constexpr int ASTG = 32768, BREG = 65536;
+  auto lwrite = [&](const u32x4* st, int p, int stg) {
+    *(lds_u32x4*)(lds + (p < 8 ? 0 : BREG) + stg * ASTG + (p & 7) * 4096 + tid * 16) = st[p];
+  };
+
+  const int wm = wave / WN, wn = wave % WN;
+  f32x16 acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  const int fr = lane & 31, fkc = lane >> 5;
+  // Fragment rows are (multiples of 32) + lane%32, so all of this lane's fragments share one
+  // swizzle, ((lane%32)/2)%8: per sub-step one A and one B base register serve the eight reads.
+  bf16x8 af[2][FM], bfr[2][FN];
+  const int sx = (fr >> 1) & 7;
+  const int bw = GATEUP ? wn * 64 : wn * 128;   // first B row of this wave
+  uint32_t rdA[NKS], rdB[NKS];
+#pragma unroll
+  for (int ks = 0; ks < NKS; ++ks) {
+    const int c = ((2 * ks + fkc) ^ sx) << 4;
+    rdA[ks] = (wm * 128 + fr) * BK * 2 + c;
+    rdB[ks] = BREG + (bw + fr) * BK * 2 + c;
+  }
+  auto fread = [&](int buf, int stg, int ks) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      af[buf][i] = *(const lds_bf16x8*)(lds + rdA[ks] + stg * ASTG + i * 32 * BK * 2);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int rb = GATEUP ? (j < FN / 2 ? 0 : BNB / 2) + (j % (FN / 2)) * 32 : j * 32;
+      bfr[buf][j] = *(const lds_bf16x8*)(lds + rdB[ks] + stg * ASTG + rb * BK * 2);
+    }
+  };
+  auto mfma = [&](int buf, int m) {
+    const int i = m >> 2, j = m & 3;
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[buf][i], bfr[buf][j], acc[i][j], 0, 0, 0);
+  };
+
+  // pieces written (and reloaded) in sub-step ks: [PW[ks], PW[ks+1]); MFMAs of the last sub-step
+  // issued before the barrier that publishes the next stage: PRE (the rest cover the first
+  // fragment reads of the next step). Measured on the Mixtral-shaped layer against reading the
+  // fragments first in each sub-step, and against 4 or 8 MFMAs before the barrier.
+  constexpr int PW[NKS + 1] = {0, 4, 8, 12, 16};
+  constexpr int PRE = 12;
+  u32x4 st0[16], st1[16];
+  // one K step: MFMAs of step kt from stage kt&1 over the first NF row fragments of this wave;
+  // the set W (step kt+1) goes to the other stage and is reloaded with step kt+3 (past the
+  // end: the last step again, never read)
+  auto step = [&](auto cs_tag, auto nf_tag, int kt, u32x4* W) {
+    constexpr int cs = decltype(cs_tag)::value, ns = cs ^ 1;
+    constexpr int NF = decltype(nf_tag)::value;
+    constexpr int NM = NF * FN, NR = NF ? NF + FN : 0;
+    const int rl = kt + 3 < KT ? kt + 3 : KT - 1;
+    auto fread_nf = [&](int buf, int stg, int ks) {
+      if constexpr (NF > 0) {
+#pragma unroll
+        for (int i = 0; i < NF; ++i)
+          af[buf][i] = *(const lds_bf16x8*)(lds + rdA[ks] + stg * ASTG + i * 32 * BK * 2);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int rb = GATEUP ? (j < FN / 2 ? 0 : BNB / 2) + (j % (FN / 2)) * 32 : j * 32;
+          bfr[buf][j] = *(const lds_bf16x8*)(lds + rdB[ks] + stg * ASTG + rb * BK * 2);
+        }
+      }
+    };
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+      const int cur = ks & 1;
+      if (ks + 1 < NKS) fread_nf(cur ^ 1, cs, ks + 1);
+#pragma unroll
+      for (int p = PW[ks]; p < PW[ks + 1]; ++p) {
+        lwrite(W, p, ns);
+        gload(W, p, rl);
+      }
+      const int nm = ks + 1 < NKS ? NM : (PRE < NM ? PRE : NM);
+#pragma unroll
+      for (int m = 0; m < nm; ++m) mfma(cur, m);
+      const int nr = ks + 1 < NKS ? NR : 0, np = PW[ks + 1] - PW[ks];
+      // per 4 MFMAs: 2 fragment reads, then 1 LDS write and 1 load
+      for (int r = 0; r < 16; ++r) {
+        if (r < nm) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        if (r < nr) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+        if ((r & 3) == 1 && r / 4 < np) __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);
+        if ((r & 3) == 3 && r / 4 < np) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    // the barrier that publishes the next stage, then its first fragment reads under the
+    // remaining MFMAs of the last sub-step
+    constexpr int cur = (NKS - 1) & 1;
+    constexpr int pre = PRE < NM ? PRE : NM;
+    __builtin_amdgcn_s_waitcnt(0xC07F);   // lgkmcnt(0): this wave's writes are in LDS
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    fread_nf(cur ^ 1, ns, 0);
+#pragma unroll
+    for (int m = pre; m < NM; ++m) mfma(cur, m);
+    for (int r = 0; r < NR; ++r) {
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      if (r + pre < NM) __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  auto main_loop = [&](auto nf_tag) {
+    // prologue: steps 0 and 1 loaded, step 0 written, set 0 reloaded with step 2
+#pragma unroll
+    for (int p = 0; p < 16; ++p) gload(st0, p, 0);
+#pragma unroll
+    for (int p = 0; p < 16; ++p) gload(st1, p, KT > 1 ? 1 : 0);
+#pragma unroll
+    for (int p = 0; p < 16; ++p) {
+      lwrite(st0, p, 0);
+      gload(st0, p, KT > 2 ? 2 : KT - 1);
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    constexpr int NF = decltype(nf_tag)::value;
+    if constexpr (NF > 0) fread(0, 0, 0);
+    // NKS = 4 sub-steps: a step starts and ends with its fragments in buffer 0. KT is even (the
+    // launch checks it), so the loop body is two whole steps.
+    static_assert(NKS % 2 == 0, "fragment buffers alternate within a step");
+    for (int kt = 0; kt < KT; kt += 2) {
+      step(std::integral_constant<int, 0>{}, nf_tag, kt, st1);
+      step(std::integral_constant<int, 1>{}, nf_tag, kt + 1, st0);
+    }
+  };
+  // Row fragments of this wave that hold rows of the segment: a segment's last m-tile is often
+  // mostly padding. The LDS reads and MFMAs of the other fragments are skipped; the loads and
+  // barriers stay, so the tile keeps the pace of the m-tiles that share its weight tiles in L2.
+  const int live_rows = __builtin_amdgcn_readfirstlane(tc.rows - tc.m_local * BM - wm * 128);
+  if (live_rows > 32) main_loop(std::integral_constant<int, FM>{});
+  else if (live_rows > 0) main_loop(std::integral_constant<int, 1>{});
+  else main_loop(std::integral_constant<int, 0>{});
+  __builtin_amdgcn_s_waitcnt(wait_vm(0));
+
+  // ---- epilogue (32x32 accumulator layout: lane holds column lane%32 and rows
+  // 8*(r/4) + 4*(lane/32) + r%4 for r = 0..15)
+  constexpr int FO = GATEUP ? FN / 2 : FN;
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FO; ++j) {
+      const int col = tc.n0 + wn * (FEAT / WN) + j * 32 + fr;
+      if (GATEUP && args.U && tc.m_local * BM + wm * 128 + i * 32 < tc.rows) {
+        const size_t o = uv_frag(tc.mt_global * BM + wm * 128 + i * 32, col - fr, N, lane);
+        uv_store(args.U + o, acc[i][j]);
+        uv_store(args.V + o, acc[i][j + FN / 2]);
+      }
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int lr = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+        if (GATEUP) {
+          if (tc.m_local * BM + lr < tc.rows) {
             const float u = acc[i][j][r];
             const float v = acc[i][j + FN / 2][r];
             args.H[(size_t)(tc.mt_global * BM + lr) * N + col] = f32_to_bf16(silu_f(u) * v);
@@ -987,6 +1262,28 @@ hipError_t launch_bf16_st(const moe_problem& p, const GemmArgs& a, const GemmArg
   return hipGetLastError();
 }
 
+// The four-wave wide kernel addresses x and h with byte offsets below 2^31 and runs whole pairs
+// of K steps; other wide shapes take the eight-wave register-staged kernel.
+static bool wide_w4_ok(const moe_problem& p, const Schedule& sc, int ksplit) {
+  return (double)p.T * p.d * 2.0 < 2147483648.0 &&
+         (double)sc.max_mtiles * 256.0 * p.d_ff * 2.0 < 2147483648.0 && p.d % 128 == 0 &&
+         p.d_ff % (128 * ksplit) == 0;
+}
+
+hipError_t launch_bf16_w4(const moe_problem& p, const GemmArgs& a, const GemmArgs& b, hipStream_t s,
+                          hipEvent_t between, bool up_only) {
+  if (p.d_ff % 128 || p.d % 256) return hipErrorInvalidValue;   // n-tiles cover N
+  hipLaunchKernelGGL(gemm_bf16_w4_kernel<true>,
+                     dim3(grid_for(a.sc.max_mtiles, p.d_ff / 128, a.sc.xcd_chunk)), dim3(256), 0, s, a);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || up_only) return err;
+  if (between && (err = hipEventRecord(between, s)) != hipSuccess) return err;
+  hipLaunchKernelGGL(gemm_bf16_w4_kernel<false>,
+                     dim3(grid_for(b.sc.max_mtiles * b.ksplit, p.d / 256, b.sc.xcd_chunk)), dim3(256), 0,
+                     s, b);
+  return hipGetLastError();
+}
+
 hipError_t launch_expert_ffn(const moe_problem& p, const void* x, const void* w1, const void* w3,
                              const void* w2, const void* ws1, const void* ws3, const void* ws2,
                              const int32_t* sorted_assign, const Schedule& sc, void* h,
@@ -1029,7 +1326,9 @@ hipError_t launch_expert_ffn(const moe_problem& p, const void* x, const void* w1
     b.out_rows_b = out_rows_b;
     if (!up_only && b.ksplit == 2 && !out_rows_b) return hipErrorInvalidValue;
     if (sc.BM == 256 && gemm_wide(p))
-      return launch_bf16<256, 256, 4, 2, 256, 4, 2, 64, 2, 1>(p, a, b, s, between, up_only);
+      return wide_w4_ok(p, sc, b.ksplit)
+                 ? launch_bf16_w4(p, a, b, s, between, up_only)
+                 : launch_bf16<256, 256, 4, 2, 256, 4, 2, 64, 2, 1>(p, a, b, s, between, up_only);
     if (sc.BM == 256) return launch_bf16_st<256, 256, 4, 2, 256, 4, 2>(p, a, b, s, between, up_only);
     if (sc.BM == 192) return launch_bf16_st<192, 256, 2, 4, 256, 2, 4>(p, a, b, s, between, up_only);
     if (sc.BM == kDecBM && gemm_dec(p)) return launch_dec(p, a, b, s, between, up_only);

@@ -456,9 +456,13 @@ void gemm_bf16_w4_kernel(GemmArgs args) {
       bfr[buf][j] = *(const lds_bf16x8*)(lds + rdB[ks] + stg * ASTG + rb * BK * 2);
     }
   };
+  // The weights are the MFMA's first operand, so each accumulator holds a transposed 32 x 32 block:
+  // lane l has row (token) l%32 of fragment i and, at r = 0..15, feature 8*(r/4) + 4*(l/32) + r%4
+  // of fragment j. Four consecutive features per lane let the epilogue store 8 (h) or 16 (fp32)
+  // contiguous bytes at a time.
   auto mfma = [&](int buf, int m) {
     const int i = m >> 2, j = m & 3;
-    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[buf][i], bfr[buf][j], acc[i][j], 0, 0, 0);
+    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[buf][j], af[buf][i], acc[i][j], 0, 0, 0);
   };
 
   // pieces written (and reloaded) in sub-step ks: [PW[ks], PW[ks+1]); MFMAs of the last sub-step
@@ -560,39 +564,33 @@ void gemm_bf16_w4_kernel(GemmArgs args) {
   else main_loop(std::integral_constant<int, 0>{});
   __builtin_amdgcn_s_waitcnt(wait_vm(0));
 
-  // ---- epilogue (32x32 accumulator layout: lane holds column lane%32 and rows
-  // 8*(r/4) + 4*(lane/32) + r%4 for r = 0..15)
+  // ---- epilogue: h = SiLU(u) * v as bf16 (round to nearest even), or the fp32 rows
   constexpr int FO = GATEUP ? FN / 2 : FN;
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+  for (int i = 0; i < FM; ++i) {
+    const int lr = wm * 128 + i * 32 + fr;   // this lane's row of the tile
+    const int rg = tc.m_local * BM + lr;
+    if (rg >= tc.rows) continue;             // padding rows are never stored
 #pragma unroll
-    for (int j = 0; j < FO; ++j) {
-      const int col = tc.n0 + wn * (FEAT / WN) + j * 32 + fr;
-      if (GATEUP && args.U && tc.m_local * BM + wm * 128 + i * 32 < tc.rows) {
-        const size_t o = uv_frag(tc.mt_global * BM + wm * 128 + i * 32, col - fr, N, lane);
-        uv_store(args.U + o, acc[i][j]);
-        uv_store(args.V + o, acc[i][j + FN / 2]);
-      }
+    for (int j = 0; j < FO; ++j)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int lr = wm * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+      for (int q = 0; q < 4; ++q) {
+        const int col = tc.n0 + wn * (FEAT / WN) + j * 32 + 8 * q + 4 * (lane >> 5);
         if (GATEUP) {
-          if (tc.m_local * BM + lr < tc.rows) {
-            const float u = acc[i][j][r];
-            const float v = acc[i][j + FN / 2][r];
-            args.H[(size_t)(tc.mt_global * BM + lr) * N + col] = f32_to_bf16(silu_f(u) * v);
-          }
+          typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+          bf16x4 h;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            h[e] = (__bf16)(silu_f(acc[i][j][4 * q + e]) * acc[i][j + FN / 2][4 * q + e]);
+          *(bf16x4*)(args.H + (size_t)(tc.mt_global * BM + lr) * N + col) = h;
         } else {
-          const int rg = tc.m_local * BM + lr;
-          if (rg < tc.rows) {
-            float* dst = shared_grp ? args.shared_out + (size_t)rg * N
-                                    : (half ? args.out_rows_b : args.out_rows) +
-                                          (size_t)(tc.off + rg) * N;
-            dst[col] = acc[i][j][r];
-          }
+          float* dst = shared_grp ? args.shared_out + (size_t)rg * N
+                                  : (half ? args.out_rows_b : args.out_rows) + (size_t)(tc.off + rg) * N;
+          *(f32x4*)(dst + col) = f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                                       acc[i][j][4 * q + 3]};
         }
       }
-    }
+  }
 }
 
 // ------------------------------------------------------------------ staggered rings
@@ -1263,7 +1261,8 @@ hipError_t launch_bf16_st(const moe_problem& p, const GemmArgs& a, const GemmArg
 }
 
 // The four-wave wide kernel addresses x and h with byte offsets below 2^31 and runs whole pairs
-// of K steps; other wide shapes take the eight-wave register-staged kernel.
+// of K steps; other wide shapes, and the backward's gate-up recompute (which also stores u and v in
+// the accumulator layout), take the eight-wave register-staged kernel.
 static bool wide_w4_ok(const moe_problem& p, const Schedule& sc, int ksplit) {
   return (double)p.T * p.d * 2.0 < 2147483648.0 &&
          (double)sc.max_mtiles * 256.0 * p.d_ff * 2.0 < 2147483648.0 && p.d % 128 == 0 &&
@@ -1326,7 +1325,7 @@ hipError_t launch_expert_ffn(const moe_problem& p, const void* x, const void* w1
     b.out_rows_b = out_rows_b;
     if (!up_only && b.ksplit == 2 && !out_rows_b) return hipErrorInvalidValue;
     if (sc.BM == 256 && gemm_wide(p))
-      return wide_w4_ok(p, sc, b.ksplit)
+      return wide_w4_ok(p, sc, b.ksplit) && !up_only
                  ? launch_bf16_w4(p, a, b, s, between, up_only)
                  : launch_bf16<256, 256, 4, 2, 256, 4, 2, 64, 2, 1>(p, a, b, s, between, up_only);
     if (sc.BM == 256) return launch_bf16_st<256, 256, 4, 2, 256, 4, 2>(p, a, b, s, between, up_only);

@@ -456,13 +456,17 @@ void gemm_bf16_w4_kernel(GemmArgs args) {
       bfr[buf][j] = *(const lds_bf16x8*)(lds + rdB[ks] + stg * ASTG + rb * BK * 2);
     }
   };
-  // The weights are the MFMA's first operand, so each accumulator holds a transposed 32 x 32 block:
-  // lane l has row (token) l%32 of fragment i and, at r = 0..15, feature 8*(r/4) + 4*(l/32) + r%4
-  // of fragment j. Four consecutive features per lane let the epilogue store 8 (h) or 16 (fp32)
-  // contiguous bytes at a time.
+  // Gate-up: the weights are the MFMA's first operand, so each accumulator holds a transposed
+  // 32 x 32 block: lane l has row (token) l%32 of fragment i and, at r = 0..15, feature
+  // 8*(r/4) + 4*(l/32) + r%4 of fragment j, and the epilogue stores four consecutive h values
+  // (8 bytes) at a time. Down: the usual layout (lane l has feature l%32 and rows
+  // 8*(r/4) + 4*(l/32) + r%4), so each fp32 store instruction writes two whole 128-byte row
+  // segments (transposed, 16-byte pieces of 32 rows: down 0.92 -> 0.94 ms).
   auto mfma = [&](int buf, int m) {
     const int i = m >> 2, j = m & 3;
-    acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[buf][j], af[buf][i], acc[i][j], 0, 0, 0);
+    acc[i][j] = GATEUP
+        ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[buf][j], af[buf][i], acc[i][j], 0, 0, 0)
+        : __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[buf][i], bfr[buf][j], acc[i][j], 0, 0, 0);
   };
 
   // pieces written (and reloaded) in sub-step ks: [PW[ks], PW[ks+1]); MFMAs of the last sub-step
@@ -566,28 +570,38 @@ void gemm_bf16_w4_kernel(GemmArgs args) {
 
   // ---- epilogue: h = SiLU(u) * v as bf16 (round to nearest even), or the fp32 rows
   constexpr int FO = GATEUP ? FN / 2 : FN;
+  if constexpr (GATEUP) {
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    const int lr = wm * 128 + i * 32 + fr;   // this lane's row of the tile
-    const int rg = tc.m_local * BM + lr;
-    if (rg >= tc.rows) continue;             // padding rows are never stored
+    for (int i = 0; i < FM; ++i) {
+      const int lr = wm * 128 + i * 32 + fr;   // this lane's row of the tile
+      if (tc.m_local * BM + lr >= tc.rows) continue;   // padding rows are never stored
 #pragma unroll
-    for (int j = 0; j < FO; ++j)
+      for (int j = 0; j < FO; ++j)
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int col = tc.n0 + wn * (FEAT / WN) + j * 32 + 8 * q + 4 * (lane >> 5);
-        if (GATEUP) {
+        for (int q = 0; q < 4; ++q) {
+          const int col = tc.n0 + wn * (FEAT / WN) + j * 32 + 8 * q + 4 * (lane >> 5);
           typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
           bf16x4 h;
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             h[e] = (__bf16)(silu_f(acc[i][j][4 * q + e]) * acc[i][j + FN / 2][4 * q + e]);
           *(bf16x4*)(args.H + (size_t)(tc.mt_global * BM + lr) * N + col) = h;
-        } else {
-          float* dst = shared_grp ? args.shared_out + (size_t)rg * N
-                                  : (half ? args.out_rows_b : args.out_rows) + (size_t)(tc.off + rg) * N;
-          *(f32x4*)(dst + col) = f32x4{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
-                                       acc[i][j][4 * q + 3]};
+        }
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FO; ++j) {
+        const int col = tc.n0 + wn * (FEAT / WN) + j * 32 + fr;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int rg = tc.m_local * BM + wm * 128 + i * 32 + 8 * (r >> 2) + 4 * (lane >> 5) + (r & 3);
+          if (rg < tc.rows) {
+            float* dst = shared_grp ? args.shared_out + (size_t)rg * N
+                                    : (half ? args.out_rows_b : args.out_rows) + (size_t)(tc.off + rg) * N;
+            dst[col] = acc[i][j][r];
+          }
         }
       }
   }
@@ -607,7 +621,7 @@ void gemm_bf16_w4_kernel(GemmArgs args) {
 // all loads issued before that step's A loads. Every slot written in step kt was last read in
 // step kt-1, which all waves finished before this step's barrier.
 // NTR (down only): the fp32 rows go out with the non-temporal hint
-template <int BM, int BNB, int WM, int WN, bool GATEUP, bool NTR = false>
+template <int BM, int BNB, int WM, int WN, bool GATEUP, bool NTR = false, bool TR = GATEUP>
 __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_st_kernel(GemmArgs args) {
   constexpr int BK = 64, NKS = BK / 16;
   constexpr int NW = WM * WN;
@@ -801,8 +815,10 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_st_kernel(GemmArgs arg
         for (int i = 0; i < NF; ++i)
 #pragma unroll
           for (int j = 0; j < FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bfr[cur][j],
-                                                                acc[i][j], 0, 0, 0);
+            acc[i][j] = TR ? __builtin_amdgcn_mfma_f32_32x32x16_bf16(bfr[cur][j], af[cur][i],
+                                                                     acc[i][j], 0, 0, 0)
+                           : __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[cur][i], bfr[cur][j],
+                                                                     acc[i][j], 0, 0, 0);
       }
     }
   };
@@ -814,8 +830,45 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_st_kernel(GemmArgs arg
   else k_loop(std::integral_constant<int, 0>{});
   __builtin_amdgcn_s_waitcnt(wait_vm(0));
 
-  // ---- epilogue (same accumulator layout and stores as gemm_bf16_kernel)
+  // ---- epilogue
   constexpr int FO = GATEUP ? FN / 2 : FN;
+  if constexpr (TR) {
+    // TR: the weights were the MFMA's first operand, so lane l holds row (token) l%32 of row
+    // fragment i and, at r = 0..15, feature 8*(r/4) + 4*(l/32) + r%4 of fragment j: four
+    // consecutive features go out as one 8-byte (h) or 16-byte (fp32 row) store. (Not used for
+    // the fp32 rows: 16-byte pieces of 32 rows per instruction, instead of two whole 128-byte
+    // row segments, made the DeepSeek-V3-shaped down GEMM 1.77 -> 1.90 ms.)
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int lr = (i * WM + wm) * 32 + fr;
+      if (lr >= rows_here) continue;   // padding rows of H feed only padding rows of the down
+      const int rg = tc.m_local * BM + lr;
+#pragma unroll
+      for (int j = 0; j < FO; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int col = tc.n0 + wn * (FEAT / WN) + j * 32 + 8 * q + 4 * (lane >> 5);
+          if (GATEUP) {
+            typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+            bf16x4 h;
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              h[e] = (__bf16)(silu_f(acc[i][j][4 * q + e]) * acc[i][j + FN / 2][4 * q + e]);
+            *(bf16x4*)(args.H + (size_t)(tc.mt_global * BM + lr) * N + col) = h;
+          } else {
+            float* dst = shared_grp ? args.shared_out + (size_t)rg * N
+                                    : (half ? args.out_rows_b : args.out_rows) + (size_t)(tc.off + rg) * N;
+            const f32x4 o{acc[i][j][4 * q], acc[i][j][4 * q + 1], acc[i][j][4 * q + 2],
+                          acc[i][j][4 * q + 3]};
+            if (NTR) __builtin_nontemporal_store(o, (f32x4*)(dst + col));
+            else *(f32x4*)(dst + col) = o;
+          }
+        }
+    }
+    return;
+  }
+  // !TR (the backward's gate-up recompute, which also stores u and v in this layout): lane l
+  // holds column l%32 and rows 8*(r/4) + 4*(l/32) + r%4, as in gemm_bf16_kernel
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -1240,9 +1293,13 @@ template <int BM, int BNB_UP, int WM_UP, int WN_UP, int BNB_DN, int WM_DN, int W
 hipError_t launch_bf16_st(const moe_problem& p, const GemmArgs& a, const GemmArgs& b,
                           hipStream_t s, hipEvent_t between, bool up_only) {
   if (p.d_ff % (BNB_UP / 2) || p.d % BNB_DN) return hipErrorInvalidValue;   // n-tiles cover N
-  hipLaunchKernelGGL((gemm_bf16_st_kernel<BM, BNB_UP, WM_UP, WN_UP, true>),
-                     dim3(grid_for(a.sc.max_mtiles, p.d_ff / (BNB_UP / 2), a.sc.xcd_chunk)), dim3(WM_UP * WN_UP * 64),
-                     0, s, a);
+  const dim3 gup(grid_for(a.sc.max_mtiles, p.d_ff / (BNB_UP / 2), a.sc.xcd_chunk));
+  if (up_only)   // the backward's recompute keeps u and v in the untransposed accumulator layout
+    hipLaunchKernelGGL((gemm_bf16_st_kernel<BM, BNB_UP, WM_UP, WN_UP, true, false, false>), gup,
+                       dim3(WM_UP * WN_UP * 64), 0, s, a);
+  else
+    hipLaunchKernelGGL((gemm_bf16_st_kernel<BM, BNB_UP, WM_UP, WN_UP, true>), gup,
+                       dim3(WM_UP * WN_UP * 64), 0, s, a);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || up_only) return err;
   if (between && (err = hipEventRecord(between, s)) != hipSuccess) return err;

@@ -40,22 +40,23 @@ PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)   # flop per byte
 KERNEL_SOURCES = {"gate_up": "gemm.hip", "down": "gemm.hip", "route": "route.hip",
                   "align": "align.hip", "schedule": "align.hip", "combine": "combine.hip"}
-KERNEL_NAMES = {"gate_up": "grouped GEMM gate-up + SwiGLU (gemm_bf16_st_kernel / gemm_bf16_kernel "
-                           "with the gate-up flag set; template by row-tile class)",
-                "down": "grouped GEMM down projection (gemm_bf16_st_kernel / gemm_bf16_kernel "
-                        "with the gate-up flag clear)"}
+KERNEL_NAMES = {"gate_up": "grouped GEMM gate-up + SwiGLU (gemm_bf16_w4_kernel / gemm_bf16_st_kernel / "
+                           "gemm_bf16_kernel with the gate-up flag set; kernel by row-tile class)",
+                "down": "grouped GEMM down projection (gemm_bf16_w4_kernel / gemm_bf16_st_kernel / "
+                        "gemm_bf16_kernel with the gate-up flag clear)"}
 COPY_PATTERN = r"copyBuffer"   # the runtime's blit kernel (the calibration copy)
 
 
 def gemm_stage(kernel_name: str):
     """'gate_up' / 'down' for a grouped-GEMM kernel name as rocprofv3 prints it, else None.
     The gate-up flag is the 7th template argument of gemm_bf16_kernel, the 5th of
-    gemm_bf16_st_kernel and the first of gemm_bf16_dec_kernel and gemm_f32_kernel."""
-    m = re.search(r"gemm_(bf16_st|bf16_dec|bf16|f32)_kernel<([^>]*)>", kernel_name)
+    gemm_bf16_st_kernel and the first of gemm_bf16_w4_kernel, gemm_bf16_dec_kernel and
+    gemm_f32_kernel."""
+    m = re.search(r"gemm_(bf16_st|bf16_dec|bf16_w4|bf16|f32)_kernel<([^>]*)>", kernel_name)
     if not m:
         return None
     args = [a.strip() for a in m.group(2).split(",")]
-    pos = {"bf16": 6, "bf16_st": 4, "bf16_dec": 0, "f32": 0}[m.group(1)]
+    pos = {"bf16": 6, "bf16_st": 4, "bf16_w4": 0, "bf16_dec": 0, "f32": 0}[m.group(1)]
     if len(args) <= pos or args[pos] not in ("true", "false"):
         return None
     return "gate_up" if args[pos] == "true" else "down"

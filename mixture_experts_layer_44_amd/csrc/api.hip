@@ -471,6 +471,15 @@ moe_status forward_impl(const moe_problem* p, const void* x, const void* w_gate,
     if (launch_schedule(*p, offs, sc, stream) != hipSuccess || mark(3) != hipSuccess)
       return MOE_EHIP;
   }
+  if (dec_down_combine(*p) && sc.BM == kDecBM) {
+    // decode-sized: gate-up, then the down GEMM and the combine in one launch (same bits as
+    // the rows-then-combine path below; the "combine" stage is empty)
+    e = launch_dec_gate_up(*p, x, w1, w3, sa, sc, at<void>(ws, L.h), stream);
+    if (e != hipSuccess || (ev && hipEventRecord(ev[4], stream) != hipSuccess)) return MOE_EHIP;
+    e = launch_dec_down_combine(*p, at<void>(ws, L.h), w2, ids, gates, ap, sc, y, stream);
+    if (e != hipSuccess || mark(5) != hipSuccess || mark(6) != hipSuccess) return MOE_EHIP;
+    return MOE_OK;
+  }
   e = launch_expert_ffn(*p, x, w1, w3, w2, ws1, ws3, ws2, sa, sc, at<void>(ws, L.h), out_rows,
                         out_b, shared_out, stream, ev ? ev[4] : nullptr);
   if (e != hipSuccess || mark(5) != hipSuccess) return MOE_EHIP;

@@ -917,7 +917,7 @@ __global__ __launch_bounds__(WM * WN * 64) void gemm_bf16_st_kernel(GemmArgs arg
 // KTW, the steps per wave (K / 256), is a template argument: the K loop is unrolled whole, so
 // the ring slots and the last loads are fixed at compile time and the compiler's vmcnt waits
 // are exact (with a rolled loop it drained every load at the loop head).
-constexpr int kDecBM = 32, kDecMaxSteps = 8;
+constexpr int kDecMaxSteps = 8;
 // output features per workgroup: gate-up 32 (16-row blocks W1, W1, W3, W3), down 64
 constexpr int dec_feat(bool gateup) { return gateup ? 32 : 64; }
 // steps in flight: as many as about 200 VGPRs of operands hold (40 per step with one A
@@ -1337,6 +1337,28 @@ hipError_t launch_bf16_w4(const moe_problem& p, const GemmArgs& a, const GemmArg
   hipLaunchKernelGGL(gemm_bf16_w4_kernel<false>,
                      dim3(grid_for(b.sc.max_mtiles * b.ksplit, p.d / 256, b.sc.xcd_chunk)), dim3(256), 0,
                      s, b);
+  return hipGetLastError();
+}
+
+hipError_t launch_dec_gate_up(const moe_problem& p, const void* x, const void* w1, const void* w3,
+                              const int32_t* sorted_assign, const Schedule& sc, void* h,
+                              hipStream_t s) {
+  if (!gemm_dec(p) || sc.BM != kDecBM || p.n_shared) return hipErrorInvalidValue;
+  if (p.T == 0) return hipSuccess;
+  GemmArgs a{};
+  a.A = (const bf16_t*)x;
+  a.B0 = (const bf16_t*)w1;
+  a.B1 = (const bf16_t*)w3;
+  a.N = p.d_ff;
+  a.K = p.d;
+  a.E = p.E;
+  a.k = p.k;
+  a.T = p.T;
+  a.sorted_assign = sorted_assign;
+  a.sc = sc;
+  a.H = (bf16_t*)h;
+  a.ksplit = 1;
+  launch_dec_k<true>(p.d / 256, dim3(grid_for(sc.max_mtiles, p.d_ff / dec_feat(true), sc.xcd_chunk)), s, a);
   return hipGetLastError();
 }
 

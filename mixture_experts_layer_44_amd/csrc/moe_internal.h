@@ -51,6 +51,7 @@ __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
 constexpr int kAlignChunk = 1024;    // assignments per align workgroup
 constexpr int kGemmBM = 128;         // rows per grouped-GEMM m-tile (bf16 path)
 constexpr int kGemmBM32 = 16;        // rows per m-tile (fp32 path; its tiles are VALU-bound)
+constexpr int kDecBM = 32;           // rows per m-tile of the decode-class GEMM kernels
 
 inline int ceil_div(int a, int b) { return (a + b - 1) / b; }
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
@@ -148,6 +149,18 @@ hipError_t launch_expert_ffn(const moe_problem& p, const void* x, const void* w1
                              float* out_rows, float* out_rows_b, float* shared_out, hipStream_t s,
                              hipEvent_t between = nullptr, int row_div = 0, float* U = nullptr,
                              float* V = nullptr);
+
+// Decode-sized layers without a shared expert (k <= 8, T*k <= 64): the gate-up GEMM alone
+// (decode class, h out), then the down GEMM and the combine in one launch, y bit-identical to
+// launch_expert_ffn's rows followed by launch_combine.
+hipError_t launch_dec_gate_up(const moe_problem& p, const void* x, const void* w1, const void* w3,
+                              const int32_t* sorted_assign, const Schedule& sc, void* h,
+                              hipStream_t s);
+bool dec_down_combine(const moe_problem& p);
+hipError_t launch_dec_down_combine(const moe_problem& p, const void* h, const void* w2,
+                                   const int32_t* ids, const float* gates,
+                                   const int32_t* assign_pos, const Schedule& sc, float* y,
+                                   hipStream_t s);
 
 // out_rows_b may be null; when given, each expert row is out_rows + out_rows_b
 hipError_t launch_combine(const moe_problem& p, const float* out_rows, const float* out_rows_b,

@@ -89,6 +89,12 @@ SMALL = [
     # padding), T not a multiple of the 64-token logits block, a logit offset and a selection bias
     W("bf16_E200", T=300, d=384, E=200, k=6, d_ff=256, seed=127, sel_bias=True,
       zipf_s=0.5),
+    # decode down GEMM + combine in one launch (T*k <= 64, k <= 8, no shared expert): dropped
+    # slots under a capacity limit, and an odd k (the second slot group one slot short) with
+    # K = d_ff of eight wave steps
+    W("bf16_dec_fused_cap", T=8, d=512, E=16, k=8, d_ff=512, seed=130, capacity_factor=0.5,
+      zipf_s=1.1),
+    W("bf16_dec_fused_k5", T=3, d=768, E=32, k=5, d_ff=2048, seed=131, sel_bias=True),
 ]
 
 
@@ -215,6 +221,11 @@ COMPOSE = [
     # T <= 16: top-k, grouping and schedule in one workgroup after the logits
     W("compose_small16", T=12, d=256, E=16, k=4, d_ff=256, seed=203, sel_bias=True,
       capacity_factor=0.8),
+    # decode-sized: moe_forward runs the down GEMM and the combine as one launch; expert_ffn +
+    # combine run them apart. Same bits.
+    W("compose_dec_fused_cap", T=8, d=512, E=16, k=8, d_ff=512, seed=204, capacity_factor=0.5),
+    W("compose_dec_T1", T=1, d=2048, E=128, k=8, d_ff=768, seed=205),
+    W("compose_dec_k3", T=2, d=256, E=8, k=3, d_ff=2048, seed=206, sel_bias=True),
 ]
 
 
@@ -238,7 +249,8 @@ def test_entry_points_compose_to_forward(w):
     # prob_sum is the same sum; small batches add it in another order (fp32 rounding only)
     torch.testing.assert_close(psum, r["prob_sum"], rtol=1e-6, atol=1e-6)
     n_kept = int(al["offsets"][-1].item())
-    assert n_kept < w.T * w.k                     # the capacity limit dropped something
+    if w.capacity_factor:
+        assert n_kept < w.T * w.k                 # the capacity limit dropped something
     for key in al:
         a, b = al[key], r[key]
         if key == "sorted_assign":                # only the first offsets[E] entries are defined

@@ -52,7 +52,7 @@ SMALL = [
     # wide tiles with the down GEMM's K range split in two (few down tiles, no shared expert)
     W("bf16_wide_ksplit", T=2048, d=1024, E=4, k=2, d_ff=1024, seed=114),
     # wide tiles under a steep logit offset: segments of 2048, 1820, 200 and 28 rows, so the
-    # evenly cut m-tiles run with 4, 3, 2, 1 and 0 live row fragments per wave
+    # four-wave kernel's waves run with all, one and no live row fragments
     W("bf16_wide_skew", T=2048, d=512, E=4, k=2, d_ff=512, seed=131, zipf_s=2.0),
     # ragged 192-row tiles: ~150 rows per expert (one tile), the shared group 600 rows (four)
     W("bf16_mid192", T=600, d=512, E=8, k=2, d_ff=384, seed=115, n_shared=1, d_ff_shared=384),

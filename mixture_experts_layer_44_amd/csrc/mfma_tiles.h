@@ -81,10 +81,26 @@ __device__ __forceinline__ bool tile_coord(const Schedule& sc, int NT, int bn, T
     }
   }
   const int lp = L - ms * NT;
-  const int n_tile = lp / mtg;
+  // Inside a group the tiles run n-tile by n-tile, its m-tiles together, so those share each
+  // weight tile in L2. A group of many m-tiles (the shared expert: every token) walks them in
+  // blocks of kMBlock m-tiles instead, n-tile by n-tile inside a block: a window of concurrent
+  // tiles then also shares its gathered rows (A) over several n-tiles rather than streaming all
+  // of the group's rows once per n-tile.
+  constexpr int kMBlock = 4;
+  int n_tile, m_local;
+  if (mtg >= 2 * kMBlock) {
+    const int b = lp / (kMBlock * NT);
+    const int rem = lp - b * kMBlock * NT;
+    const int sz = min(kMBlock, mtg - b * kMBlock);
+    n_tile = rem / sz;
+    m_local = b * kMBlock + rem - n_tile * sz;
+  } else {
+    n_tile = lp / mtg;
+    m_local = lp - n_tile * mtg;
+  }
   tc.g = g;
   tc.mtg = mtg;
-  tc.m_local = lp - n_tile * mtg;
+  tc.m_local = m_local;
   tc.n0 = n_tile * bn;
   tc.mt_global = ms + tc.m_local;
   tc.rows = rows;

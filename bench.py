@@ -8,9 +8,10 @@ SwiGLU -> grouped down GEMM -> combine) over one batch of synthetic input
 already resident in HBM. W untimed warm-up steps, then exactly K steps
 between two device synchronisations. A second pass of K steps records HIP
 events on the launch stream between the stages, for the per-stage times and
-the dominant kernel's average launch duration (its roofline). A third, cold
-pass reads a 1 GiB buffer before each step, outside its events, so no step
-finds the last one's data in L2 or the Infinity Cache ("cold": medians). Prints ONE
+the dominant kernel's average launch duration (its roofline). Two cold passes
+read a 1 GiB buffer before each step, outside its events, so no step finds the
+last one's data in L2 or the Infinity Cache ("cold": medians): one with the
+stage events (per-stage times), one timing the plain step alone. Prints ONE
 JSON line on stdout: tokens/s of the whole job, that roofline, and the fp64
 CPU oracle timed on a bounded sample of the same workload (1 core).
 
@@ -38,8 +39,11 @@ PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
 PEAK_F32_TFLOPS = 157.3        # MI355X fp32 vector
 PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
 RIDGE = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)   # flop per byte
-KERNEL_SOURCES = {"gate_up": "gemm.hip", "down": "gemm.hip", "route": "route.hip",
-                  "align": "align.hip", "schedule": "align.hip", "combine": "combine.hip"}
+# the sources a stage's kernels are built from (the counter summaries are void once any changes)
+_GEMM_SOURCES = ("gemm.hip", "mfma_tiles.h", "moe_internal.h")
+KERNEL_SOURCES = {"gate_up": _GEMM_SOURCES, "down": _GEMM_SOURCES + ("down_combine.hip",),
+                  "route": ("route.hip", "topk.h"), "align": ("align.hip",),
+                  "schedule": ("align.hip",), "combine": ("combine.hip",)}
 KERNEL_NAMES = {"gate_up": "grouped GEMM gate-up + SwiGLU (gemm_bf16_w4_kernel / gemm_bf16_st_kernel / "
                            "gemm_bf16_kernel with the gate-up flag set; kernel by row-tile class)",
                 "down": "grouped GEMM down projection (gemm_bf16_w4_kernel / gemm_bf16_st_kernel / "
@@ -115,8 +119,11 @@ def kernel_work(w, counts, stage, T=None):
 
 
 def source_sha(stage: str) -> str:
-    path = os.path.join(ROOT, "mixture_experts_layer_44_amd", "csrc", KERNEL_SOURCES[stage])
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES[stage]:
+        with open(os.path.join(ROOT, "mixture_experts_layer_44_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
 
 
 def traffic_from_profile(stage: str, workload: str):
@@ -570,7 +577,8 @@ def config_entry(w, r):
 def measure_forward(w, args, g, dev, torch, moe):
     """Warm-up, then exactly K moe_forward steps between two device synchronisations (the
     throughput), a staged pass of K steps (per-stage event times, the dominant kernel's average
-    launch duration) and a cold pass of K staged steps with the caches scrubbed before each."""
+    launch duration), and two cold passes with the caches scrubbed before each step: K staged
+    steps (per-stage times) and K plain steps, each between two events (the cold step time)."""
     p = moe.problem_for(w)
     ws = torch.empty(moe.workspace_bytes(p), dtype=torch.uint8, device=dev)
     y = torch.empty((w.T, w.d), dtype=torch.float32, device=dev)
@@ -649,14 +657,29 @@ def measure_forward(w, args, g, dev, torch, moe):
             scrub.max()
         moe.forward_staged(p, g["x"], g["w_gate"], g["w1"], g["w3"], g["w2"], handles[s_], y=y, **kw)
     torch.cuda.synchronize()
-    del scrub
     cold_stage = {name: statistics.median(events[s][i].elapsed_time(events[s][i + 1])
                                           for s in range(args.steps))
                   for i, name in enumerate(moe.STAGES)}
-    cold_steps = [events[s][0].elapsed_time(events[s][len(moe.STAGES)]) for s in range(args.steps)]
+    staged_cold_steps = [events[s][0].elapsed_time(events[s][len(moe.STAGES)])
+                         for s in range(args.steps)]
+    # the cold step itself: the plain forward (the timed pass's call) between two events, the
+    # caches scrubbed before each; the stage events above cost a few microseconds each, which at
+    # decode sizes is a large part of a step
+    for s_ in range(args.steps):
+        if args.scrub == "write":
+            scrub.fill_(s_)
+        else:
+            scrub.max()
+        events[s_][0].record(stream)
+        step()
+        events[s_][1].record(stream)
+    torch.cuda.synchronize()
+    del scrub
+    cold_steps = [events[s][0].elapsed_time(events[s][1]) for s in range(args.steps)]
     log(f"[bench] {w.name} cold stage ms (median): " + ", ".join(f"{k}={v:.4f}" for k, v in cold_stage.items()))
     log(f"[bench] cold step (caches scrubbed): median {statistics.median(cold_steps):.4f} ms, "
-        f"min {min(cold_steps):.4f} ms")
+        f"min {min(cold_steps):.4f} ms (with the stage events: median "
+        f"{statistics.median(staged_cold_steps):.4f} ms)")
 
     # dominant kernel roofline
     dom = max(("gate_up", "down"), key=lambda s: stage_ms[s])
@@ -683,6 +706,7 @@ def measure_forward(w, args, g, dev, torch, moe):
     cold_dom_s = cold_stage[dom] * 1e-3
     cold = {"scrub_bytes": 1 << 30, "ms_per_step_median": statistics.median(cold_steps),
             "ms_per_step_min": min(cold_steps),
+            "staged_ms_per_step_median": statistics.median(staged_cold_steps),
             "stage_ms_median": {k: round(v, 5) for k, v in cold_stage.items()},
             "dominant_achieved": (kwk["flops"] / cold_dom_s / 1e12 if roof["unit"] == "TFLOP/s"
                                   else kwk["bytes"] / cold_dom_s / 1e9),

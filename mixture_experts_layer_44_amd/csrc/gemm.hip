@@ -967,19 +967,22 @@ __global__ __launch_bounds__(256) void gemm_bf16_dec_kernel(GemmArgs args) {
     sa[f] = GATEUP ? args.sorted_assign[tc.off + (!shared_grp && r < tc.rows ? r : 0)] : 0;
   }
   const bf16_t* ap[kDecBM / 16];
+  auto make_ap = [&]() {
 #pragma unroll
-  for (int f = 0; f < kDecBM / 16; ++f) {
-    int srow;
-    if (GATEUP) {
-      const int r = tc.m_local * kDecBM + f * 16 + r16;
-      const int rr = r < tc.rows ? r : 0;             // padding rows repeat the first row
-      const int tok = shared_grp ? rr : sa[f] / args.k;
-      srow = (unsigned)tok < (unsigned)args.T ? tok : 0;
-    } else {
-      srow = tc.mt_global * kDecBM + f * 16 + r16;     // padding rows: results not stored
+    for (int f = 0; f < kDecBM / 16; ++f) {
+      int srow;
+      if (GATEUP) {
+        const int r = tc.m_local * kDecBM + f * 16 + r16;
+        const int rr = r < tc.rows ? r : 0;             // padding rows repeat the first row
+        const int tok = shared_grp ? rr : sa[f] / args.k;
+        srow = (unsigned)tok < (unsigned)args.T ? tok : 0;
+      } else {
+        srow = tc.mt_global * kDecBM + f * 16 + r16;     // padding rows: results not stored
+      }
+      ap[f] = args.A + (size_t)srow * K + kbase;
     }
-    ap[f] = args.A + (size_t)srow * K + kbase;
-  }
+  };
+  if (GATEUP) make_ap();
 
   auto run = [&](auto nf_tag) {
     constexpr int NF = decltype(nf_tag)::value;
@@ -991,19 +994,37 @@ __global__ __launch_bounds__(256) void gemm_bf16_dec_kernel(GemmArgs args) {
       for (int b = 0; b < NBLK; ++b) acc[f][b] = f32x4{0.f, 0.f, 0.f, 0.f};
     // A and B of a step are issued together, D steps ahead: vector-memory loads retire in
     // order, so an A load issued after a later step's B loads would make its wait cover them.
+    // The down GEMM issues its first D steps as all weights, then all h rows: decode T = 128
+    // down 83 -> 78 us, T = 32 67.5 -> 64.5 us. (The same for the gate-up, with its row addresses computed after the
+    // weight loads went out, made it slower: T = 1 13.5 -> 15.1 us, T = 128 139 -> 150 us.)
     bf16x8 bq[D][NBLK][2], aq[D][NF][2];
-    auto load = [&](int d, int kt) {
+    auto load_b = [&](int d, int kt) {
 #pragma unroll
       for (int b = 0; b < NBLK; ++b)
 #pragma unroll
         for (int s = 0; s < 2; ++s) bq[d][b][s] = *(const bf16x8*)(bp[b] + kt * 64 + s * 32);
+    };
+    auto load_a = [&](int d, int kt) {
 #pragma unroll
       for (int f = 0; f < NF; ++f)
 #pragma unroll
         for (int s = 0; s < 2; ++s) aq[d][f][s] = *(const bf16x8*)(ap[f] + kt * 64 + s * 32);
     };
+    auto load = [&](int d, int kt) {
+      load_b(d, kt);
+      load_a(d, kt);
+    };
+    if constexpr (GATEUP) {
 #pragma unroll
-    for (int d = 0; d < D; ++d) load(d, d);
+      for (int d = 0; d < D; ++d) load(d, d);
+    } else {
+#pragma unroll
+      for (int d = 0; d < D; ++d) load_b(d, d);
+      __builtin_amdgcn_sched_barrier(0);
+      make_ap();
+#pragma unroll
+      for (int d = 0; d < D; ++d) load_a(d, d);
+    }
 #pragma unroll
     for (int kt = 0; kt < KTW; ++kt) {
       const int d = kt % D;

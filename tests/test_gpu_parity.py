@@ -54,6 +54,10 @@ SMALL = [
     # wide tiles under a steep logit offset: segments of 2048, 1820, 200 and 28 rows, so the
     # four-wave kernel's waves run with all, one and no live row fragments
     W("bf16_wide_skew", T=2048, d=512, E=4, k=2, d_ff=512, seed=131, zipf_s=2.0),
+    # one token: routing, grouping and schedule in one wave, with a shared expert (a group of
+    # its own after the routed ones), a selection bias and a capacity limit
+    W("bf16_T1_shared_selbias", T=1, d=512, E=64, k=6, d_ff=256, seed=132, n_shared=1,
+      d_ff_shared=256, sel_bias=True, capacity_factor=1.0),
     # ragged 192-row tiles: ~150 rows per expert (one tile), the shared group 600 rows (four)
     W("bf16_mid192", T=600, d=512, E=8, k=2, d_ff=384, seed=115, n_shared=1, d_ff_shared=384),
     # ragged 192-row tiles, ~350 rows per expert (two tiles each)

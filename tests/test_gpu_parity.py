@@ -54,6 +54,10 @@ SMALL = [
     # wide tiles under a steep logit offset: segments of 2048, 1820, 200 and 28 rows, so the
     # four-wave kernel's waves run with all, one and no live row fragments
     W("bf16_wide_skew", T=2048, d=512, E=4, k=2, d_ff=512, seed=131, zipf_s=2.0),
+    # wide tiles under a capacity limit (overflow dropped, tiles dealt to the XCDs in chunks,
+    # the down GEMM's K range split in two)
+    W("bf16_wide_cap", T=2048, d=512, E=4, k=2, d_ff=512, seed=133, capacity_factor=0.9,
+      zipf_s=0.5),
     # one token: routing, grouping and schedule in one wave, with a shared expert (a group of
     # its own after the routed ones), a selection bias and a capacity limit
     W("bf16_T1_shared_selbias", T=1, d=512, E=64, k=6, d_ff=256, seed=132, n_shared=1,

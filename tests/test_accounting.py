@@ -60,3 +60,31 @@ def test_gemm_stage_names():
     assert bench.gemm_stage("moe::gemm_f32_kernel<false>(x)") == "down"
     assert bench.gemm_stage("__amd_rocclr_copyBuffer") is None
     assert bench.gemm_stage("moe::combine_kernel(float const*)") is None
+
+
+def test_counter_summaries_go_void_when_a_kernel_source_changes(tmp_path, monkeypatch):
+    """A profiles/traffic_*.json summary counts only while every source its stage's kernels are
+    built from (the GEMM file, the tile walk, the shared definitions) is unchanged."""
+    import json
+    import os
+    import shutil
+    import bench
+    csrc = os.path.join(bench.ROOT, "mixture_experts_layer_44_amd", "csrc")
+    shutil.copytree(csrc, tmp_path / "mixture_experts_layer_44_amd" / "csrc")
+    (tmp_path / "profiles").mkdir()
+    monkeypatch.setattr(bench, "ROOT", str(tmp_path))
+    for stage in ("gate_up", "down"):
+        for name in bench.KERNEL_SOURCES[stage]:
+            assert os.path.exists(tmp_path / "mixture_experts_layer_44_amd" / "csrc" / name)
+        sha = bench.source_sha(stage)
+        rec = {"source_sha": sha, "traffic_bytes_per_launch": 123.0}
+        (tmp_path / "profiles" / f"traffic_{stage}_w.json").write_text(json.dumps(rec))
+        assert bench.traffic_from_profile(stage, "w") == 123.0
+        assert bench.traffic_from_profile(stage, "other") is None
+        for name in bench.KERNEL_SOURCES[stage]:     # touching any one source voids it
+            path = tmp_path / "mixture_experts_layer_44_amd" / "csrc" / name
+            orig = path.read_bytes()
+            path.write_bytes(orig + b"\n")
+            assert bench.traffic_from_profile(stage, "w") is None, name
+            path.write_bytes(orig)
+        assert bench.traffic_from_profile(stage, "w") == 123.0

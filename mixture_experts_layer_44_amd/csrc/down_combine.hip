@@ -11,7 +11,8 @@
 // workgroup owns 16 output features of one token and computes them for all of the token's
 // kept slots, then folds the slots into y in slot order. No row goes to HBM and one launch
 // (with its start-up latency and its dependent loads) disappears from the step: a decode
-// step is four launches (router logits; top-k with grouping and schedule; gate-up; this).
+// step of one or two tokens is four launches (router logits; top-k with grouping and schedule;
+// gate-up; this).
 // (Measured and not kept: gate-up tiles found from the top-k ids directly, h by assignment, so
 // that neither GEMM looks up the schedule. Decode T = 1 kernel times were the same, and at
 // T = 8 the assignments that share an expert each streamed its weights: gate-up 60 -> 62 us.)
@@ -148,11 +149,13 @@ void launch_dc_k(int steps, dim3 grid, hipStream_t s, const DcArgs& a) {
 
 }  // namespace
 
-// Decode class (the decode GEMM kernel's shapes), no shared expert, k <= 8 and at most 64
+// Decode class (the decode GEMM kernel's shapes), no shared expert, k <= 8 and at most 16
 // assignments: with so few tokens the expert rows are each read back once by one token's
-// combine, and the grouping has next to nothing to share between tokens.
+// combine, and the grouping has next to nothing to share between tokens. (At T = 8, k = 8 the
+// decode down GEMM, since its weights-first prologue, and the combine apart are faster: step
+// 108.7 -> 107.3 us; at T = 1 this launch still wins, 31.8 against 33.5 us.)
 bool dec_down_combine(const moe_problem& p) {
-  return gemm_dec(p) && p.n_shared == 0 && p.k <= kDcMaxK && (long long)p.T * p.k <= 64 &&
+  return gemm_dec(p) && p.n_shared == 0 && p.k <= kDcMaxK && (long long)p.T * p.k <= 16 &&
          p.d % kDcFeat == 0 && down_ksplit(p) == 1;
 }
 

@@ -150,7 +150,7 @@ hipError_t launch_expert_ffn(const moe_problem& p, const void* x, const void* w1
                              hipEvent_t between = nullptr, int row_div = 0, float* U = nullptr,
                              float* V = nullptr);
 
-// Decode-sized layers without a shared expert (k <= 8, T*k <= 64): the gate-up GEMM alone
+// Decode-sized layers without a shared expert (k <= 8, T*k <= 16): the gate-up GEMM alone
 // (decode class, h out), then the down GEMM and the combine in one launch, y bit-identical to
 // launch_expert_ffn's rows followed by launch_combine.
 hipError_t launch_dec_gate_up(const moe_problem& p, const void* x, const void* w1, const void* w3,

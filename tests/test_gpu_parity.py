@@ -100,10 +100,13 @@ SMALL = [
     # padding), T not a multiple of the 64-token logits block, a logit offset and a selection bias
     W("bf16_E200", T=300, d=384, E=200, k=6, d_ff=256, seed=127, sel_bias=True,
       zipf_s=0.5),
-    # decode down GEMM + combine in one launch (T*k <= 64, k <= 8, no shared expert): dropped
-    # slots under a capacity limit, and an odd k (the second slot group one slot short) with
-    # K = d_ff of eight wave steps
-    W("bf16_dec_fused_cap", T=8, d=512, E=16, k=8, d_ff=512, seed=130, capacity_factor=0.5,
+    # decode down GEMM + combine in one launch (T*k <= 16, k <= 8, no shared expert): dropped
+    # slots under a capacity limit (one row per expert), and an odd k (the second slot group one
+    # slot short) with K = d_ff of eight wave steps
+    W("bf16_dec_fused_cap", T=2, d=512, E=16, k=8, d_ff=512, seed=130, capacity_factor=0.5,
+      zipf_s=1.1),
+    # the same shape at T = 8 (64 assignments): the down GEMM and the combine apart
+    W("bf16_dec_cap_T8", T=8, d=512, E=16, k=8, d_ff=512, seed=130, capacity_factor=0.5,
       zipf_s=1.1),
     W("bf16_dec_fused_k5", T=3, d=768, E=32, k=5, d_ff=2048, seed=131, sel_bias=True),
 ]
@@ -234,7 +237,7 @@ COMPOSE = [
       capacity_factor=0.8),
     # decode-sized: moe_forward runs the down GEMM and the combine as one launch; expert_ffn +
     # combine run them apart. Same bits.
-    W("compose_dec_fused_cap", T=8, d=512, E=16, k=8, d_ff=512, seed=204, capacity_factor=0.5),
+    W("compose_dec_fused_cap", T=2, d=512, E=16, k=8, d_ff=512, seed=204, capacity_factor=0.5),
     W("compose_dec_T1", T=1, d=2048, E=128, k=8, d_ff=768, seed=205),
     W("compose_dec_k3", T=2, d=256, E=8, k=3, d_ff=2048, seed=206, sel_bias=True),
 ]

@@ -105,6 +105,8 @@ SMALL = [
     # slot short) with K = d_ff of eight wave steps
     W("bf16_dec_fused_cap", T=2, d=512, E=16, k=8, d_ff=512, seed=130, capacity_factor=0.5,
       zipf_s=1.1),
+    # just past the merged launch's limit (18 assignments): the down GEMM and the combine apart
+    W("bf16_dec_T3_k6", T=3, d=1024, E=32, k=6, d_ff=512, seed=134, sel_bias=True),
     # the same shape at T = 8 (64 assignments): the down GEMM and the combine apart
     W("bf16_dec_cap_T8", T=8, d=512, E=16, k=8, d_ff=512, seed=130, capacity_factor=0.5,
       zipf_s=1.1),
